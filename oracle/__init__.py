@@ -1,0 +1,7 @@
+"""CPU oracle for the STAR-KV decode path (test infrastructure, not product).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It shares no code with the HIP library.
+"""
+
+from .starkv_oracle import append, decode, gather_latents  # noqa: F401
