@@ -1,0 +1,158 @@
+/*
+ * starkv.h - C ABI of libstarkv: STAR-KV decode over a low-rank paged KV cache
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The method (Proxima README text on wpnews, "Show HN: Proxima ...", opening
+ * description of STAR-KV): each layer stores a low-rank projection of its KV
+ * cache.  Keys are decomposed per head - head h of token t keeps a rank-r_k
+ * latent c_k[t,h] and its key is c_k[t,h] . B_k[h] - and values jointly - token
+ * t keeps one rank-r_v latent c_v[t] shared by all heads and its value row over
+ * all heads is c_v[t] . B_v, head h owning columns [h*d, (h+1)*d) of B_v.  The
+ * latents are stored in a compressed paged format.  Paging (botdigit page on
+ * vLLM PagedAttention, "How Dynamic KV-Cache Compaction Works", block-level
+ * management item): fixed-size blocks handed to sequences as they grow, not
+ * contiguous, found through a per-sequence block table.  Block size 16 (Proxima
+ * README, measured results, block-count comparison).
+ *
+ * Conventions shared by every call
+ *  - All tensors are dense, row-major, in device memory (HBM) unless marked
+ *    "host".  fp16 is IEEE binary16; accumulation is fp32.
+ *  - Paged layout (physical block p, slot j = position % 16):
+ *      k_cache [num_blocks][H][16][r_k]  fp16  (head-major inside a block)
+ *      v_cache [num_blocks][r_v][16]     fp16  (latent-dim-major inside a block)
+ *    Position t of sequence b lives in block block_tables[b*max_blocks_per_seq
+ *    + t/16], slot t%16.
+ *  - The caller owns every buffer.  The library never allocates, frees or
+ *    synchronizes device memory in these calls; work is enqueued on `stream`
+ *    (a hipStream_t, NULL = the null stream) and runs asynchronously.
+ *  - Errors that the host can see are returned synchronously as a status and
+ *    nothing is enqueued.  Device-side contracts (block ids in range, lengths
+ *    within bounds) are the caller's: violating them is undefined behaviour.
+ *  - Functions never abort and never throw across the ABI.
+ */
+#ifndef STARKV_H
+#define STARKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  STARKV_OK = 0,
+  STARKV_ERR_INVALID_ARG = 1, /* null pointer, non-positive or inconsistent size, misalignment */
+  STARKV_ERR_UNSUPPORTED = 2, /* valid but not built: block_size != 16 or a shape with no kernel */
+  STARKV_ERR_WORKSPACE = 3,   /* workspace smaller than starkv_decode_workspace_size() */
+  STARKV_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} starkv_status;
+
+/* Host struct, passed by pointer; read during the call only. */
+typedef struct {
+  int32_t num_heads;          /* H (query heads == KV heads)            */
+  int32_t head_dim;           /* d, multiple of 8, <= 256               */
+  int32_t rank_k;             /* r_k per head                           */
+  int32_t rank_v;             /* r_v joint over heads                   */
+  int32_t block_size;         /* tokens per paged block; must be 16     */
+  int32_t num_blocks;         /* physical blocks in each pool           */
+  int32_t max_blocks_per_seq; /* row stride of block_tables             */
+} starkv_dims;
+
+/* Latent shapes with a decode kernel built into this library:
+ *   (H, r_k, r_v) = (32, 64, 1024) and (4, 16, 64).  Others -> UNSUPPORTED. */
+
+/*
+ * starkv_append - project new K/V rows into latents and write them into their
+ * paged slots (the method's "stored in a compressed paged format" step).
+ *
+ *   c_k[i,h,:] = fp16( w_k[h] . k[i,h,:] )      w_k [H][r_k][d]
+ *   c_v[i,:]   = fp16( w_v . vec(v[i]) )        w_v [r_v][H*d], vec = heads concatenated
+ * computed with fp32 accumulation and rounded once to fp16 (nearest even).
+ * The down-projections are stored output-major (row r is the weight vector of
+ * latent r).  With orthonormal-row up-projections B, w = B gives the
+ * least-squares latents, so callers may pass b_k / b_v of starkv_decode.
+ *
+ *   n_tokens     number of rows; 0 is a no-op returning STARKV_OK.
+ *   k, v         [n_tokens][H][d] fp16, 16-byte aligned.
+ *   block_tables [B][max_blocks_per_seq] int32.  The target block of every
+ *                token must already be assigned (allocation is the caller's).
+ *   token_seq    [n_tokens] int32: table row of token i.
+ *   token_pos    [n_tokens] int32: 0-based position of token i in its sequence;
+ *                token_pos/16 < max_blocks_per_seq.  (seq, pos) pairs within
+ *                one call must be distinct.
+ *   k_cache, v_cache  pools (layout above), 16-byte aligned; exactly
+ *                H*r_k + r_v fp16 values per token are written, nothing else.
+ */
+starkv_status starkv_append(const starkv_dims* dims, int32_t n_tokens,
+                            const void* k, const void* v,
+                            const void* w_k, const void* w_v,
+                            const int32_t* block_tables,
+                            const int32_t* token_seq, const int32_t* token_pos,
+                            void* k_cache, void* v_cache, void* stream);
+
+/*
+ * starkv_decode_workspace_size - bytes of device scratch starkv_decode needs
+ * for this (dims, batch, max_context_len).  Host-only; depends on nothing but
+ * its arguments.  Returns 0 if the arguments are invalid.
+ */
+size_t starkv_decode_workspace_size(const starkv_dims* dims, int32_t batch,
+                                    int32_t max_context_len);
+
+/*
+ * starkv_decode - single-query attention of every sequence in the batch over
+ * its latent paged cache (the method's decode step):
+ *
+ *   K_h = C_k[:,h,:] . B_k[h],  V_h = (C_v . B_v)[:, h*d:(h+1)*d]
+ *   out[b,h,:] = softmax(scale * K_h q[b,h]) . V_h      (context_lens[b] tokens)
+ *
+ * computed in latent space: q is projected by B_k (q~ = scale*log2(e)*B_k[h] q),
+ * scored against the latents, split into token ranges with a per-range
+ * max / sum / weighted latent sum, merged by log-sum-exp and up-projected by
+ * B_v.  context_lens[b] == 0 gives a zero output row.
+ *
+ *   batch            B >= 1 rows of q, block_tables, context_lens and out.
+ *   max_context_len  host upper bound of context_lens (sizes the launch and the
+ *                    workspace); 0 <= context_lens[b] <= max_context_len <=
+ *                    16*max_blocks_per_seq.
+ *   q                [B][H][d] fp16, 16-byte aligned.
+ *   b_k              [H][r_k][d] fp16, 16-byte aligned.
+ *   b_v              [r_v][H*d] fp16, 2-byte aligned.
+ *   k_cache, v_cache pools (layout above), 16-byte aligned.  Entries of a
+ *                    table row at index >= ceil(len/16), and slots >= len%16 of
+ *                    the last block, are never read.
+ *   block_tables     [B][max_blocks_per_seq] int32; context_lens [B] int32.
+ *   scale            softmax scale applied to q.k (e.g. 1/sqrt(d)).
+ *   workspace        device scratch of workspace_bytes >= the size above,
+ *                    256-byte aligned; contents need not be initialised and are
+ *                    garbage afterwards.  Two calls in flight at once need two
+ *                    workspaces.
+ *   out              [B][H][d] fp16.
+ */
+starkv_status starkv_decode(const starkv_dims* dims, int32_t batch, int32_t max_context_len,
+                            const void* q, const void* b_k, const void* b_v,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            float scale, void* workspace, size_t workspace_bytes,
+                            void* out, void* stream);
+
+/* Static, human-readable name of a status code (host-only). */
+const char* starkv_status_string(starkv_status status);
+
+/*
+ * Measurement hooks (host-only, process-wide, not for use while another
+ * thread is decoding).  Between starkv_profile_begin() and
+ * starkv_profile_end(), every starkv_decode call brackets its latent
+ * attention kernel with a pair of HIP events on its own stream (up to 4096
+ * calls).  starkv_profile_end() waits for those events, writes the summed
+ * kernel time in milliseconds and the number of bracketed launches, and
+ * releases the events.  Returns STARKV_ERR_HIP if an event call failed.
+ */
+starkv_status starkv_profile_begin(void);
+starkv_status starkv_profile_end(double* attn_kernel_ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STARKV_H */

@@ -1,0 +1,208 @@
+"""Python binding of libstarkv (STAR-KV decode over a low-rank paged KV cache).
+
+Argument marshalling only: every step of the path runs in the HIP library
+(include/starkv.h).  Tensors are torch tensors on the GPU; torch provides
+device memory and the current stream, nothing else.  If the compiled library
+is missing, every call raises - there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "Dims", "StarkvError", "load_library", "library_path", "status_string",
+    "decode_workspace_size", "decode", "append", "profile_begin", "profile_end",
+    "BLOCK_SIZE",
+]
+
+BLOCK_SIZE = 16
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libstarkv.so"
+
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
+
+
+class StarkvError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {status_string(code)}")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("rank_k", ctypes.c_int32),
+        ("rank_v", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+    ]
+
+    @classmethod
+    def make(cls, heads, head_dim, rank_k, rank_v, num_blocks, max_blocks_per_seq, block_size=BLOCK_SIZE):
+        return cls(heads, head_dim, rank_k, rank_v, block_size, num_blocks, max_blocks_per_seq)
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("STARKV_LIBRARY", os.path.join(_HERE, _LIB_NAME))
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libstarkv.so (built by rank_compressed_paged_amd.build)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path()
+    if not os.path.exists(p):
+        raise RuntimeError(f"libstarkv not built: {p} is missing (run python -m rank_compressed_paged_amd.build)")
+    lib = ctypes.CDLL(p)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    dp = ctypes.POINTER(Dims)
+    lib.starkv_status_string.argtypes = [ctypes.c_int]
+    lib.starkv_status_string.restype = ctypes.c_char_p
+    lib.starkv_decode_workspace_size.argtypes = [dp, i32, i32]
+    lib.starkv_decode_workspace_size.restype = sz
+    lib.starkv_decode.argtypes = [dp, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, vp, sz, vp, vp]
+    lib.starkv_decode.restype = ctypes.c_int
+    lib.starkv_append.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.starkv_append.restype = ctypes.c_int
+    lib.starkv_profile_begin.argtypes = []
+    lib.starkv_profile_begin.restype = ctypes.c_int
+    lib.starkv_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
+    lib.starkv_profile_end.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    try:
+        return load_library().starkv_status_string(int(code)).decode()
+    except RuntimeError:
+        return STATUS.get(int(code), f"status {code}")
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise StarkvError(code, what)
+
+
+def _need(t, name, dtype, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def dims_of(k_cache, v_cache, block_tables, head_dim):
+    nb, heads, bs, rank_k = k_cache.shape
+    rank_v = v_cache.shape[1]
+    return Dims.make(heads, head_dim, rank_k, rank_v, nb, block_tables.shape[1], block_size=bs)
+
+
+def decode_workspace_size(dims: Dims, batch: int, max_context_len: int) -> int:
+    return int(load_library().starkv_decode_workspace_size(ctypes.byref(dims), batch, max_context_len))
+
+
+def decode(q, b_k, b_v, k_cache, v_cache, block_tables, context_lens, scale, *,
+           max_context_len=None, workspace=None, out=None, stream=None):
+    """out[b, h, :] of single-query attention over the latent paged cache.
+
+    q [B, H, d] fp16; b_k [H, r_k, d] fp16; b_v [r_v, H*d] fp16;
+    k_cache [NB, H, 16, r_k] fp16; v_cache [NB, r_v, 16] fp16;
+    block_tables [B, MB] int32; context_lens [B] int32.  max_context_len
+    defaults to 16*MB (no host sync).  Returns out [B, H, d] fp16.
+    """
+    import torch
+    lib = load_library()
+    batch, heads, d = q.shape
+    dims = dims_of(k_cache, v_cache, block_tables, d)
+    if max_context_len is None:
+        max_context_len = BLOCK_SIZE * block_tables.shape[1]
+    ptrs = [
+        _need(q, "q", torch.float16, 3), _need(b_k, "b_k", torch.float16, 3),
+        _need(b_v, "b_v", torch.float16, 2), _need(k_cache, "k_cache", torch.float16, 4),
+        _need(v_cache, "v_cache", torch.float16, 3), _need(block_tables, "block_tables", torch.int32, 2),
+        _need(context_lens, "context_lens", torch.int32, 1),
+    ]
+    if block_tables.shape[0] != batch or context_lens.shape[0] != batch:
+        raise ValueError("block_tables / context_lens rows must match q's batch")
+    if tuple(b_k.shape) != (heads, dims.rank_k, d) or tuple(b_v.shape) != (dims.rank_v, heads * d):
+        raise ValueError("projection shapes do not match the caches")
+    if tuple(v_cache.shape) != (dims.num_blocks, dims.rank_v, BLOCK_SIZE) or k_cache.shape[2] != BLOCK_SIZE:
+        raise ValueError("cache shapes do not match the paged layout")
+    need = lib.starkv_decode_workspace_size(ctypes.byref(dims), batch, int(max_context_len))
+    if need == 0:
+        _check(1, "starkv_decode_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+    ws_ptr = _need(workspace, "workspace", torch.uint8, 1)
+    pad = (-ws_ptr) % 256
+    if out is None:
+        out = torch.empty_like(q)
+    optr = _need(out, "out", torch.float16, 3)
+    code = lib.starkv_decode(ctypes.byref(dims), batch, int(max_context_len), *ptrs[:5], ptrs[5], ptrs[6],
+                             float(scale), ctypes.c_void_p(ws_ptr + pad), workspace.numel() - pad,
+                             ctypes.c_void_p(optr), _stream(stream))
+    _check(code, "starkv_decode")
+    return out
+
+
+def append(k, v, w_k, w_v, block_tables, token_seq, token_pos, k_cache, v_cache, *, stream=None):
+    """Project new rows into latents and scatter them into the paged caches (in place).
+
+    k, v [n, H, d] fp16; w_k [H, r_k, d] fp16; w_v [r_v, H*d] fp16 (output-major
+    down-projections); token_seq / token_pos [n] int32.
+    """
+    import torch
+    lib = load_library()
+    n, heads, d = k.shape
+    dims = dims_of(k_cache, v_cache, block_tables, d)
+    ptrs = [
+        _need(k, "k", torch.float16, 3), _need(v, "v", torch.float16, 3),
+        _need(w_k, "w_k", torch.float16, 3), _need(w_v, "w_v", torch.float16, 2),
+        _need(block_tables, "block_tables", torch.int32, 2),
+        _need(token_seq, "token_seq", torch.int32, 1), _need(token_pos, "token_pos", torch.int32, 1),
+        _need(k_cache, "k_cache", torch.float16, 4), _need(v_cache, "v_cache", torch.float16, 3),
+    ]
+    if tuple(v.shape) != (n, heads, d) or token_seq.shape[0] != n or token_pos.shape[0] != n:
+        raise ValueError("k, v, token_seq and token_pos must agree on n")
+    if tuple(w_k.shape) != (heads, dims.rank_k, d) or tuple(w_v.shape) != (dims.rank_v, heads * d):
+        raise ValueError("down-projection shapes do not match the caches")
+    code = lib.starkv_append(ctypes.byref(dims), n, *[ctypes.c_void_p(p) for p in ptrs], _stream(stream))
+    _check(code, "starkv_append")
+
+
+def profile_begin():
+    _check(load_library().starkv_profile_begin(), "starkv_profile_begin")
+
+
+def profile_end():
+    """(summed attention-kernel milliseconds, bracketed launches) since profile_begin()."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int32()
+    _check(load_library().starkv_profile_end(ctypes.byref(ms), ctypes.byref(n)), "starkv_profile_end")
+    return ms.value, n.value

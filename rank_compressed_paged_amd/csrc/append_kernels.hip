@@ -1,0 +1,192 @@
+// STAR-KV append kernels for gfx950: project new K/V rows into latents, round
+// once to fp16 and scatter them into their paged slots.
+//
+// Method: Proxima README text on wpnews ("Show HN: Proxima ..."), opening
+// description of STAR-KV (per-head K projection, one joint V projection, paged
+// compressed storage).  The down-projections are stored output-major
+// (w_k [H][r_k][d], w_v [r_v][H*d]) so both MFMA operands are contiguous along
+// the contraction.  Slot of token i: block block_tables[seq_i][pos_i / 16],
+// slot pos_i % 16 (fixed-size blocks via a block table, botdigit
+// PagedAttention page, block-level management item).
+
+#include "common.h"
+#include "launch.h"
+
+namespace starkv {
+
+struct SlotOf {
+  const int32_t* bt;
+  const int32_t* seq;
+  const int32_t* pos;
+  int mb;
+  __device__ void operator()(int i, int& phys, int& slot) const {
+    const int p = pos[i];
+    phys = bt[(size_t)seq[i] * mb + p / kBlock];
+    slot = p % kBlock;
+  }
+};
+
+// K side, MFMA: one wave computes a [32 tokens x 32 latents] tile of one head.
+__global__ void __launch_bounds__(64)
+append_k_mfma_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int n, int H, int D, int RK,
+                     SlotOf where, f16* __restrict__ kc) {
+  const int lane = threadIdx.x;
+  const int rtiles = RK / 32;
+  const int rt = blockIdx.x % rtiles;
+  const int h = (blockIdx.x / rtiles) % H;
+  const int tt = blockIdx.x / (rtiles * H);
+  const int t = tt * 32 + (lane & 31);
+  const int r = rt * 32 + (lane & 31);
+  const int kofs = (lane >> 5) * 8;
+  floatx16 acc = {};
+  for (int k0 = 0; k0 < D; k0 += 16) {
+    half8 a = {};
+    if (t < n) a = *reinterpret_cast<const half8*>(k + ((size_t)t * H + h) * D + k0 + kofs);
+    const half8 b = *reinterpret_cast<const half8*>(wk + ((size_t)h * RK + r) * D + k0 + kofs);
+    acc = mfma32x32x16(a, b, acc);
+  }
+#pragma unroll
+  for (int reg = 0; reg < 16; ++reg) {
+    const int ti = tt * 32 + mfma_row(reg, lane);
+    if (ti < n) {
+      int phys, slot;
+      where(ti, phys, slot);
+      kc[(((size_t)phys * H + h) * kBlock + slot) * RK + r] = (f16)acc[reg];
+    }
+  }
+}
+
+// K side, VALU: one thread per (token, head, latent).
+__global__ void __launch_bounds__(256)
+append_k_valu_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int n, int H, int D, int RK,
+                     SlotOf where, f16* __restrict__ kc) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n * H * RK) return;
+  const int r = idx % RK;
+  const int h = (idx / RK) % H;
+  const int t = idx / (RK * H);
+  const f16* x = k + ((size_t)t * H + h) * D;
+  const f16* wrow = wk + ((size_t)h * RK + r) * D;
+  float acc = 0.f;
+  for (int i = 0; i < D; i += 8) {
+    const half8 a = *reinterpret_cast<const half8*>(x + i);
+    const half8 b = *reinterpret_cast<const half8*>(wrow + i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
+  }
+  int phys, slot;
+  where(t, phys, slot);
+  kc[(((size_t)phys * H + h) * kBlock + slot) * RK + r] = (f16)acc;
+}
+
+// V side, MFMA: a workgroup computes a [32 tokens x 32 latents] tile; its four
+// waves split the H*d contraction and reduce through LDS.
+__global__ void __launch_bounds__(256)
+append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
+                     SlotOf where, f16* __restrict__ vc) {
+  __shared__ float red[4][16][64];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int jtiles = RV / 32;
+  const int jt = blockIdx.x % jtiles;
+  const int tt = blockIdx.x / jtiles;
+  const int t = tt * 32 + (lane & 31);
+  const int j = jt * 32 + (lane & 31);
+  const int kofs = (lane >> 5) * 8;
+  const int kspan = K / 4;
+  floatx16 acc = {};
+  for (int k0 = w * kspan; k0 < (w + 1) * kspan; k0 += 16) {
+    half8 a = {};
+    if (t < n) a = *reinterpret_cast<const half8*>(v + (size_t)t * K + k0 + kofs);
+    const half8 b = *reinterpret_cast<const half8*>(wv + (size_t)j * K + k0 + kofs);
+    acc = mfma32x32x16(a, b, acc);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[w][r][lane] = acc[r];
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ti = tt * 32 + mfma_row(r, lane);
+      if (ti < n) {
+        const float s = red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane];
+        int phys, slot;
+        where(ti, phys, slot);
+        vc[((size_t)phys * RV + j) * kBlock + slot] = (f16)s;
+      }
+    }
+  }
+}
+
+// V side, VALU: one wave per joint latent j and up to 16 tokens (grid.y walks
+// token groups); lanes split the H*d contraction, coalesced along w_v's row.
+constexpr int kAppendGroup = 16;
+
+__global__ void __launch_bounds__(256)
+append_v_valu_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
+                     SlotOf where, f16* __restrict__ vc) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= RV) return;
+  const int t0 = blockIdx.y * kAppendGroup;
+  const int cnt = min(kAppendGroup, n - t0);
+  float acc[kAppendGroup];
+#pragma unroll
+  for (int i = 0; i < kAppendGroup; ++i) acc[i] = 0.f;
+  for (int k0 = lane * 8; k0 < K; k0 += 512) {
+    const half8 b = *reinterpret_cast<const half8*>(wv + (size_t)j * K + k0);
+#pragma unroll
+    for (int i = 0; i < kAppendGroup; ++i) {
+      if (i < cnt) {
+        const half8 a = *reinterpret_cast<const half8*>(v + (size_t)(t0 + i) * K + k0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i] += (float)a[e] * (float)b[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kAppendGroup; ++i) {
+    float s = acc[i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (lane == 0 && i < cnt) {
+      int phys, slot;
+      where(t0 + i, phys, slot);
+      vc[((size_t)phys * RV + j) * kBlock + slot] = (f16)s;
+    }
+  }
+}
+
+hipError_t append_enqueue(const AppendLaunch& a) {
+  const Shape& s = a.s;
+  const SlotOf where{a.block_tables, a.token_seq, a.token_pos, s.MB};
+  const f16* k = static_cast<const f16*>(a.k);
+  const f16* v = static_cast<const f16*>(a.v);
+  const f16* wk = static_cast<const f16*>(a.w_k);
+  const f16* wv = static_cast<const f16*>(a.w_v);
+  f16* kc = static_cast<f16*>(a.k_cache);
+  f16* vc = static_cast<f16*>(a.v_cache);
+  const int K = s.H * s.D;
+  if (a.n >= 16 && s.RK % 32 == 0 && s.D % 16 == 0) {
+    const int grid = ((a.n + 31) / 32) * s.H * (s.RK / 32);
+    hipLaunchKernelGGL(append_k_mfma_kernel, dim3(grid), dim3(64), 0, a.stream, k, wk, a.n, s.H, s.D, s.RK,
+                       where, kc);
+  } else {
+    const int grid = (a.n * s.H * s.RK + 255) / 256;
+    hipLaunchKernelGGL(append_k_valu_kernel, dim3(grid), dim3(256), 0, a.stream, k, wk, a.n, s.H, s.D, s.RK,
+                       where, kc);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (a.n >= 16 && s.RV % 32 == 0 && K % 64 == 0) {
+    const int grid = ((a.n + 31) / 32) * (s.RV / 32);
+    hipLaunchKernelGGL(append_v_mfma_kernel, dim3(grid), dim3(256), 0, a.stream, v, wv, a.n, K, s.RV, where,
+                       vc);
+  } else {
+    const dim3 grid((s.RV + 3) / 4, (a.n + kAppendGroup - 1) / kAppendGroup);
+    hipLaunchKernelGGL(append_v_valu_kernel, grid, dim3(256), 0, a.stream, v, wv, a.n, K, s.RV, where, vc);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace starkv

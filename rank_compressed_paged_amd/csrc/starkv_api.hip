@@ -1,0 +1,215 @@
+// C ABI of libstarkv: argument checks, workspace sizing and dispatch.
+// The operations themselves are described in include/starkv.h.
+
+#include <atomic>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "common.h"
+#include "launch.h"
+#include "starkv.h"
+
+using namespace starkv;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+starkv_status check_dims(const starkv_dims* d) {
+  if (!d) return STARKV_ERR_INVALID_ARG;
+  if (d->num_heads <= 0 || d->head_dim <= 0 || d->rank_k <= 0 || d->rank_v <= 0 || d->block_size <= 0 ||
+      d->num_blocks <= 0 || d->max_blocks_per_seq <= 0)
+    return STARKV_ERR_INVALID_ARG;
+  if (d->block_size != kBlock) return STARKV_ERR_UNSUPPORTED;
+  if (d->head_dim % 8 != 0 || d->head_dim > 256 || d->rank_k % 8 != 0 || d->rank_v % 32 != 0)
+    return STARKV_ERR_UNSUPPORTED;
+  // 64-bit products stay far from overflow; 32-bit indices inside kernels need:
+  if ((long long)d->num_heads * d->head_dim > (1 << 20) || (long long)d->rank_v * kBlock > (1 << 24))
+    return STARKV_ERR_UNSUPPORTED;
+  return STARKV_OK;
+}
+
+Shape shape_of(const starkv_dims* d) {
+  return Shape{d->num_heads, d->head_dim, d->rank_k, d->rank_v, d->max_blocks_per_seq};
+}
+
+bool decode_args_ok(const starkv_dims* d, int32_t batch, int32_t max_context_len) {
+  if (batch < 1 || batch > (1 << 20) || max_context_len < 0) return false;
+  if ((long long)max_context_len > (long long)kBlock * d->max_blocks_per_seq) return false;
+  const long long blocks = (long long)batch * ((max_context_len + kBlock - 1) / kBlock);
+  return blocks < (1LL << 30);
+}
+
+// Attention grid per (device, shape), filled on first use.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_resident[kMaxDevices][4];
+
+int shape_slot(int H, int RK, int RV) {
+  if (H == 32 && RK == 64 && RV == 1024) return 0;
+  if (H == 4 && RK == 16 && RV == 64) return 1;
+  return 3;
+}
+
+int resident_grid(int H, int RK, int RV, int device) {
+  if (device < 0 || device >= kMaxDevices) return attn_resident_grid(H, RK, RV, device);
+  std::atomic<int>& cell = g_resident[device][shape_slot(H, RK, RV)];
+  int v = cell.load(std::memory_order_relaxed);
+  if (v <= 0) {
+    v = attn_resident_grid(H, RK, RV, device);
+    cell.store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// measurement hooks
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+bool g_prof_err = false;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_prof_events;
+constexpr size_t kMaxProfiled = 4096;
+
+}  // namespace
+
+extern "C" {
+
+const char* starkv_status_string(starkv_status status) {
+  switch (status) {
+    case STARKV_OK: return "STARKV_OK";
+    case STARKV_ERR_INVALID_ARG: return "STARKV_ERR_INVALID_ARG: null pointer, bad size or misalignment";
+    case STARKV_ERR_UNSUPPORTED: return "STARKV_ERR_UNSUPPORTED: shape or block size not built into this library";
+    case STARKV_ERR_WORKSPACE: return "STARKV_ERR_WORKSPACE: workspace smaller than starkv_decode_workspace_size()";
+    case STARKV_ERR_HIP: return "STARKV_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "STARKV: unknown status";
+}
+
+size_t starkv_decode_workspace_size(const starkv_dims* dims, int32_t batch, int32_t max_context_len) {
+  if (check_dims(dims) != STARKV_OK || !decode_args_ok(dims, batch, max_context_len)) return 0;
+  return decode_layout(shape_of(dims), batch, max_context_len).bytes;
+}
+
+starkv_status starkv_decode(const starkv_dims* dims, int32_t batch, int32_t max_context_len, const void* q,
+                            const void* b_k, const void* b_v, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens, float scale,
+                            void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const starkv_status ds = check_dims(dims);
+  if (ds != STARKV_OK) return ds;
+  if (!decode_args_ok(dims, batch, max_context_len)) return STARKV_ERR_INVALID_ARG;
+  if (!q || !b_k || !b_v || !k_cache || !v_cache || !block_tables || !context_lens || !workspace || !out)
+    return STARKV_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(b_k, 16) || !aligned(b_v, 2) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      !aligned(workspace, 256) || !aligned(out, 2))
+    return STARKV_ERR_INVALID_ARG;
+  if (!(scale == scale)) return STARKV_ERR_INVALID_ARG;  // NaN scale
+  if (!attn_shape_supported(dims->num_heads, dims->rank_k, dims->rank_v)) return STARKV_ERR_UNSUPPORTED;
+  const Shape s = shape_of(dims);
+  const DecodeLayout lay = decode_layout(s, batch, max_context_len);
+  if (workspace_bytes < lay.bytes) return STARKV_ERR_WORKSPACE;
+
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return STARKV_ERR_HIP;
+  int grid = resident_grid(s.H, s.RK, s.RV, device);
+  if (grid > lay.grid_cap) grid = lay.grid_cap;
+  if (grid < 1) grid = 1;
+
+  DecodeLaunch a{};
+  a.s = s;
+  a.batch = batch;
+  a.grid = grid;
+  a.q = q;
+  a.b_k = b_k;
+  a.b_v = b_v;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.scale = scale;
+  a.ws = static_cast<char*>(workspace);
+  a.lay = lay;
+  a.out = out;
+  a.stream = static_cast<hipStream_t>(stream);
+
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_prof_on && g_prof_events.size() < kMaxProfiled) {
+      hipEvent_t e0 = nullptr, e1 = nullptr;
+      if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
+        g_prof_events.emplace_back(e0, e1);
+        a.ev_attn_start = e0;
+        a.ev_attn_stop = e1;
+      } else {
+        g_prof_err = true;
+        if (e0) (void)hipEventDestroy(e0);
+      }
+    }
+  }
+  return decode_enqueue(a) == hipSuccess ? STARKV_OK : STARKV_ERR_HIP;
+}
+
+starkv_status starkv_append(const starkv_dims* dims, int32_t n_tokens, const void* k, const void* v,
+                            const void* w_k, const void* w_v, const int32_t* block_tables,
+                            const int32_t* token_seq, const int32_t* token_pos, void* k_cache, void* v_cache,
+                            void* stream) {
+  const starkv_status ds = check_dims(dims);
+  if (ds != STARKV_OK) return ds;
+  if (n_tokens < 0 || n_tokens > (1 << 24)) return STARKV_ERR_INVALID_ARG;
+  if (n_tokens == 0) return STARKV_OK;
+  if (!k || !v || !w_k || !w_v || !block_tables || !token_seq || !token_pos || !k_cache || !v_cache)
+    return STARKV_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) ||
+      !aligned(block_tables, 4) || !aligned(token_seq, 4) || !aligned(token_pos, 4) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16))
+    return STARKV_ERR_INVALID_ARG;
+  AppendLaunch a{};
+  a.s = shape_of(dims);
+  a.n = n_tokens;
+  a.k = k;
+  a.v = v;
+  a.w_k = w_k;
+  a.w_v = w_v;
+  a.block_tables = block_tables;
+  a.token_seq = token_seq;
+  a.token_pos = token_pos;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.stream = static_cast<hipStream_t>(stream);
+  return append_enqueue(a) == hipSuccess ? STARKV_OK : STARKV_ERR_HIP;
+}
+
+starkv_status starkv_profile_begin(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& e : g_prof_events) {
+    (void)hipEventDestroy(e.first);
+    (void)hipEventDestroy(e.second);
+  }
+  g_prof_events.clear();
+  g_prof_err = false;
+  g_prof_on = true;
+  return STARKV_OK;
+}
+
+starkv_status starkv_profile_end(double* attn_kernel_ms, int32_t* launches) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  double total = 0.0;
+  bool bad = g_prof_err;
+  for (auto& e : g_prof_events) {
+    float ms = 0.f;
+    if (hipEventSynchronize(e.second) != hipSuccess || hipEventElapsedTime(&ms, e.first, e.second) != hipSuccess)
+      bad = true;
+    total += ms;
+  }
+  if (attn_kernel_ms) *attn_kernel_ms = total;
+  if (launches) *launches = (int32_t)g_prof_events.size();
+  for (auto& e : g_prof_events) {
+    (void)hipEventDestroy(e.first);
+    (void)hipEventDestroy(e.second);
+  }
+  g_prof_events.clear();
+  g_prof_on = false;
+  g_prof_err = false;
+  return bad ? STARKV_ERR_HIP : STARKV_OK;
+}
+
+}  // extern "C"

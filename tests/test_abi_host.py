@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function include/starkv.h declares, and
+reject bad arguments with the documented status before touching the device.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import rank_compressed_paged_amd as starkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "starkv.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return starkv.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(starkv_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("starkv_append", "starkv_decode", "starkv_decode_workspace_size", "starkv_status_string",
+              "starkv_profile_begin", "starkv_profile_end"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_exports_are_c_symbols():
+    # C linkage: the dynamic symbol table holds the plain names
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", starkv.library_path()], capture_output=True,
+                         text=True).stdout
+    syms = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for name in declared_functions():
+        assert name in syms, name
+
+
+def test_status_strings(lib):
+    for code, tag in [(0, "OK"), (1, "INVALID_ARG"), (2, "UNSUPPORTED"), (3, "WORKSPACE"), (4, "HIP")]:
+        assert tag in starkv.status_string(code)
+    assert "unknown" in starkv.status_string(99)
+
+
+def main_dims(**over):
+    d = dict(heads=32, head_dim=128, rank_k=64, rank_v=1024, num_blocks=32768, max_blocks_per_seq=512)
+    d.update(over)
+    return starkv.Dims.make(**d)
+
+
+def ws_size(lib, dims, batch, max_len):
+    return lib.starkv_decode_workspace_size(ctypes.byref(dims), batch, max_len)
+
+
+def test_workspace_size_host_only_and_monotone(lib):
+    d = main_dims()
+    a = ws_size(lib, d, 64, 8192)
+    b = ws_size(lib, d, 64, 4096)
+    c = ws_size(lib, d, 32, 8192)
+    assert a > 0 and b > 0 and c > 0
+    assert b <= a and c <= a
+    assert a % 256 == 0
+    # partial-state slots dominate: H * r_v fp32 each, at most (grid cap + batch) of them
+    assert a >= (1024 + 64) * 32 * 1024 * 4
+    assert ws_size(lib, d, 64, 0) > 0                       # empty batch still plans
+    assert ws_size(lib, d, 0, 8192) == 0                    # invalid batch
+    assert ws_size(lib, d, 64, 8192 + 1) == 0               # beyond 16 * max_blocks_per_seq
+    assert ws_size(lib, main_dims(block_size=32), 64, 8192) == 0
+
+
+def call_decode(lib, dims, batch=4, max_len=64, ptr=0x1000, ws_bytes=1 << 30, scale=0.1, out=0x1000):
+    p = ctypes.c_void_p(ptr)
+    return lib.starkv_decode(ctypes.byref(dims) if dims is not None else None, batch, max_len,
+                             p, p, p, p, p, p, p, scale, p, ws_bytes, ctypes.c_void_p(out), None)
+
+
+def test_decode_rejects_before_touching_the_device(lib):
+    d = main_dims()
+    assert call_decode(lib, None) == INVALID
+    assert call_decode(lib, d, ptr=0) == INVALID                  # null pointers
+    assert call_decode(lib, d, ptr=0x1008) == INVALID             # 16-byte alignment
+    assert call_decode(lib, d, batch=0) == INVALID
+    assert call_decode(lib, d, max_len=-1) == INVALID
+    assert call_decode(lib, d, max_len=512 * 16 + 1) == INVALID
+    assert call_decode(lib, d, scale=float("nan")) == INVALID
+    assert call_decode(lib, main_dims(heads=0)) == INVALID
+    assert call_decode(lib, main_dims(block_size=8)) == UNSUPPORTED
+    assert call_decode(lib, main_dims(rank_k=48)) == UNSUPPORTED     # no kernel for this shape
+    assert call_decode(lib, main_dims(rank_v=1000)) == UNSUPPORTED   # not a multiple of 32
+    assert call_decode(lib, main_dims(head_dim=12)) == UNSUPPORTED
+    assert call_decode(lib, d, ws_bytes=1024) == WORKSPACE
+
+
+def test_append_rejects_before_touching_the_device(lib):
+    d = main_dims()
+    p = ctypes.c_void_p(0x1000)
+    args = [p] * 9
+    assert lib.starkv_append(ctypes.byref(d), 0, *[ctypes.c_void_p(0)] * 9, None) == OK   # n = 0 no-op
+    assert lib.starkv_append(ctypes.byref(d), -1, *args, None) == INVALID
+    assert lib.starkv_append(ctypes.byref(d), 4, *[ctypes.c_void_p(0)] * 9, None) == INVALID
+    bad = list(args)
+    bad[0] = ctypes.c_void_p(0x1002)
+    assert lib.starkv_append(ctypes.byref(d), 4, *bad, None) == INVALID
+    assert lib.starkv_append(ctypes.byref(main_dims(block_size=32)), 4, *args, None) == UNSUPPORTED
+
+
+def test_profile_hooks_without_launches(lib):
+    starkv.profile_begin()
+    ms, n = starkv.profile_end()
+    assert n == 0 and ms == 0.0
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        starkv.load_library(str(tmp_path / "nope.so"))

@@ -1,0 +1,256 @@
+"""GPU parity of starkv_decode against the fp64 CPU oracle (through the C ABI).
+
+Tolerance: normwise per (sequence, head) row, max|gpu - oracle| / max|oracle|
+<= 2e-3 (fp16 latents, q, weights and output; fp32 accumulation).  Rows of
+empty sequences must be exactly zero.  Index work (block-table walking,
+masking) is checked bit-exactly through invariances: moving physical blocks
+or poisoning unread slots must not change a single output bit.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from helpers import DECODE_TOL, decode_gpu, elementwise_err, gpu, log, normwise_err, scales, to_dev
+from rank_compressed_paged_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def check(got_t, ref, rows=None, tol=DECODE_TOL, what=""):
+    got = got_t.float().cpu().numpy() if hasattr(got_t, "cpu") else got_t
+    if rows is not None:
+        got = got[rows]
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = normwise_err(got, ref)
+    ew = elementwise_err(got, ref)
+    log(f"  {what}: normwise max {err.max():.3e}, elementwise(floored) max {ew.max():.3e}")
+    assert err.max() <= tol, f"{what}: normwise error {err.max():.3e} > {tol}"
+    return err.max()
+
+
+def oracle_rows(case, lens, scale, rows):
+    return oracle.decode(case["q"][rows], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
+                         case["block_tables"][rows], np.asarray(lens)[rows], scale)
+
+
+@pytest.mark.parametrize("scale_kind", ["inv_sqrt_d", "one"])
+def test_config1_tiny(scale_kind):
+    dev = gpu()
+    cfg = synth.CONFIGS[1]
+    case = synth.make_config_case(cfg)
+    scale = scales(cfg.head_dim)[0 if scale_kind == "inv_sqrt_d" else 1]
+    log(f"config 1 {cfg.name} scale={scale}")
+    out = decode_gpu(to_dev(case, dev), case["context_lens"], scale, dev)
+    ref = oracle.decode(case["q"], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
+                        case["block_tables"], case["context_lens"], scale)
+    check(out, ref, what="config1")
+
+
+@pytest.fixture(scope="module")
+def config2():
+    cfg = synth.CONFIGS[2]
+    return cfg, synth.make_config_case(cfg)
+
+
+@pytest.mark.parametrize("scale_kind", ["inv_sqrt_d", "one"])
+def test_config2_full(config2, scale_kind):
+    dev = gpu()
+    cfg, case = config2
+    scale = scales(cfg.head_dim)[0 if scale_kind == "inv_sqrt_d" else 1]
+    log(f"config 2 {cfg.name} scale={scale}")
+    out = decode_gpu(to_dev(case, dev), case["context_lens"], scale, dev)
+    ref = oracle.decode(case["q"], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
+                        case["block_tables"], case["context_lens"], scale)
+    check(out, ref, what="config2")
+
+
+def small_main_case(seed, lens, spare=0):
+    return synth.make_case(seed, len(lens), 32, 128, 64, 1024, np.asarray(lens, np.int32), spare_tokens=spare)
+
+
+@pytest.mark.parametrize("scale", [1.0 / math.sqrt(128), 1.0])
+def test_edge_lengths_and_empty_rows(scale):
+    dev = gpu()
+    lens = [1, 15, 16, 17, 255, 257, 0, 33, 2]
+    case = small_main_case(101, lens, spare=3)
+    log(f"edge lengths {lens} scale={scale}")
+    out = decode_gpu(to_dev(case, dev), lens, scale, dev)
+    got = out.float().cpu().numpy()
+    ref = oracle.decode(case["q"], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
+                        case["block_tables"], np.array(lens), scale)
+    assert np.array_equal(got[6], np.zeros_like(got[6])), "empty sequence must give a zero row"
+    check(got, ref, what="edge lengths")
+
+
+def test_all_empty_batch_is_zero():
+    dev = gpu()
+    lens = [0, 0, 0]
+    case = small_main_case(102, [16, 16, 16])
+    out = decode_gpu(to_dev(case, dev), lens, 0.1, dev, max_context_len=0)
+    assert not out.float().abs().sum().item()
+
+
+@pytest.mark.parametrize("cfg_id", [1, "main"])
+def test_block_table_permutation_bit_identical(cfg_id):
+    dev = gpu()
+    if cfg_id == 1:
+        case = synth.make_config_case(synth.CONFIGS[1])
+        lens = case["context_lens"]
+    else:
+        lens = [300, 47, 129, 512, 1]
+        case = small_main_case(103, lens)
+    moved = synth.permute_pool(case, 7)
+    log(f"permutation case {cfg_id}")
+    a = decode_gpu(to_dev(case, dev), lens, 1.0, dev).cpu().numpy()
+    b = decode_gpu(to_dev(moved, dev), lens, 1.0, dev).cpu().numpy()
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_unread_slots_never_read_bit_identical():
+    dev = gpu()
+    lens = [37, 16, 1, 250]
+    poisoned = small_main_case(104, lens, spare=9)
+    assert np.isnan(poisoned["k_pool"]).any()
+    clean = dict(poisoned)
+    clean["k_pool"] = np.nan_to_num(poisoned["k_pool"], nan=0.0)
+    clean["v_pool"] = np.nan_to_num(poisoned["v_pool"], nan=0.0)
+    junk_tables = poisoned["block_tables"].copy()
+    junk_tables[junk_tables < 0] = poisoned["num_blocks"] + 7     # never dereferenced
+    clean["block_tables"] = junk_tables
+    a = decode_gpu(to_dev(poisoned, dev), lens, 1.0, dev).cpu().numpy()
+    b = decode_gpu(to_dev(clean, dev), lens, 1.0, dev).cpu().numpy()
+    assert np.isfinite(a.astype(np.float32)).all()
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_workspace_reuse_is_deterministic():
+    import torch
+    import rank_compressed_paged_amd as starkv
+    dev = gpu()
+    lens = [400, 90, 1000]
+    case = small_main_case(105, lens)
+    g = to_dev(case, dev)
+    dims = starkv.dims_of(g["k_pool"], g["v_pool"], g["block_tables"], 128)
+    ws = torch.full((starkv.decode_workspace_size(dims, 3, 1000) + 256,), 0x7F, dtype=torch.uint8, device=dev)
+    a = decode_gpu(g, lens, 1.0, dev, max_context_len=1000, workspace=ws).cpu().numpy()
+    b = decode_gpu(g, lens, 1.0, dev, max_context_len=1000, workspace=ws).cpu().numpy()
+    c = decode_gpu(g, lens, 1.0, dev, max_context_len=4096).cpu().numpy()   # looser bound, other plan
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    ref = oracle.decode(case["q"], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
+                        case["block_tables"], np.array(lens), 1.0)
+    check(a, ref, what="workspace reuse")
+    check(c, ref, what="looser max_context_len")
+
+
+@pytest.mark.parametrize("batch", [8, 40])
+def test_batch_paths_valu_and_partial_mfma_tiles(batch):
+    """batch < 16 takes the VALU projections; 40 leaves a partial 32-row MFMA tile."""
+    dev = gpu()
+    rng = np.random.default_rng(batch)
+    lens = rng.integers(1, 700, size=batch)
+    case = small_main_case(106 + batch, lens)
+    log(f"batch {batch}")
+    out = decode_gpu(to_dev(case, dev), lens, 1.0, dev)
+    ref = oracle.decode(case["q"], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
+                        case["block_tables"], lens, 1.0)
+    check(out, ref, what=f"batch {batch}")
+
+
+def test_ranges_spanning_many_sequences():
+    """Short sequences: one workgroup range crosses far more sequences than it
+    stages up front, so later sequences take the in-loop q~ staging path."""
+    dev = gpu()
+    rng = np.random.default_rng(9)
+    lens = rng.integers(1, 40, size=200)
+    lens[::17] = 0
+    case = small_main_case(107, lens)
+    out = decode_gpu(to_dev(case, dev), lens, 1.0, dev)
+    ref = oracle.decode(case["q"], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
+                        case["block_tables"], lens, 1.0)
+    got = out.float().cpu().numpy()
+    assert not np.abs(got[lens == 0]).any()
+    live = lens > 0
+    check(got[live], ref[live], what="many short sequences")
+
+
+# ------------------------------------------------------------- full sizes
+@pytest.fixture(scope="module")
+def config3():
+    cfg = synth.CONFIGS[3]
+    log("generating config 3 (batch 64, seq 8192)")
+    return cfg, synth.make_config_case(cfg)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("scale_kind", ["inv_sqrt_d", "one"])
+def test_config3_full_size_sampled(config3, scale_kind):
+    dev = gpu()
+    cfg, case = config3
+    scale = scales(cfg.head_dim)[0 if scale_kind == "inv_sqrt_d" else 1]
+    log(f"config 3 {cfg.name} scale={scale}")
+    g = to_dev(case, dev)
+    out = decode_gpu(g, case["context_lens"], scale, dev)
+    rows = np.array([0, 21, 42, 63])
+    ref = oracle_rows(case, case["context_lens"], scale, rows)
+    check(out, ref, rows=rows, what="config3 sampled")
+    del g
+
+
+@pytest.mark.slow
+def test_config4_ragged_append_then_decode():
+    import torch
+    import rank_compressed_paged_amd as starkv
+    dev = gpu()
+    cfg = synth.CONFIGS[4]
+    steps = 3
+    case = synth.make_config_case(cfg, spare_tokens=steps)
+    lens0 = case["context_lens"].copy()
+    log(f"config 4 {cfg.name}: {steps} append+decode steps, total tokens {int(lens0.sum())}")
+    g = to_dev(case, dev)
+    seqs = np.arange(cfg.batch, dtype=np.int32)
+    kp, vp = case["k_pool"], case["v_pool"]
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    for s in range(steps):
+        k_new, v_new = synth.make_new_rows(cfg.seed, cfg.batch, cfg.heads, cfg.head_dim, key=(s,))
+        pos = (lens0 + s).astype(np.int32)
+        starkv.append(torch.from_numpy(k_new).to(dev), torch.from_numpy(v_new).to(dev), g["b_k"], g["b_v"],
+                      g["block_tables"], torch.from_numpy(seqs).to(dev), torch.from_numpy(pos).to(dev),
+                      g["k_pool"], g["v_pool"])
+        out = decode_gpu(g, pos + 1, scale, dev, max_context_len=int(pos.max()) + 1)
+        kp, vp = oracle.append(k_new, v_new, case["b_k"], case["b_v"], case["block_tables"], seqs, pos, kp, vp)
+    lens = lens0 + steps
+    rows = np.array([0, 7, 19, 30, 47])
+    ref = oracle.decode(case["q"][rows], case["b_k"], case["b_v"], kp, vp, case["block_tables"][rows],
+                        lens[rows], scale)
+    check(out, ref, rows=rows, what="config4 after appends")
+    # the appended latents match the oracle's to 1 fp16 step; nothing else moved
+    from helpers import fp16_ulp_diff
+    gk = g["k_pool"].cpu().numpy()
+    gv = g["v_pool"].cpu().numpy()
+    bt = case["block_tables"]
+    for s in range(steps):
+        for b in range(cfg.batch):
+            p, j = bt[b, (lens0[b] + s) // 16], (lens0[b] + s) % 16
+            assert fp16_ulp_diff(gk[p, :, j, :], kp[p, :, j, :]).max() <= 1
+            assert fp16_ulp_diff(gv[p, :, j], vp[p, :, j]).max() <= 1
+            gk[p, :, j, :] = kp[p, :, j, :]
+            gv[p, :, j] = vp[p, :, j]
+    assert np.array_equal(gk.view(np.uint16), kp.view(np.uint16))
+    assert np.array_equal(gv.view(np.uint16), vp.view(np.uint16))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", [0, 31])
+def test_config5_layer_full_size_sampled(layer):
+    dev = gpu()
+    cfg = synth.CONFIGS[5]
+    case = synth.make_config_case(cfg, layer=layer)
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    log(f"config 5 layer {layer}: batch 4, seq 32768")
+    out = decode_gpu(to_dev(case, dev), case["context_lens"], scale, dev)
+    rows = np.array([0, 3])
+    ref = oracle_rows(case, case["context_lens"], scale, rows)
+    check(out, ref, rows=rows, what=f"config5 layer {layer}")
