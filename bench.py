@@ -1,0 +1,205 @@
+"""Benchmark of the STAR-KV decode hot path on one MI355X.
+
+A step is one pass of the whole path over the batch: append one new K/V row
+per sequence into the latent paged cache (projection + scatter), then decode
+every sequence over its latent cache (query projection, latent scores, split
+softmax, V-latent accumulation, merge, up-projection).  Workload: batch 64,
+32 heads, head_dim 128, r_k 64, r_v 1024, 8192 cached tokens per sequence;
+each step writes the token at position 8192 (overwriting the previous step's,
+so every step does identical work) and decodes over 8193 tokens.
+
+Prints one JSON line.  Options:
+  --steps K --warmup W     timed / untimed steps (default 50 / 5)
+  --gpus N                 only 1 is supported (one GPU per box)
+  --no-cpu-baseline        skip the oracle timing
+  --calib-copy             run only a plain device copy of known size (for
+                           scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s and achieved HBM GB/s (32h, d=128, r_k=64) at batch 64, seq 8192"
+PEAK_HBM_GBPS = 8000.0
+COPY_BYTES = 1 << 31
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_b64_l8192_traffic.json")
+KERNEL_SOURCES = ["rank_compressed_paged_amd/csrc/decode_kernels.hip", "rank_compressed_paged_amd/csrc/common.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(units: int):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs,
+    or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("tokens_per_launch") != units:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def calib_copy():
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": COPY_BYTES, "calib_copy_bytes_written": COPY_BYTES,
+                      "launches": 3}), flush=True)
+
+
+def cpu_baseline(case, cfg, k_new, v_new, scale, budget_s=12.0):
+    """The oracle as it stands, on a bounded sample: whole steps (append the new
+    token + decode over 8193 tokens) for as many sequences as fit the budget."""
+    import oracle
+    bt = case["block_tables"]
+    lens = case["context_lens"]
+    done = 0
+    t0 = time.perf_counter()
+    while done < cfg.batch and (done == 0 or time.perf_counter() - t0 < budget_s):
+        b = done
+        nblk = (int(lens[b]) + 1 + 15) // 16
+        blocks = bt[b, :nblk]
+        # compact pool holding only this sequence's blocks (input preparation)
+        kp = case["k_pool"][blocks]
+        vp = case["v_pool"][blocks]
+        table = np.arange(nblk, dtype=np.int32)[None]
+        kp, vp = oracle.append(k_new[b:b + 1], v_new[b:b + 1], case["b_k"], case["b_v"], table,
+                               [0], [int(lens[b])], kp, vp)
+        oracle.decode(case["q"][b:b + 1], case["b_k"], case["b_v"], kp, vp, table,
+                      np.array([int(lens[b]) + 1]), scale)
+        done += 1
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {cfg.batch} sequences, one full step each (append 1 token + decode over "
+                      f"{int(lens[0]) + 1} tokens), fp64 numpy, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.calib_copy:
+        calib_copy()
+        return
+
+    import torch
+
+    import rank_compressed_paged_amd as starkv
+    from rank_compressed_paged_amd import synth
+
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[3]
+    t_gen = time.perf_counter()
+    case = synth.make_config_case(cfg, spare_tokens=1)
+    k_new, v_new = synth.make_new_rows(cfg.seed, cfg.batch, cfg.heads, cfg.head_dim)
+    print(f"# inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    g = {k: torch.from_numpy(v).to(dev) for k, v in case.items() if isinstance(v, np.ndarray)}
+    kn = torch.from_numpy(k_new).to(dev)
+    vn = torch.from_numpy(v_new).to(dev)
+    seqs = torch.arange(cfg.batch, dtype=torch.int32, device=dev)
+    pos_np = case["context_lens"].astype(np.int32)
+    pos = torch.from_numpy(pos_np).to(dev)
+    lens = pos + 1
+    max_len = int(pos_np.max()) + 1
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    dims = starkv.dims_of(g["k_pool"], g["v_pool"], g["block_tables"], cfg.head_dim)
+    ws = torch.empty(starkv.decode_workspace_size(dims, cfg.batch, max_len) + 256, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(g["q"])
+
+    def step():
+        starkv.append(kn, vn, g["b_k"], g["b_v"], g["block_tables"], seqs, pos, g["k_pool"], g["v_pool"])
+        starkv.decode(g["q"], g["b_k"], g["b_v"], g["k_pool"], g["v_pool"], g["block_tables"], lens, scale,
+                      max_context_len=max_len, workspace=ws, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starkv.profile_begin()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    attn_ms, launches = starkv.profile_end()
+    assert launches == args.steps, (launches, args.steps)
+    assert torch.isfinite(out.float()).all().item()
+
+    ms_step = 1e3 * dt / args.steps
+    tokens_per_s = cfg.batch * args.steps / dt
+    tokens = int(lens.sum().item())
+    latent_bytes = tokens * cfg.latent_bytes_per_token()          # algorithmic bytes per attention launch
+    attn_avg_s = attn_ms / launches / 1e3
+    achieved = latent_bytes / attn_avg_s / 1e9
+    traffic = measured_traffic(tokens)
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "b64_l8192: batch 64, 32 heads, head_dim 128, r_k 64, r_v 1024, 8192 cached tokens "
+                        "per sequence, block size 16; step = append 1 token/sequence + decode over 8193",
+            "global_batch": cfg.batch, "seq_len": max_len, "parallelism": "single_gpu",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+        },
+        "attn_kernel_us": attn_avg_s * 1e6,
+        "latent_bytes_per_step": latent_bytes,
+        "step_latent_gbps": latent_bytes / (dt / args.steps) / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, cfg, k_new, v_new, scale)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -72,3 +72,24 @@ def fp16_ulp_diff(a, b):
         x = np.asarray(x).view(np.uint16).astype(np.int32)
         return np.where(x & 0x8000, 0x8000 - (x & 0x7FFF), 0x8000 + x)   # monotone, -0 == +0
     return np.abs(ordered(a) - ordered(b))
+
+
+def fp16_ulp(x):
+    """Spacing of fp16 numbers at |x| (subnormal spacing below 2^-14)."""
+    ax = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -14)))
+    return 2.0 ** (e - 10)
+
+
+def check_latents(got16, exact, abssum, terms):
+    """Append latents: the kernel rounds an fp32-accumulated dot product once to
+    fp16, so |got - exact| <= ulp16/2 + (terms/16 + 8) * 2^-24 * sum|w x|
+    (fp32 rounding on the longest accumulation path of 16-term MFMA steps).
+    Returns the fraction of latents within one fp16 step of round(exact)."""
+    got = np.asarray(got16).astype(np.float64)
+    slack = (terms / 16 + 8) * 2.0 ** -24 * abssum
+    bound = 0.5 * fp16_ulp(np.maximum(np.abs(exact), np.abs(got))) + slack
+    bad = np.abs(got - exact) > bound
+    assert not bad.any(), f"{bad.sum()} latents beyond the fp32-accumulation bound"
+    near = fp16_ulp_diff(np.asarray(got16), exact.astype(np.float16)) <= 1
+    return float(np.mean(near))

@@ -4,8 +4,9 @@ The scatter is integer work and is checked bit-exactly on the whole pool
 image.  Latent values are floating point: with an exact projection (a
 selection matrix, or the hand-worked values whose sums are exact in fp32) they
 must match bit for bit; with a general projection the fp32-accumulate-then-
-round kernel may land one fp16 step from the oracle's single rounding of the
-exact value, so they are compared at <= 1 fp16 step.
+round kernel is held to the a-priori fp32 accumulation bound around the exact
+value (one fp16 step away from the oracle for well-conditioned latents, more
+only where the dot product cancels to near zero).
 """
 
 import json
@@ -15,7 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
-from helpers import fp16_ulp_diff, gpu, log, to_dev
+from helpers import check_latents, fp16_ulp_diff, gpu, log, to_dev
 from rank_compressed_paged_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -109,10 +110,26 @@ def test_append_general_projection_within_one_step(n_per_seq):
     kp, vp = gpu_append(to_dev(case, dev), k, v, case["b_k"], case["b_v"], seqs, poss, dev)
     ek, ev = oracle.append(k, v, case["b_k"], case["b_v"], case["block_tables"], seqs, poss,
                            case["k_pool"], case["v_pool"])
+    # exact latents and the size of their terms, in fp64
+    wk = case["b_k"].astype(np.float64)
+    wv = case["b_v"].astype(np.float64)
+    kx = k.astype(np.float64)
+    vx = v.astype(np.float64).reshape(len(seqs), -1)
+    ck_exact = np.einsum("hrd,thd->thr", wk, kx)
+    ck_abs = np.einsum("hrd,thd->thr", np.abs(wk), np.abs(kx))
+    cv_exact = vx @ wv.T
+    cv_abs = np.abs(vx) @ np.abs(wv).T
+    bt = case["block_tables"]
+    phys = np.array([bt[b, p // 16] for b, p in zip(seqs, poss)])
+    slot = poss % 16
+    gk = kp[phys, :, slot, :]                           # [n, H, r_k]
+    gv = vp[phys, :, slot]                              # [n, r_v]
+    near_k = check_latents(gk, ck_exact, ck_abs, d)
+    near_v = check_latents(gv, cv_exact, cv_abs, H * d)
     dk = fp16_ulp_diff(kp, ek)
     dv = fp16_ulp_diff(vp, ev)
-    log(f"  max fp16 steps: K {dk.max()}, V {dv.max()}; exact fraction K {np.mean(dk == 0):.4f}")
-    assert dk.max() <= 1 and dv.max() <= 1
+    log(f"  vs oracle: max fp16 steps K {dk.max()}, V {dv.max()}; within 1 step K {near_k:.5f}, V {near_v:.5f}")
+    assert near_k > 0.999 and near_v > 0.99
     # untouched slots (including NaN sentinels) are bit-identical
     touched_k = np.zeros(kp.shape[0:1] + (16,), bool)
     for b, p in zip(seqs, poss):

@@ -131,13 +131,13 @@ def test_workspace_reuse_is_deterministic():
     import rank_compressed_paged_amd as starkv
     dev = gpu()
     lens = [400, 90, 1000]
-    case = small_main_case(105, lens)
+    case = small_main_case(105, lens, spare=3000)      # wide tables: room for a looser bound
     g = to_dev(case, dev)
     dims = starkv.dims_of(g["k_pool"], g["v_pool"], g["block_tables"], 128)
     ws = torch.full((starkv.decode_workspace_size(dims, 3, 1000) + 256,), 0x7F, dtype=torch.uint8, device=dev)
     a = decode_gpu(g, lens, 1.0, dev, max_context_len=1000, workspace=ws).cpu().numpy()
     b = decode_gpu(g, lens, 1.0, dev, max_context_len=1000, workspace=ws).cpu().numpy()
-    c = decode_gpu(g, lens, 1.0, dev, max_context_len=4096).cpu().numpy()   # looser bound, other plan
+    c = decode_gpu(g, lens, 1.0, dev, max_context_len=4000).cpu().numpy()   # looser bound, other plan
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
     ref = oracle.decode(case["q"], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
                         case["block_tables"], np.array(lens), 1.0)
@@ -226,18 +226,25 @@ def test_config4_ragged_append_then_decode():
     ref = oracle.decode(case["q"][rows], case["b_k"], case["b_v"], kp, vp, case["block_tables"][rows],
                         lens[rows], scale)
     check(out, ref, rows=rows, what="config4 after appends")
-    # the appended latents match the oracle's to 1 fp16 step; nothing else moved
-    from helpers import fp16_ulp_diff
+    # appended latents within the fp32-accumulation bound of the exact values;
+    # every other pool element is bit-identical to the oracle's pools
+    from helpers import check_latents
     gk = g["k_pool"].cpu().numpy()
     gv = g["v_pool"].cpu().numpy()
     bt = case["block_tables"]
+    wk = case["b_k"].astype(np.float64)
+    wv = case["b_v"].astype(np.float64)
     for s in range(steps):
-        for b in range(cfg.batch):
-            p, j = bt[b, (lens0[b] + s) // 16], (lens0[b] + s) % 16
-            assert fp16_ulp_diff(gk[p, :, j, :], kp[p, :, j, :]).max() <= 1
-            assert fp16_ulp_diff(gv[p, :, j], vp[p, :, j]).max() <= 1
-            gk[p, :, j, :] = kp[p, :, j, :]
-            gv[p, :, j] = vp[p, :, j]
+        k_new, v_new = synth.make_new_rows(cfg.seed, cfg.batch, cfg.heads, cfg.head_dim, key=(s,))
+        pos = lens0 + s
+        p, j = bt[seqs, pos // 16], pos % 16
+        kx = k_new.astype(np.float64)
+        vx = v_new.astype(np.float64).reshape(cfg.batch, -1)
+        check_latents(gk[p, :, j, :], np.einsum("hrd,thd->thr", wk, kx),
+                      np.einsum("hrd,thd->thr", np.abs(wk), np.abs(kx)), cfg.head_dim)
+        check_latents(gv[p, :, j], vx @ wv.T, np.abs(vx) @ np.abs(wv).T, cfg.heads * cfg.head_dim)
+        gk[p, :, j, :] = kp[p, :, j, :]
+        gv[p, :, j] = vp[p, :, j]
     assert np.array_equal(gk.view(np.uint16), kp.view(np.uint16))
     assert np.array_equal(gv.view(np.uint16), vp.view(np.uint16))
 
