@@ -27,6 +27,8 @@ struct SlotOf {
 };
 
 // K side, MFMA: one wave computes a [32 tokens x 32 latents] tile of one head.
+// The destination slots and all operand loads are issued before the first
+// MFMA, so the launch costs about one memory latency.
 __global__ void __launch_bounds__(64)
 append_k_mfma_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int n, int H, int D, int RK,
                      SlotOf where, f16* __restrict__ kc) {
@@ -36,24 +38,37 @@ append_k_mfma_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int 
   const int h = (blockIdx.x / rtiles) % H;
   const int tt = blockIdx.x / (rtiles * H);
   const int t = tt * 32 + (lane & 31);
+  const bool trow = t < n;
   const int r = rt * 32 + (lane & 31);
   const int kofs = (lane >> 5) * 8;
-  floatx16 acc = {};
-  for (int k0 = 0; k0 < D; k0 += 16) {
-    half8 a = {};
-    if (t < n) a = *reinterpret_cast<const half8*>(k + ((size_t)t * H + h) * D + k0 + kofs);
-    const half8 b = *reinterpret_cast<const half8*>(wk + ((size_t)h * RK + r) * D + k0 + kofs);
-    acc = mfma32x32x16(a, b, acc);
-  }
+  size_t dst[16];
 #pragma unroll
   for (int reg = 0; reg < 16; ++reg) {
-    const int ti = tt * 32 + mfma_row(reg, lane);
-    if (ti < n) {
-      int phys, slot;
-      where(ti, phys, slot);
-      kc[(((size_t)phys * H + h) * kBlock + slot) * RK + r] = (f16)acc[reg];
+    const int ti = min(tt * 32 + mfma_row(reg, lane), n - 1);
+    int phys, slot;
+    where(ti, phys, slot);
+    dst[reg] = (((size_t)phys * H + h) * kBlock + slot) * RK + r;
+  }
+  const f16* xrow = k + ((size_t)(trow ? t : n - 1) * H + h) * D + kofs;
+  const f16* wrow = wk + ((size_t)h * RK + r) * D + kofs;
+  const int ksteps = D / 16;
+  floatx16 acc = {};
+  for (int c = 0; c < ksteps; c += 8) {
+    half8 a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k0 = min(c + u, ksteps - 1) * 16;
+      a[u] = *reinterpret_cast<const half8*>(xrow + k0);
+      b[u] = *reinterpret_cast<const half8*>(wrow + k0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (c + u < ksteps) acc = mfma32x32x16(trow ? a[u] : half8{}, b[u], acc);
     }
   }
+#pragma unroll
+  for (int reg = 0; reg < 16; ++reg)
+    if (tt * 32 + mfma_row(reg, lane) < n) kc[dst[reg]] = (f16)acc[reg];
 }
 
 // K side, VALU: one thread per (token, head, latent).
@@ -79,42 +94,55 @@ append_k_valu_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int 
   kc[(((size_t)phys * H + h) * kBlock + slot) * RK + r] = (f16)acc;
 }
 
-// V side, MFMA: a workgroup computes a [32 tokens x 32 latents] tile; its four
-// waves split the H*d contraction and reduce through LDS.
-__global__ void __launch_bounds__(256)
+// V side, MFMA: a workgroup computes a [32 tokens x 32 latents] tile; its 16
+// waves split the H*d contraction (all loads of eight k-steps in flight before
+// the first MFMA) and reduce through LDS.
+constexpr int kAppendVWaves = 16;
+
+__global__ void __launch_bounds__(kAppendVWaves * 64)
 append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
                      SlotOf where, f16* __restrict__ vc) {
-  __shared__ float red[4][16][64];
+  __shared__ float red[kAppendVWaves][16][64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int jtiles = RV / 32;
   const int jt = blockIdx.x % jtiles;
   const int tt = blockIdx.x / jtiles;
   const int t = tt * 32 + (lane & 31);
+  const bool trow = t < n;
   const int j = jt * 32 + (lane & 31);
   const int kofs = (lane >> 5) * 8;
-  const int kspan = K / 4;
+  const int ksteps = K / (16 * kAppendVWaves);
+  const int kbase = w * ksteps * 16;
+  const f16* xrow = v + (size_t)(trow ? t : n - 1) * K + kofs;
+  const f16* wrow = wv + (size_t)j * K + kofs;
   floatx16 acc = {};
-  for (int k0 = w * kspan; k0 < (w + 1) * kspan; k0 += 16) {
-    half8 a = {};
-    if (t < n) a = *reinterpret_cast<const half8*>(v + (size_t)t * K + k0 + kofs);
-    const half8 b = *reinterpret_cast<const half8*>(wv + (size_t)j * K + k0 + kofs);
-    acc = mfma32x32x16(a, b, acc);
+  for (int c = 0; c < ksteps; c += 8) {
+    half8 a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k0 = kbase + min(c + u, ksteps - 1) * 16;
+      a[u] = *reinterpret_cast<const half8*>(xrow + k0);
+      b[u] = *reinterpret_cast<const half8*>(wrow + k0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (c + u < ksteps) acc = mfma32x32x16(trow ? a[u] : half8{}, b[u], acc);
+    }
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) red[w][r][lane] = acc[r];
   __syncthreads();
-  if (w == 0) {
+  // wave w finishes accumulator register w (16 waves, 16 registers)
+  const int r = w;
+  float sum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int ti = tt * 32 + mfma_row(r, lane);
-      if (ti < n) {
-        const float s = red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane];
-        int phys, slot;
-        where(ti, phys, slot);
-        vc[((size_t)phys * RV + j) * kBlock + slot] = (f16)s;
-      }
-    }
+  for (int x = 0; x < kAppendVWaves; ++x) sum += red[x][r][lane];
+  const int ti = tt * 32 + mfma_row(r, lane);
+  if (ti < n) {
+    int phys, slot;
+    where(ti, phys, slot);
+    vc[((size_t)phys * RV + j) * kBlock + slot] = (f16)sum;
   }
 }
 
@@ -178,10 +206,10 @@ hipError_t append_enqueue(const AppendLaunch& a) {
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (a.n >= 16 && s.RV % 32 == 0 && K % 64 == 0) {
+  if (a.n >= 16 && s.RV % 32 == 0 && K % (16 * kAppendVWaves) == 0) {
     const int grid = ((a.n + 31) / 32) * (s.RV / 32);
-    hipLaunchKernelGGL(append_v_mfma_kernel, dim3(grid), dim3(256), 0, a.stream, v, wv, a.n, K, s.RV, where,
-                       vc);
+    hipLaunchKernelGGL(append_v_mfma_kernel, dim3(grid), dim3(kAppendVWaves * 64), 0, a.stream, v, wv, a.n, K,
+                       s.RV, where, vc);
   } else {
     const dim3 grid((s.RV + 3) / 4, (a.n + kAppendGroup - 1) / kAppendGroup);
     hipLaunchKernelGGL(append_v_valu_kernel, grid, dim3(256), 0, a.stream, v, wv, a.n, K, s.RV, where, vc);

@@ -57,6 +57,9 @@ int attn_resident_grid(int H, int RK, int RV, int device);
 
 hipError_t decode_enqueue(const DecodeLaunch& a);
 
+// The latent attention launch (one kernel; qt, plan, pz, pml live in a.ws).
+hipError_t launch_attn_kernel(const DecodeLaunch& a, const float* qt, int32_t* plan, float* pz, float* pml);
+
 struct AppendLaunch {
   Shape s;
   int n;
