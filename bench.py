@@ -12,6 +12,7 @@ Prints one JSON line.  Options:
   --steps K --warmup W     timed / untimed steps (default 50 / 5)
   --gpus N                 only 1 is supported (one GPU per box)
   --no-cpu-baseline        skip the oracle timing
+  --no-ceiling             skip the HBM read-ceiling probe
   --calib-copy             run only a plain device copy of known size (for
                            scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
 """
@@ -70,6 +71,36 @@ def calib_copy():
                       "launches": 3}), flush=True)
 
 
+def read_ceiling(dev, nbytes=1 << 32, reps=5):
+    """Best sustained plain sequential HBM read rate of this GPU (own probe kernel)."""
+    import torch
+    import rank_compressed_paged_amd as starkv
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    best = (0.0, None)
+    for block in (256, 512, 1024):
+        for per_cu in (1, 2, 4, 8):
+            grid = cus * per_cu
+            if block * per_cu > 2048:
+                continue
+            starkv.stream_read_probe(buf, sink, grid, block)
+            times = []
+            for _ in range(reps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                starkv.stream_read_probe(buf, sink, grid, block)
+                e1.record()
+                e1.synchronize()
+                times.append(e0.elapsed_time(e1) / 1e3)
+            gbps = nbytes / sorted(times)[len(times) // 2] / 1e9
+            if gbps > best[0]:
+                best = (gbps, {"grid": grid, "block": block})
+    del buf
+    return {"gbps": best[0], "bytes": nbytes, **best[1]}
+
+
 def cpu_baseline(case, cfg, k_new, v_new, scale, budget_s=12.0):
     """The oracle as it stands, on a bounded sample: whole steps (append the new
     token + decode over 8193 tokens) for as many sequences as fit the budget."""
@@ -109,6 +140,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the HBM read-ceiling probe")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr, flush=True)
@@ -196,6 +228,10 @@ def main():
         "latent_bytes_per_step": latent_bytes,
         "step_latent_gbps": latent_bytes / (dt / args.steps) / 1e9,
     }
+    if not args.no_ceiling:
+        ceiling = read_ceiling(dev)
+        line["hbm_read_ceiling"] = ceiling
+        line["attn_frac_of_read_ceiling"] = achieved / ceiling["gbps"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, cfg, k_new, v_new, scale)
     print(json.dumps(line), flush=True)

@@ -151,6 +151,17 @@ const char* starkv_status_string(starkv_status status);
 starkv_status starkv_profile_begin(void);
 starkv_status starkv_profile_end(double* attn_kernel_ms, int32_t* launches);
 
+/*
+ * starkv_stream_read_probe - measurement kernel, not part of the method: reads
+ * `bytes` (a multiple of 16) from device buffer `src` (16-byte aligned) once,
+ * sequentially, with `grid` workgroups of `block` threads (64..1024, multiple
+ * of 64), so a caller can time the plain HBM read ceiling that the latent scan
+ * is compared with.  `sink` (device, >= grid uint32) may be written.
+ * INVALID_ARG on bad arguments; asynchronous on `stream`.
+ */
+starkv_status starkv_stream_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t grid,
+                                       int32_t block, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

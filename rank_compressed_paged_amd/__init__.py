@@ -13,7 +13,7 @@ import os
 
 __all__ = [
     "Dims", "StarkvError", "load_library", "library_path", "status_string",
-    "decode_workspace_size", "decode", "append", "profile_begin", "profile_end",
+    "decode_workspace_size", "decode", "append", "profile_begin", "profile_end", "stream_read_probe",
     "BLOCK_SIZE",
 ]
 
@@ -76,6 +76,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.starkv_profile_begin.restype = ctypes.c_int
     lib.starkv_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
     lib.starkv_profile_end.restype = ctypes.c_int
+    lib.starkv_stream_read_probe.argtypes = [vp, sz, vp, i32, i32, vp]
+    lib.starkv_stream_read_probe.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -194,6 +196,17 @@ def append(k, v, w_k, w_v, block_tables, token_seq, token_pos, k_cache, v_cache,
         raise ValueError("down-projection shapes do not match the caches")
     code = lib.starkv_append(ctypes.byref(dims), n, *[ctypes.c_void_p(p) for p in ptrs], _stream(stream))
     _check(code, "starkv_append")
+
+
+def stream_read_probe(buf, sink, grid: int, block: int, stream=None):
+    """Launch the HBM stream-read probe over the whole of `buf` (uint8, GPU)."""
+    import torch
+    p = _need(buf, "buf", torch.uint8, 1)
+    sp = _need(sink, "sink", torch.int32, 1)
+    if sink.numel() < grid:
+        raise ValueError("sink needs one int32 per workgroup")
+    _check(load_library().starkv_stream_read_probe(ctypes.c_void_p(p), buf.numel() // 16 * 16, ctypes.c_void_p(sp),
+                                                    grid, block, _stream(stream)), "starkv_stream_read_probe")
 
 
 def profile_begin():
