@@ -59,8 +59,16 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
             float* __restrict__ part_z, float* __restrict__ part_ml, float tau) {
   using C = AttnCfg<H, RK, RV, NW>;
   __shared__ float s_lds[2][32][kBlock];
-  constexpr int QCAP = 4;            // sequences whose q~ is staged up front
+  constexpr int QCAP = 2;            // sequences whose q~ is staged up front
   __shared__ __attribute__((aligned(16))) float q_lds[QCAP][H * RK];
+  // Partial-state stash.  On gfx9 stores share the in-order vector-memory
+  // counter with the latent prefetch, so a partial written in the middle of a
+  // range makes later prefetch waits also wait for those stores, which drain
+  // slowly while every CU is streaming reads.  The first partial that ends
+  // inside the range therefore waits here and is written after the last
+  // latent load (a range ends at most one sequence boundary in uniform
+  // batches; later ones in the same range are written directly).
+  __shared__ float stash[NW][C::TPW][16][64];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -98,17 +106,22 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
   auto piece_head = [&](int j) { return ((w * C::PPW + j) * 512 + lane * 8) / C::kHeadHalves; };
   auto piece_tok = [&](int j) { return (((w * C::PPW + j) * 512 + lane * 8) / RK) % kBlock; };
 
-  auto load_k = [&](half8 (&dst)[C::PPW], int phys) {
+  // Latents are read exactly once: non-temporal loads stream them past the
+  // caches instead of evicting the small reused data (q~, tables, partials).
+  // `spare` loads (issued only to keep the in-order wait counts exact, see
+  // below) make every wave read the same first piece of a block it already
+  // holds, so they cost one cached 1 KiB row per wave instead of a block.
+  auto load_k = [&](half8 (&dst)[C::PPW], int phys, bool spare) {
     const half8* base = reinterpret_cast<const half8*>(kpool + (size_t)phys * C::kBlockKHalves) +
-                        (w * C::PPW) * 64 + lane;
+                        (spare ? 0 : (w * C::PPW) * 64) + lane;
 #pragma unroll
-    for (int j = 0; j < C::PPW; ++j) dst[j] = base[j * 64];
+    for (int j = 0; j < C::PPW; ++j) dst[j] = __builtin_nontemporal_load(base + j * 64);
   };
-  auto load_v = [&](half8 (&dst)[C::TPW], int phys) {
+  auto load_v = [&](half8 (&dst)[C::TPW], int phys, bool spare) {
     const half8* base = reinterpret_cast<const half8*>(vpool + (size_t)phys * (RV * kBlock)) +
-                        ((w * C::TPW) * 32 + (lane & 31)) * 2 + (lane >> 5);
+                        ((spare ? 0 : (w * C::TPW) * 32) + (lane & 31)) * 2 + (lane >> 5);
 #pragma unroll
-    for (int t = 0; t < C::TPW; ++t) dst[t] = base[t * 64];
+    for (int t = 0; t < C::TPW; ++t) dst[t] = __builtin_nontemporal_load(base + t * 64);
   };
 
   half8 kb[2][C::PPW];
@@ -135,20 +148,44 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
   __syncthreads();
   const float* qcur = q_lds[0];
 
-  // Every body issues the same loads on every path (past the range end it
-  // re-reads the current block), so the compiler's in-order wait counts stay
-  // exact instead of collapsing to a full drain.
+  // Block i is consumed from buffer (i - start) & 1 while blocks i+1 and i+2
+  // are in flight.  Every body issues the same loads on every path (past the
+  // range end they are `spare` re-reads), so the compiler's in-order wait
+  // counts stay exact instead of collapsing to a full drain.
   It pf = cur;                       // next block to prefetch
   const int phys0 = phys_of(pf);
-  load_k(kb[0], phys0);
-  load_v(vb[0], phys0);
+  load_k(kb[0], phys0, false);
+  load_v(vb[0], phys0, false);
   advance(pf);
   {
-    const int phys1 = (pf.gi < end) ? phys_of(pf) : phys0;
-    load_k(kb[1], phys1);
-    load_v(vb[1], phys1);
-    if (pf.gi < end) advance(pf);
+    const bool more = pf.gi < end;
+    const int phys1 = more ? phys_of(pf) : phys0;
+    load_k(kb[1], phys1, !more);
+    load_v(vb[1], phys1, !more);
+    if (more) advance(pf);
   }
+
+  // register r of lane l holds row (r&3) + 8(r>>2) + 4(l>>5): the r part goes
+  // into a uniform base, the lane part into one 32-bit offset
+  auto store_partial = [&](int pslot, auto value, float m, float l) {
+    float* zp = part_z + (size_t)pslot * H * RV;
+    const int lane_off = 4 * half_ * RV + w * C::TPW * 32 + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rrow = (r & 3) + 8 * (r >> 2);
+      if (rrow >= H) continue;                         // compile-time for H = 32
+      float* zr = zp + (size_t)rrow * RV;
+#pragma unroll
+      for (int t = 0; t < C::TPW; ++t)
+        if (rrow + 4 * half_ < H) zr[lane_off + t * 32] = value(t, r);
+    }
+    if (w == 0 && half_ == 0 && row_live) {
+      part_ml[((size_t)pslot * H + h) * 2 + 0] = m;
+      part_ml[((size_t)pslot * H + h) * 2 + 1] = l;
+    }
+  };
+  int stash_slot = -1;
+  float stash_m = 0.f, stash_l = 0.f;
 
   auto body = [&](auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
@@ -194,7 +231,7 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     }
     const bool more = pf.gi < end;
     const int pphys = more ? phys_of(pf) : cphys;
-    load_k(kb[BUF], pphys);
+    load_k(kb[BUF], pphys, !more);
     __syncthreads();
 
     // online softmax in the MFMA A-operand layout: row h, tokens 8*half_..+7
@@ -245,23 +282,20 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     }
 #pragma unroll
     for (int t = 0; t < C::TPW; ++t) acc[t] = mfma32x32x16(pf16, vb[BUF][t], acc[t]);
-    load_v(vb[BUF], pphys);
+    load_v(vb[BUF], pphys, !more);
     if (more) advance(pf);
 
     if (seg_last) {
-      float* zp = part_z + (size_t)slot * H * RV;
+      if (cur.gi + 1 != end && stash_slot < 0) {
 #pragma unroll
-      for (int t = 0; t < C::TPW; ++t) {
-        const int dim = (w * C::TPW + t) * 32 + (lane & 31);
+        for (int t = 0; t < C::TPW; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = mfma_row(r, lane);
-          if (row < H) zp[(size_t)row * RV + dim] = acc[t][r];
-        }
-      }
-      if (w == 0 && half_ == 0 && row_live) {
-        part_ml[((size_t)slot * H + h) * 2 + 0] = m_run;
-        part_ml[((size_t)slot * H + h) * 2 + 1] = l_run;
+          for (int r = 0; r < 16; ++r) stash[w][t][r][lane] = acc[t][r];
+        stash_slot = slot;
+        stash_m = m_run;
+        stash_l = l_run;
+      } else {
+        store_partial(slot, [&](int t, int r) { return acc[t][r]; }, m_run, l_run);
       }
     }
     advance(cur);
@@ -274,6 +308,8 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     body(IC<1>{});
   }
   if (i < end) body(IC<0>{});
+  if (stash_slot >= 0)
+    store_partial(stash_slot, [&](int t, int r) { return stash[w][t][r][lane]; }, stash_m, stash_l);
 }
 
 // ---------------------------------------------------------------------------
