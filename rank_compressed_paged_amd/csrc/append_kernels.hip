@@ -105,9 +105,14 @@ append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
   __shared__ float red[kAppendVWaves][16][64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
+  // XCD-aware order (workgroup i runs on XCD i % 8): the token tiles of one
+  // latent tile share its w_v rows, so their ids are equal mod 8
   const int jtiles = RV / 32;
-  const int jt = blockIdx.x % jtiles;
-  const int tt = blockIdx.x / jtiles;
+  const int ttiles = (n + 31) / 32;
+  const int x = blockIdx.x % 8, y = blockIdx.x / 8;
+  const int jt = (y / ttiles) * 8 + x;
+  const int tt = y % ttiles;
+  if (jt >= jtiles) return;
   const int t = tt * 32 + (lane & 31);
   const bool trow = t < n;
   const int j = jt * 32 + (lane & 31);
@@ -207,7 +212,7 @@ hipError_t append_enqueue(const AppendLaunch& a) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (a.n >= 16 && s.RV % 32 == 0 && K % (16 * kAppendVWaves) == 0) {
-    const int grid = ((a.n + 31) / 32) * (s.RV / 32);
+    const int grid = ((s.RV / 32 + 7) / 8) * 8 * ((a.n + 31) / 32);
     hipLaunchKernelGGL(append_v_mfma_kernel, dim3(grid), dim3(kAppendVWaves * 64), 0, a.stream, v, wv, a.n, K,
                        s.RV, where, vc);
   } else {

@@ -109,13 +109,23 @@ qproj_plan_mfma_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, fl
   const int r = (pair % rtiles) * 32 + (lane & 31);
   const int b = btile * 32 + (lane & 31);
   const int kofs = (lane >> 5) * 8;
+  // all operand loads of eight k-steps are in flight before the first MFMA
+  const bool brow = b < batch;
+  const f16* qrow = q + ((size_t)(brow ? b : batch - 1) * H + head) * D + kofs;
+  const f16* brw = bk + ((size_t)head * RK + r) * D + kofs;
+  const int ksteps = D / 16;
   floatx16 acc = {};
-  const half8 zero = {};
-  for (int k0 = 0; k0 < D; k0 += 16) {
-    half8 a = zero;
-    if (b < batch) a = *reinterpret_cast<const half8*>(q + ((size_t)b * H + head) * D + k0 + kofs);
-    half8 bb = *reinterpret_cast<const half8*>(bk + ((size_t)head * RK + r) * D + k0 + kofs);
-    acc = mfma32x32x16(a, bb, acc);
+  for (int c = 0; c < ksteps; c += 8) {
+    half8 a[8], bb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k0 = min(c + u, ksteps - 1) * 16;
+      a[u] = *reinterpret_cast<const half8*>(qrow + k0);
+      bb[u] = *reinterpret_cast<const half8*>(brw + k0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c + u < ksteps) acc = mfma32x32x16(brow ? a[u] : half8{}, bb[u], acc);
   }
 #pragma unroll
   for (int reg = 0; reg < 16; ++reg) {
@@ -170,28 +180,43 @@ merge_kernel(const float* __restrict__ part_z, const float* __restrict__ part_ml
       *reinterpret_cast<floatx4*>(zrow + d) = floatx4{};
     return;
   }
-  float M = -INFINITY;
-  for (int s = s0; s < s1; ++s) M = fmaxf(M, part_ml[((size_t)s * H + h) * 2]);
-  float den = 0.f;
-  for (int s = s0; s < s1; ++s)
-    den += fast_exp2(part_ml[((size_t)s * H + h) * 2] - M) * part_ml[((size_t)s * H + h) * 2 + 1];
-  const float inv = 1.f / den;
+  // A sequence spans few ranges: fetch up to 8 slots' (m, l, z) at once and
+  // merge them online, so the launch costs about one memory round trip.
+  constexpr int U = 8;
   const float* ml = part_ml + (size_t)h * 2;
   const float* zb = part_z + (size_t)h * RV;
   const size_t zs = (size_t)H * RV;                 // slot stride
   for (int d = threadIdx.x * 4; d < RV; d += blockDim.x * 4) {
     floatx4 a = {};
-    int s = s0;
-    for (; s + 4 <= s1; s += 4) {                   // four independent loads in flight
-      floatx4 z[4];
+    float M = -INFINITY, den = 0.f;
+    for (int c = s0; c < s1; c += U) {
+      float m[U], l[U];
+      floatx4 z[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) z[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)(s + u) * zs + d);
+      for (int u = 0; u < U; ++u) {
+        const int sl = min(c + u, s1 - 1);
+        m[u] = ml[(size_t)sl * H * 2];
+        l[u] = ml[(size_t)sl * H * 2 + 1];
+        z[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs + d);
+      }
+      float cm = M;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) a += fast_exp2(ml[(size_t)(s + u) * H * 2] - M) * z[u];
+      for (int u = 0; u < U; ++u)
+        if (c + u < s1) cm = fmaxf(cm, m[u]);
+      const float sc = fast_exp2(M - cm);           // 0 while M is still -inf
+      a *= sc;
+      den *= sc;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (c + u < s1) {
+          const float wgt = fast_exp2(m[u] - cm);
+          a += wgt * z[u];
+          den += wgt * l[u];
+        }
+      }
+      M = cm;
     }
-    for (; s < s1; ++s)
-      a += fast_exp2(ml[(size_t)s * H * 2] - M) * *reinterpret_cast<const floatx4*>(zb + (size_t)s * zs + d);
-    *reinterpret_cast<floatx4*>(zrow + d) = a * inv;
+    *reinterpret_cast<floatx4*>(zrow + d) = a * (1.f / den);
   }
 }
 
@@ -200,56 +225,72 @@ merge_kernel(const float* __restrict__ part_z, const float* __restrict__ part_ml
 // ---------------------------------------------------------------------------
 
 // MFMA path: a workgroup computes a [32 batch x 32 dims] tile of one head; its
-// eight waves split r_v and reduce through LDS.  Each wave issues all loads of
-// eight k-steps before the first MFMA, so a launch costs about one memory
-// latency, not one per k-step.  Z (fp32) enters the f16 MFMA as a hi + lo
-// pair, so the product keeps ~22 bits of Z.
+// eight waves split r_v and reduce through LDS.  B_v is stored dims-contiguous,
+// so each wave reads its [r_v/8 x 32] slice of B_v with coalesced 16-byte row
+// loads and transposes it through LDS into k-contiguous MFMA fragments.  Z
+// (fp32) enters the f16 MFMA as a hi + lo pair, so the product keeps ~22 bits
+// of Z.  All global loads are in flight before the first MFMA.
 constexpr int kUpWaves = 8;
+constexpr int kUpMaxSpan = 128;          // r_v / kUpWaves <= 128 (r_v <= 1024)
+constexpr int kUpPad = 8;
 
 __global__ void __launch_bounds__(kUpWaves * 64)
 upproj_mfma_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
                    int batch, int H, int D, int RV) {
+  __shared__ __attribute__((aligned(16))) f16 bt[kUpWaves][32][kUpMaxSpan + kUpPad];
   __shared__ float red[kUpWaves][16][64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int ntiles = D / 32;
-  const int nt = blockIdx.x % ntiles;
-  const int h = (blockIdx.x / ntiles) % H;
-  const int btile = blockIdx.x / (ntiles * H);
+  // XCD-aware order: workgroup i runs on XCD i % 8, and the ntiles workgroups
+  // of one (batch tile, head) group share its Z rows, so they get ids that are
+  // equal mod 8 and hit the same L2
+  const int x = blockIdx.x % 8, y = blockIdx.x / 8;
+  const int group = (y / ntiles) * 8 + x;
+  const int nt = y % ntiles;
+  if (group >= ((batch + 31) / 32) * H) return;
+  const int h = group % H;
+  const int btile = group / H;
   const int b = btile * 32 + (lane & 31);
   const bool brow = b < batch;
   const int n = nt * 32 + (lane & 31);
   const int kofs = (lane >> 5) * 8;
   const size_t ld = (size_t)H * D;
-  const int ksteps = RV / (16 * kUpWaves);
-  const int kbase = w * ksteps * 16;
-  const float* zrow = zf + ((size_t)(brow ? b : batch - 1) * H + h) * RV + kofs;
-  const f16* bcol = bv + (size_t)kofs * ld + (size_t)h * D + n;
-  floatx16 acc = {};
-  for (int c = 0; c < ksteps; c += 8) {
-    floatx4 za[8][2];
-    half8 bb[8];
+  const int kspan = RV / kUpWaves;       // multiple of 16
+  const int kbase = w * kspan;
+  // B_v slice rows kbase.., 32 dims from h*D + nt*32: lane -> (row l/4, 8 dims)
+  const f16* bsrc = bv + (size_t)(kbase + (lane >> 2)) * ld + (size_t)h * D + nt * 32 + (lane & 3) * 8;
+  const float* zrow = zf + ((size_t)(brow ? b : batch - 1) * H + h) * RV + kbase + kofs;
+  half8 braw[kUpMaxSpan / 16];
+  floatx4 za[kUpMaxSpan / 16][2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k0 = kbase + min(c + u, ksteps - 1) * 16;
-      za[u][0] = *reinterpret_cast<const floatx4*>(zrow + k0);
-      za[u][1] = *reinterpret_cast<const floatx4*>(zrow + k0 + 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bb[u][e] = bcol[(size_t)(k0 + e) * ld];
+  for (int u = 0; u < kUpMaxSpan / 16; ++u) {
+    if (u * 16 < kspan) {
+      braw[u] = *reinterpret_cast<const half8*>(bsrc + (size_t)u * 16 * ld);
+      za[u][0] = *reinterpret_cast<const floatx4*>(zrow + u * 16);
+      za[u][1] = *reinterpret_cast<const floatx4*>(zrow + u * 16 + 4);
     }
+  }
+  f16 (*tw)[kUpMaxSpan + kUpPad] = bt[w];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (c + u < ksteps) {
-        half8 hi, lo;
+  for (int u = 0; u < kUpMaxSpan / 16; ++u)
+    if (u * 16 < kspan)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float z = brow ? za[u][e >> 2][e & 3] : 0.f;
-          hi[e] = (f16)z;
-          lo[e] = (f16)(z - (float)hi[e]);
-        }
-        acc = mfma32x32x16(hi, bb[u], acc);
-        acc = mfma32x32x16(lo, bb[u], acc);
+      for (int e = 0; e < 8; ++e) tw[(lane & 3) * 8 + e][u * 16 + (lane >> 2)] = braw[u][e];
+  floatx16 acc = {};
+#pragma unroll
+  for (int u = 0; u < kUpMaxSpan / 16; ++u) {
+    if (u * 16 < kspan) {
+      const half8 bb = *reinterpret_cast<const half8*>(&tw[lane & 31][u * 16 + kofs]);
+      half8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float z = brow ? za[u][e >> 2][e & 3] : 0.f;
+        hi[e] = (f16)z;
+        lo[e] = (f16)(z - (float)hi[e]);
       }
+      acc = mfma32x32x16(hi, bb, acc);
+      acc = mfma32x32x16(lo, bb, acc);
     }
   }
 #pragma unroll
@@ -377,8 +418,9 @@ hipError_t decode_enqueue(const DecodeLaunch& a) {
   if (err != hipSuccess) return err;
 
   // 4. up-projection
-  if (a.batch >= kSmallBatch && s.D % 32 == 0 && s.RV % (16 * kUpWaves) == 0) {
-    const int grid = ((a.batch + 31) / 32) * s.H * (s.D / 32);
+  if (a.batch >= kSmallBatch && s.D % 32 == 0 && s.RV % (16 * kUpWaves) == 0 && s.RV <= kUpWaves * kUpMaxSpan) {
+    const int groups = ((a.batch + 31) / 32) * s.H;
+    const int grid = ((groups + 7) / 8) * 8 * (s.D / 32);
     hipLaunchKernelGGL(upproj_mfma_kernel, dim3(grid), dim3(kUpWaves * 64), 0, a.stream, zf,
                        static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H, s.D, s.RV);
   } else {
