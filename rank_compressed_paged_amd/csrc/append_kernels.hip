@@ -94,60 +94,69 @@ append_k_valu_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int 
   kc[(((size_t)phys * H + h) * kBlock + slot) * RK + r] = (f16)acc;
 }
 
-// V side, MFMA: a workgroup computes a [32 tokens x 32 latents] tile; its 16
-// waves split the H*d contraction (all loads of eight k-steps in flight before
-// the first MFMA) and reduce through LDS.
-constexpr int kAppendVWaves = 16;
+// V side, MFMA: a workgroup computes a [16 tokens x 16 latents] tile with the
+// 16x16x32 f16 MFMA, so one wave load instruction reads 16 rows x 64 bytes
+// (four lanes per row) of w_v and v instead of 32 rows x 32 bytes; the
+// 32x32 tiles spent the launch on address lookups.  Four waves split the H*d
+// contraction (eight k-steps of loads in flight before the first MFMA) and
+// reduce through LDS.
+constexpr int kAppendVWaves = 4;
+
+__device__ __forceinline__ floatx4 mfma16x16x32(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
 __global__ void __launch_bounds__(kAppendVWaves * 64)
 append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
                      SlotOf where, f16* __restrict__ vc) {
-  __shared__ float red[kAppendVWaves][16][64];
+  __shared__ float red[kAppendVWaves][4][64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   // XCD-aware order (workgroup i runs on XCD i % 8): the token tiles of one
   // latent tile share its w_v rows, so their ids are equal mod 8
-  const int jtiles = RV / 32;
-  const int ttiles = (n + 31) / 32;
+  const int jtiles = RV / 16;
+  const int ttiles = (n + 15) / 16;
   const int x = blockIdx.x % 8, y = blockIdx.x / 8;
   const int jt = (y / ttiles) * 8 + x;
   const int tt = y % ttiles;
   if (jt >= jtiles) return;
-  const int t = tt * 32 + (lane & 31);
+  const int t = tt * 16 + (lane & 15);
   const bool trow = t < n;
-  const int j = jt * 32 + (lane & 31);
-  const int kofs = (lane >> 5) * 8;
-  const int ksteps = K / (16 * kAppendVWaves);
-  const int kbase = w * ksteps * 16;
+  const int j = jt * 16 + (lane & 15);
+  const int kofs = (lane >> 4) * 8;
+  const int ksteps = K / (32 * kAppendVWaves);
+  const int kbase = w * ksteps * 32;
   const f16* xrow = v + (size_t)(trow ? t : n - 1) * K + kofs;
   const f16* wrow = wv + (size_t)j * K + kofs;
-  floatx16 acc = {};
+  floatx4 acc = {};
   for (int c = 0; c < ksteps; c += 8) {
     half8 a[8], b[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int k0 = kbase + min(c + u, ksteps - 1) * 16;
+      const int k0 = kbase + min(c + u, ksteps - 1) * 32;
       a[u] = *reinterpret_cast<const half8*>(xrow + k0);
       b[u] = *reinterpret_cast<const half8*>(wrow + k0);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      if (c + u < ksteps) acc = mfma32x32x16(trow ? a[u] : half8{}, b[u], acc);
+      if (c + u < ksteps) acc = mfma16x16x32(trow ? a[u] : half8{}, b[u], acc);
     }
   }
+  // result layout: lane l, register r holds D[4(l/16) + r][l % 16]
 #pragma unroll
-  for (int r = 0; r < 16; ++r) red[w][r][lane] = acc[r];
+  for (int r = 0; r < 4; ++r) red[w][r][lane] = acc[r];
   __syncthreads();
-  // wave w finishes accumulator register w (16 waves, 16 registers)
-  const int r = w;
-  float sum = 0.f;
+  if (w < 4) {                         // wave w finishes register w
+    const int r = w;
+    float sum = 0.f;
 #pragma unroll
-  for (int x = 0; x < kAppendVWaves; ++x) sum += red[x][r][lane];
-  const int ti = tt * 32 + mfma_row(r, lane);
-  if (ti < n) {
-    int phys, slot;
-    where(ti, phys, slot);
-    vc[((size_t)phys * RV + j) * kBlock + slot] = (f16)sum;
+    for (int q = 0; q < kAppendVWaves; ++q) sum += red[q][r][lane];
+    const int ti = tt * 16 + 4 * (lane >> 4) + r;
+    if (ti < n) {
+      int phys, slot;
+      where(ti, phys, slot);
+      vc[((size_t)phys * RV + j) * kBlock + slot] = (f16)sum;
+    }
   }
 }
 
@@ -211,8 +220,8 @@ hipError_t append_enqueue(const AppendLaunch& a) {
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (a.n >= 16 && s.RV % 32 == 0 && K % (16 * kAppendVWaves) == 0) {
-    const int grid = ((s.RV / 32 + 7) / 8) * 8 * ((a.n + 31) / 32);
+  if (a.n >= 16 && s.RV % 16 == 0 && K % (32 * kAppendVWaves) == 0) {
+    const int grid = ((s.RV / 16 + 7) / 8) * 8 * ((a.n + 15) / 16);
     hipLaunchKernelGGL(append_v_mfma_kernel, dim3(grid), dim3(kAppendVWaves * 64), 0, a.stream, v, wv, a.n, K,
                        s.RV, where, vc);
   } else {
