@@ -13,6 +13,7 @@ Prints one JSON line.  Options:
   --gpus N                 only 1 is supported (one GPU per box)
   --no-cpu-baseline        skip the oracle timing
   --no-ceiling             skip the HBM read-ceiling probe
+  --config N               time parity workload N (1-5) instead; own JSON line
   --calib-copy             run only a plain device copy of known size (for
                            scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
 """
@@ -133,6 +134,91 @@ def cpu_baseline(case, cfg, k_new, v_new, scale, budget_s=12.0):
                       f"{int(lens[0]) + 1} tokens), fp64 numpy, {dt:.1f} s wall"}
 
 
+def config_report(cfg_id: int, steps: int, warmup: int):
+    """Timing of one of the five parity workloads (a separate JSON line).
+
+    A step appends one token per sequence, then decodes; for the 32-layer stack
+    a step runs that for every layer (tokens/s = batch / summed layer time).
+    Uniform workloads overwrite the token at position L each step; the ragged
+    one grows every sequence by one token per step.  Workloads that fit the
+    256 MB last-level cache get a 1 GiB write between steps, outside the timed
+    events.
+    """
+    import torch
+
+    import rank_compressed_paged_amd as starkv
+    from rank_compressed_paged_amd import synth
+
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[cfg_id]
+    grow = cfg.seq_range is not None
+    spare = (warmup + steps) if grow else 1
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    layers = []
+    for layer in range(cfg.layers):
+        case = synth.make_config_case(cfg, layer=layer, spare_tokens=spare)
+        k_new, v_new = synth.make_new_rows(cfg.seed, cfg.batch, cfg.heads, cfg.head_dim, key=(layer,))
+        g = {k: torch.from_numpy(v).to(dev) for k, v in case.items() if isinstance(v, np.ndarray)}
+        g["k_new"] = torch.from_numpy(k_new).to(dev)
+        g["v_new"] = torch.from_numpy(v_new).to(dev)
+        layers.append(g)
+        lens0 = case["context_lens"].astype(np.int64)
+        del case
+    seqs = torch.arange(cfg.batch, dtype=torch.int32, device=dev)
+    max_len = int(lens0.max()) + spare
+    g0 = layers[0]
+    dims = starkv.dims_of(g0["k_pool"], g0["v_pool"], g0["block_tables"], cfg.head_dim)
+    ws = torch.empty(starkv.decode_workspace_size(dims, cfg.batch, max_len) + 256, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(g0["q"])
+    pool_bytes = sum(g["k_pool"].numel() * 2 + g["v_pool"].numel() * 2 for g in layers)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if pool_bytes < (1 << 30) else None
+
+    pos_all = [(lens0 + (s if grow else 0)).astype(np.int32) for s in range(warmup + steps)]
+    pos_dev = [torch.from_numpy(p).to(dev) for p in pos_all]
+    lens_dev = [p + 1 for p in pos_dev]
+    torch.cuda.synchronize()
+
+    def step(s):
+        pos_np, pos, lens = pos_all[s], pos_dev[s], lens_dev[s]
+        for g in layers:
+            starkv.append(g["k_new"], g["v_new"], g["b_k"], g["b_v"], g["block_tables"], seqs, pos,
+                          g["k_pool"], g["v_pool"])
+            starkv.decode(g["q"], g["b_k"], g["b_v"], g["k_pool"], g["v_pool"], g["block_tables"], lens, scale,
+                          max_context_len=max_len, workspace=ws, out=out)
+        return int(pos_np.astype(np.int64).sum()) + cfg.batch
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    starkv.profile_begin()
+    total_ms = 0.0
+    tokens = 0
+    for s in range(warmup, warmup + steps):
+        if flush is not None:
+            flush.fill_(s & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tokens += step(s) * cfg.layers
+        e1.record()
+        e1.synchronize()
+        total_ms += e0.elapsed_time(e1)
+    attn_ms, launches = starkv.profile_end()
+    latent = tokens * cfg.latent_bytes_per_token()
+    line = {
+        "config": cfg.index, "workload": cfg.name, "batch": cfg.batch, "layers": cfg.layers,
+        "steps": steps, "warmup": warmup, "ms_per_step": total_ms / steps,
+        "decode_tokens_per_s": cfg.batch * steps / (total_ms / 1e3),
+        "attn_kernel_us_per_launch": attn_ms / launches * 1e3,
+        "latent_gb_per_step": latent / steps / 1e9,
+        "attn_latent_gbps": latent / (attn_ms / 1e3) / 1e9,
+        "attn_frac_of_8tbps": latent / (attn_ms / 1e3) / 1e9 / PEAK_HBM_GBPS,
+        "step_latent_gbps": latent / (total_ms / 1e3) / 1e9,
+        "cache_flush_between_steps": flush is not None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,12 +227,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the HBM read-ceiling probe")
+    ap.add_argument("--config", type=int, default=0,
+                    help="time parity workload 1-5 instead (prints its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr, flush=True)
         sys.exit(2)
     if args.calib_copy:
         calib_copy()
+        return
+    if args.config:
+        config_report(args.config, args.steps, args.warmup)
         return
 
     import torch

@@ -52,8 +52,8 @@ typedef enum {
 typedef struct {
   int32_t num_heads;          /* H (query heads == KV heads)            */
   int32_t head_dim;           /* d, multiple of 8, <= 256               */
-  int32_t rank_k;             /* r_k per head                           */
-  int32_t rank_v;             /* r_v joint over heads                   */
+  int32_t rank_k;             /* r_k per head, multiple of 8            */
+  int32_t rank_v;             /* r_v joint over heads, multiple of 32, <= 1024 */
   int32_t block_size;         /* tokens per paged block; must be 16     */
   int32_t num_blocks;         /* physical blocks in each pool           */
   int32_t max_blocks_per_seq; /* row stride of block_tables             */

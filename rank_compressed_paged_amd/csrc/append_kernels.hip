@@ -160,40 +160,60 @@ append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
   }
 }
 
-// V side, VALU: one wave per joint latent j and up to 16 tokens (grid.y walks
-// token groups); lanes split the H*d contraction, coalesced along w_v's row.
-constexpr int kAppendGroup = 16;
+// V side, VALU (fewer than 16 tokens): a workgroup of eight waves owns eight
+// joint latents and up to four tokens.  The tokens' v rows are staged in LDS
+// once; each wave fetches its whole w_v row with 16-byte loads before any
+// arithmetic, then reduces one dot product per token across its lanes.
+constexpr int kAppendGroup = 4;
+constexpr int kAppendChunk = 4096;                  // contraction elements per pass
 
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 append_v_valu_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
                      SlotOf where, f16* __restrict__ vc) {
+  __shared__ __attribute__((aligned(16))) f16 vl[kAppendGroup][kAppendChunk];
   const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (j >= RV) return;
+  const int j = blockIdx.x * 8 + (threadIdx.x >> 6);
   const int t0 = blockIdx.y * kAppendGroup;
   const int cnt = min(kAppendGroup, n - t0);
-  float acc[kAppendGroup];
+  float acc[kAppendGroup] = {};
+  for (int kc = 0; kc < K; kc += kAppendChunk) {
+    const int kn = min(kAppendChunk, K - kc);       // multiple of 8
+    half8 wr[kAppendChunk / 512];
 #pragma unroll
-  for (int i = 0; i < kAppendGroup; ++i) acc[i] = 0.f;
-  for (int k0 = lane * 8; k0 < K; k0 += 512) {
-    const half8 b = *reinterpret_cast<const half8*>(wv + (size_t)j * K + k0);
+    for (int i = 0; i < kAppendChunk / 512; ++i) {
+      const int k = i * 512 + lane * 8;
+      wr[i] = (j < RV && k < kn) ? *reinterpret_cast<const half8*>(wv + (size_t)j * K + kc + k) : half8{};
+    }
+    __syncthreads();                                // previous pass's readers are done
+    for (int idx = threadIdx.x; idx < cnt * (kn / 8); idx += 512) {
+      const int r = idx / (kn / 8), c = idx % (kn / 8);
+      *reinterpret_cast<half8*>(&vl[r][c * 8]) = *reinterpret_cast<const half8*>(v + (size_t)(t0 + r) * K + kc + c * 8);
+    }
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kAppendGroup; ++i) {
-      if (i < cnt) {
-        const half8 a = *reinterpret_cast<const half8*>(v + (size_t)(t0 + i) * K + k0);
+    for (int r = 0; r < kAppendGroup; ++r) {
+      if (r < cnt) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[i] += (float)a[e] * (float)b[e];
+        for (int i = 0; i < kAppendChunk / 512; ++i) {
+          const int k = i * 512 + lane * 8;
+          if (k < kn) {
+            const half8 x = *reinterpret_cast<const half8*>(&vl[r][k]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[r] += (float)x[e] * (float)wr[i][e];
+          }
+        }
       }
     }
   }
+  if (j >= RV) return;                              // no barrier follows
 #pragma unroll
-  for (int i = 0; i < kAppendGroup; ++i) {
-    float s = acc[i];
+  for (int r = 0; r < kAppendGroup; ++r) {
+    float s = acc[r];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (lane == 0 && i < cnt) {
+    if (lane == 0 && r < cnt) {
       int phys, slot;
-      where(t0 + i, phys, slot);
+      where(t0 + r, phys, slot);
       vc[((size_t)phys * RV + j) * kBlock + slot] = (f16)s;
     }
   }
@@ -225,8 +245,8 @@ hipError_t append_enqueue(const AppendLaunch& a) {
     hipLaunchKernelGGL(append_v_mfma_kernel, dim3(grid), dim3(kAppendVWaves * 64), 0, a.stream, v, wv, a.n, K,
                        s.RV, where, vc);
   } else {
-    const dim3 grid((s.RV + 3) / 4, (a.n + kAppendGroup - 1) / kAppendGroup);
-    hipLaunchKernelGGL(append_v_valu_kernel, grid, dim3(256), 0, a.stream, v, wv, a.n, K, s.RV, where, vc);
+    const dim3 grid((s.RV + 7) / 8, (a.n + kAppendGroup - 1) / kAppendGroup);
+    hipLaunchKernelGGL(append_v_valu_kernel, grid, dim3(512), 0, a.stream, v, wv, a.n, K, s.RV, where, vc);
   }
   return hipGetLastError();
 }

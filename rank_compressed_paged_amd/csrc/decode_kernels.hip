@@ -165,59 +165,62 @@ qproj_plan_valu_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, fl
 // 3. merge of a sequence's partials
 // ---------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(256)
+constexpr int kMergeDims = 256;                    // latent dims per workgroup (64 lanes x 4)
+
+__global__ void __launch_bounds__(64)
 merge_kernel(const float* __restrict__ part_z, const float* __restrict__ part_ml,
              const int32_t* __restrict__ plan, const int32_t* __restrict__ lens,
              int batch, int H, int RV, float* __restrict__ zf) {
-  const int b = blockIdx.x / H;
-  const int h = blockIdx.x % H;
+  const int dchunks = (RV + kMergeDims - 1) / kMergeDims;
+  const int dc = blockIdx.x % dchunks;
+  const int h = (blockIdx.x / dchunks) % H;
+  const int b = blockIdx.x / (dchunks * H);
+  const int d = dc * kMergeDims + threadIdx.x * 4;
+  if (d >= RV) return;
   float* zrow = zf + ((size_t)b * H + h) * RV;
   const PlanView pv{plan, batch};
   const int s0 = pv.slot_base()[b];
   const int s1 = pv.slot_base()[b + 1];
   if (lens[b] == 0 || s1 <= s0) {
-    for (int d = threadIdx.x * 4; d < RV; d += blockDim.x * 4)
-      *reinterpret_cast<floatx4*>(zrow + d) = floatx4{};
+    *reinterpret_cast<floatx4*>(zrow + d) = floatx4{};
     return;
   }
-  // A sequence spans few ranges: fetch up to 8 slots' (m, l, z) at once and
-  // merge them online, so the launch costs about one memory round trip.
-  constexpr int U = 8;
+  // Long sequences span many ranges: sixteen slots' (m, l, z) are fetched at
+  // once and merged online, so a launch costs a few memory round trips.
+  constexpr int U = 16;
   const float* ml = part_ml + (size_t)h * 2;
-  const float* zb = part_z + (size_t)h * RV;
+  const float* zb = part_z + (size_t)h * RV + d;
   const size_t zs = (size_t)H * RV;                 // slot stride
-  for (int d = threadIdx.x * 4; d < RV; d += blockDim.x * 4) {
-    floatx4 a = {};
-    float M = -INFINITY, den = 0.f;
-    for (int c = s0; c < s1; c += U) {
-      float m[U], l[U];
-      floatx4 z[U];
+  floatx4 a = {};
+  float M = -INFINITY, den = 0.f;
+  for (int c = s0; c < s1; c += U) {
+    float m[U], l[U];
+    floatx4 z[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int sl = min(c + u, s1 - 1);
-        m[u] = ml[(size_t)sl * H * 2];
-        l[u] = ml[(size_t)sl * H * 2 + 1];
-        z[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs + d);
-      }
-      float cm = M;
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (c + u < s1) cm = fmaxf(cm, m[u]);
-      const float sc = fast_exp2(M - cm);           // 0 while M is still -inf
-      a *= sc;
-      den *= sc;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (c + u < s1) {
-          const float wgt = fast_exp2(m[u] - cm);
-          a += wgt * z[u];
-          den += wgt * l[u];
-        }
-      }
-      M = cm;
+    for (int u = 0; u < U; ++u) {
+      const int sl = min(c + u, s1 - 1);
+      m[u] = ml[(size_t)sl * H * 2];
+      l[u] = ml[(size_t)sl * H * 2 + 1];
+      z[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs);
     }
-    *reinterpret_cast<floatx4*>(zrow + d) = a * (1.f / den);
+    float cm = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (c + u < s1) cm = fmaxf(cm, m[u]);
+    const float sc = fast_exp2(M - cm);             // 0 while M is still -inf
+    a *= sc;
+    den *= sc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c + u < s1) {
+        const float wgt = fast_exp2(m[u] - cm);
+        a += wgt * z[u];
+        den += wgt * l[u];
+      }
+    }
+    M = cm;
   }
+  *reinterpret_cast<floatx4*>(zrow + d) = a * (1.f / den);
 }
 
 // ---------------------------------------------------------------------------
@@ -307,44 +310,72 @@ upproj_mfma_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
   }
 }
 
-// VALU path (small batches): a workgroup owns 64 output dims of one head for
-// up to 16 rows (grid.y walks further row groups); four waves split r_v.  B_v
-// rows are read once per row group, coalesced along dims.
+// VALU path (batch < 16): a workgroup owns 32 output dims of one head and up to
+// 16 rows.  Lane group (t & 3) owns 8 dims, t >> 2 picks the r_v rows
+// t/4 + 64 i: all of the workgroup's B_v slice is fetched with 16-byte loads
+// before any arithmetic, Z rows come from LDS, and the 64 row-partial sums of
+// each output are reduced through LDS.  Requires r_v <= 1024.
 constexpr int kSmallBatch = 16;
+constexpr int kUpvMaxRV = 1024;
 
 __global__ void __launch_bounds__(256)
 upproj_valu_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
                    int batch, int H, int D, int RV) {
-  __shared__ float red[4][kSmallBatch][64];
-  const int lane = threadIdx.x & 63;
-  const int ks = threadIdx.x >> 6;
-  const int ngroups = (D + 63) / 64;
-  const int h = blockIdx.x / ngroups;
-  const int n = (blockIdx.x % ngroups) * 64 + lane;
-  const size_t ld = (size_t)H * D;
+  __shared__ __attribute__((aligned(16))) float zl[kSmallBatch][kUpvMaxRV];
+  __shared__ float red[64][4][33];
+  const int t = threadIdx.x;
+  const int nchunks = (D + 31) / 32;
+  const int h = blockIdx.x / nchunks;
+  const int n0 = (blockIdx.x % nchunks) * 32;
+  const int nsub = (t & 3) * 8;
+  const int krow = t >> 2;
+  const bool nlive = n0 + nsub < D;              // D % 8 == 0: a chunk is all in or all out
   const int row0 = blockIdx.y * kSmallBatch;
   const int rows = min(kSmallBatch, batch - row0);
-  zf += (size_t)row0 * H * RV;
-  out += (size_t)row0 * H * D;
-  float acc[kSmallBatch];
+  const size_t ld = (size_t)H * D;
+  half8 bvr[kUpvMaxRV / 64];
 #pragma unroll
-  for (int i = 0; i < kSmallBatch; ++i) acc[i] = 0.f;
-  const int kspan = (RV + 3) / 4;
-  const int k1 = min(RV, (ks + 1) * kspan);
-  for (int k = ks * kspan; k < k1; ++k) {
-    const float x = (n < D) ? (float)bv[(size_t)k * ld + (size_t)h * D + n] : 0.f;
-#pragma unroll
-    for (int i = 0; i < kSmallBatch; ++i)
-      if (i < rows) acc[i] += zf[((size_t)i * H + h) * RV + k] * x;
+  for (int i = 0; i < kUpvMaxRV / 64; ++i) {
+    const int k = krow + 64 * i;
+    bvr[i] = (nlive && k < RV) ? *reinterpret_cast<const half8*>(bv + (size_t)k * ld + (size_t)h * D + n0 + nsub)
+                               : half8{};
   }
-#pragma unroll
-  for (int i = 0; i < kSmallBatch; ++i) red[ks][i][lane] = acc[i];
+  for (int idx = t; idx < rows * (RV / 4); idx += 256) {
+    const int r = idx / (RV / 4), c = idx % (RV / 4);
+    *reinterpret_cast<floatx4*>(&zl[r][c * 4]) =
+        *reinterpret_cast<const floatx4*>(zf + ((size_t)(row0 + r) * H + h) * RV + c * 4);
+  }
   __syncthreads();
-  if (ks == 0 && n < D) {
+  for (int g = 0; g < rows; g += 4) {
+    float acc[4][8];
 #pragma unroll
-    for (int i = 0; i < kSmallBatch; ++i)
-      if (i < rows)
-        out[((size_t)i * H + h) * D + n] = (f16)(red[0][i][lane] + red[1][i][lane] + red[2][i][lane] + red[3][i][lane]);
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kUpvMaxRV / 64; ++i) {
+      const int k = krow + 64 * i;
+      if (k < RV) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float z = (g + r < rows) ? zl[g + r][k] : 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[r][e] += z * (float)bvr[i][e];
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[krow][r][nsub + e] = acc[r][e];
+    __syncthreads();
+    if (t < 128) {
+      const int r = t >> 5, nn = t & 31;
+      float v = 0.f;
+      for (int q = 0; q < 64; ++q) v += red[q][r][nn];
+      if (g + r < rows && n0 + nn < D) out[((size_t)(row0 + g + r) * H + h) * D + n0 + nn] = (f16)v;
+    }
+    __syncthreads();
   }
 }
 
@@ -412,8 +443,8 @@ hipError_t decode_enqueue(const DecodeLaunch& a) {
   if (err != hipSuccess) return err;
 
   // 3. merge
-  hipLaunchKernelGGL(merge_kernel, dim3(a.batch * s.H), dim3(256), 0, a.stream, pz, pml, plan, a.context_lens,
-                     a.batch, s.H, s.RV, zf);
+  hipLaunchKernelGGL(merge_kernel, dim3(a.batch * s.H * ((s.RV + kMergeDims - 1) / kMergeDims)), dim3(64), 0,
+                     a.stream, pz, pml, plan, a.context_lens, a.batch, s.H, s.RV, zf);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
@@ -424,7 +455,7 @@ hipError_t decode_enqueue(const DecodeLaunch& a) {
     hipLaunchKernelGGL(upproj_mfma_kernel, dim3(grid), dim3(kUpWaves * 64), 0, a.stream, zf,
                        static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H, s.D, s.RV);
   } else {
-    const int grid = s.H * ((s.D + 63) / 64);
+    const int grid = s.H * ((s.D + 31) / 32);
     hipLaunchKernelGGL(upproj_valu_kernel, dim3(grid, (a.batch + kSmallBatch - 1) / kSmallBatch), dim3(256), 0, a.stream, zf,
                        static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H, s.D, s.RV);
   }

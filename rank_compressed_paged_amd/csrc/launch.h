@@ -10,7 +10,7 @@ namespace starkv {
 // Attention workgroups never take fewer than this many 16-token blocks when
 // the batch is big enough: each range flushes H*r_v fp32 of partial state, so
 // short ranges would spend more HBM traffic on partials than on latents.
-constexpr int kMinBlocksPerWG = 32;
+constexpr int kMinBlocksPerWG = 8;
 // Hard cap on attention workgroups (sizes the workspace without a device query).
 constexpr int kMaxGrid = 1024;
 // Lazy-rescale threshold (log2 units) of the running softmax maximum.

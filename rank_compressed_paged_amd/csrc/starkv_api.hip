@@ -22,7 +22,8 @@ starkv_status check_dims(const starkv_dims* d) {
       d->num_blocks <= 0 || d->max_blocks_per_seq <= 0)
     return STARKV_ERR_INVALID_ARG;
   if (d->block_size != kBlock) return STARKV_ERR_UNSUPPORTED;
-  if (d->head_dim % 8 != 0 || d->head_dim > 256 || d->rank_k % 8 != 0 || d->rank_v % 32 != 0)
+  if (d->head_dim % 8 != 0 || d->head_dim > 256 || d->rank_k % 8 != 0 || d->rank_v % 32 != 0 ||
+      d->rank_v > 1024)
     return STARKV_ERR_UNSUPPORTED;
   // 64-bit products stay far from overflow; 32-bit indices inside kernels need:
   if ((long long)d->num_heads * d->head_dim > (1 << 20) || (long long)d->rank_v * kBlock > (1 << 24))
