@@ -165,54 +165,63 @@ qproj_plan_valu_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, fl
 // 3. merge of a sequence's partials
 // ---------------------------------------------------------------------------
 
-constexpr int kMergeDims = 256;                    // latent dims per workgroup (64 lanes x 4)
-
-__global__ void __launch_bounds__(64)
+// One 256-thread workgroup merges 1024/W latent dims of one (sequence, head):
+// W slot groups (W = 1 or 4) each take every W-th slot, up to sixteen slots per
+// memory round trip, merge them online and combine through LDS.  W = 4 when
+// the launch has few workgroups (long sequences split into many ranges).
+template <int W>
+__global__ void __launch_bounds__(256)
 merge_kernel(const float* __restrict__ part_z, const float* __restrict__ part_ml,
              const int32_t* __restrict__ plan, const int32_t* __restrict__ lens,
              int batch, int H, int RV, float* __restrict__ zf) {
-  const int dchunks = (RV + kMergeDims - 1) / kMergeDims;
+  constexpr int kLanes = 256 / W;                   // threads per slot group
+  constexpr int kDims = 4 * kLanes;                 // latent dims per workgroup
+  __shared__ floatx4 ca[W][kLanes];
+  __shared__ float cm_s[W], cl_s[W];
+  const int li = threadIdx.x % kLanes;
+  const int w = threadIdx.x / kLanes;
+  const int dchunks = (RV + kDims - 1) / kDims;
   const int dc = blockIdx.x % dchunks;
   const int h = (blockIdx.x / dchunks) % H;
   const int b = blockIdx.x / (dchunks * H);
-  const int d = dc * kMergeDims + threadIdx.x * 4;
-  if (d >= RV) return;
+  const int d = dc * kDims + li * 4;
+  const bool live = d < RV;
   float* zrow = zf + ((size_t)b * H + h) * RV;
   const PlanView pv{plan, batch};
   const int s0 = pv.slot_base()[b];
   const int s1 = pv.slot_base()[b + 1];
   if (lens[b] == 0 || s1 <= s0) {
-    *reinterpret_cast<floatx4*>(zrow + d) = floatx4{};
+    if (w == 0 && live) *reinterpret_cast<floatx4*>(zrow + d) = floatx4{};
     return;
   }
-  // Long sequences span many ranges: sixteen slots' (m, l, z) are fetched at
-  // once and merged online, so a launch costs a few memory round trips.
   constexpr int U = 16;
   const float* ml = part_ml + (size_t)h * 2;
-  const float* zb = part_z + (size_t)h * RV + d;
+  const float* zb = part_z + (size_t)h * RV + (live ? d : 0);
   const size_t zs = (size_t)H * RV;                 // slot stride
   floatx4 a = {};
   float M = -INFINITY, den = 0.f;
-  for (int c = s0; c < s1; c += U) {
+  for (int c = s0 + w; c < s1; c += U * W) {
     float m[U], l[U];
     floatx4 z[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int sl = min(c + u, s1 - 1);
-      m[u] = ml[(size_t)sl * H * 2];
-      l[u] = ml[(size_t)sl * H * 2 + 1];
-      z[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs);
+      const int sl = c + u * W;
+      if (sl < s1) {
+        m[u] = ml[(size_t)sl * H * 2];
+        l[u] = ml[(size_t)sl * H * 2 + 1];
+        z[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs);
+      }
     }
     float cm = M;
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (c + u < s1) cm = fmaxf(cm, m[u]);
+      if (c + u * W < s1) cm = fmaxf(cm, m[u]);
     const float sc = fast_exp2(M - cm);             // 0 while M is still -inf
     a *= sc;
     den *= sc;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (c + u < s1) {
+      if (c + u * W < s1) {
         const float wgt = fast_exp2(m[u] - cm);
         a += wgt * z[u];
         den += wgt * l[u];
@@ -220,7 +229,32 @@ merge_kernel(const float* __restrict__ part_z, const float* __restrict__ part_ml
     }
     M = cm;
   }
-  *reinterpret_cast<floatx4*>(zrow + d) = a * (1.f / den);
+  if constexpr (W == 1) {
+    if (live) *reinterpret_cast<floatx4*>(zrow + d) = a * (1.f / den);
+  } else {
+    ca[w][li] = a;
+    if (li == 0) {
+      cm_s[w] = M;
+      cl_s[w] = den;
+    }
+    __syncthreads();
+    if (w == 0 && live) {
+      float top = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < W; ++q) top = fmaxf(top, cm_s[q]);
+      floatx4 sum = {};
+      float dsum = 0.f;
+#pragma unroll
+      for (int q = 0; q < W; ++q) {
+        if (cm_s[q] != -INFINITY) {                 // groups without slots hold nothing
+          const float wgt = fast_exp2(cm_s[q] - top);
+          sum += wgt * ca[q][li];
+          dsum += wgt * cl_s[q];
+        }
+      }
+      *reinterpret_cast<floatx4*>(zrow + d) = sum * (1.f / dsum);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -443,8 +477,14 @@ hipError_t decode_enqueue(const DecodeLaunch& a) {
   if (err != hipSuccess) return err;
 
   // 3. merge
-  hipLaunchKernelGGL(merge_kernel, dim3(a.batch * s.H * ((s.RV + kMergeDims - 1) / kMergeDims)), dim3(64), 0,
-                     a.stream, pz, pml, plan, a.context_lens, a.batch, s.H, s.RV, zf);
+  // few (sequence, head) pairs -> long sequences split into many ranges
+  const bool few = (long long)a.batch * s.H < 512;
+  if (few)
+    hipLaunchKernelGGL(merge_kernel<4>, dim3(a.batch * s.H * ((s.RV + 255) / 256)), dim3(256), 0, a.stream, pz,
+                       pml, plan, a.context_lens, a.batch, s.H, s.RV, zf);
+  else
+    hipLaunchKernelGGL(merge_kernel<1>, dim3(a.batch * s.H * ((s.RV + 1023) / 1024)), dim3(256), 0, a.stream, pz,
+                       pml, plan, a.context_lens, a.batch, s.H, s.RV, zf);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
