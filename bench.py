@@ -13,7 +13,7 @@ Prints one JSON line.  Options:
   --gpus N                 only 1 is supported (one GPU per box)
   --no-cpu-baseline        skip the oracle timing
   --no-ceiling             skip the HBM read-ceiling probe
-  --config N               time parity workload N (1-5) instead; own JSON line
+  --config N               time workload N (1-6) instead; own JSON line
   --calib-copy             run only a plain device copy of known size (for
                            scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
 """
@@ -167,9 +167,11 @@ def config_report(cfg_id: int, steps: int, warmup: int):
     seqs = torch.arange(cfg.batch, dtype=torch.int32, device=dev)
     max_len = int(lens0.max()) + spare
     g0 = layers[0]
-    dims = starkv.dims_of(g0["k_pool"], g0["v_pool"], g0["block_tables"], cfg.head_dim)
-    ws = torch.empty(starkv.decode_workspace_size(dims, cfg.batch, max_len) + 256, dtype=torch.uint8, device=dev)
+    ws_bytes = max(starkv.decode_workspace_size(starkv.dims_of(g["k_pool"], g["v_pool"], g["block_tables"],
+                                                               cfg.head_dim), cfg.batch, max_len) for g in layers)
+    ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
     out = torch.empty_like(g0["q"])
+    layer_bytes = [cfg.latent_bytes_per_token(l) for l in range(cfg.layers)]
     pool_bytes = sum(g["k_pool"].numel() * 2 + g["v_pool"].numel() * 2 for g in layers)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if pool_bytes < (1 << 30) else None
 
@@ -199,14 +201,15 @@ def config_report(cfg_id: int, steps: int, warmup: int):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        tokens += step(s) * cfg.layers
+        tokens += step(s)
         e1.record()
         e1.synchronize()
         total_ms += e0.elapsed_time(e1)
     attn_ms, launches = starkv.profile_end()
-    latent = tokens * cfg.latent_bytes_per_token()
+    latent = tokens * sum(layer_bytes)
     line = {
         "config": cfg.index, "workload": cfg.name, "batch": cfg.batch, "layers": cfg.layers,
+        "mean_latent_elems_per_token_layer": sum(layer_bytes) / 2 / cfg.layers,
         "steps": steps, "warmup": warmup, "ms_per_step": total_ms / steps,
         "decode_tokens_per_s": cfg.batch * steps / (total_ms / 1e3),
         "attn_kernel_us_per_launch": attn_ms / launches * 1e3,
@@ -228,7 +231,7 @@ def main():
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the HBM read-ceiling probe")
     ap.add_argument("--config", type=int, default=0,
-                    help="time parity workload 1-5 instead (prints its own JSON line)")
+                    help="time workload 1-6 instead (prints its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr, flush=True)

@@ -60,7 +60,10 @@ typedef struct {
 } starkv_dims;
 
 /* Latent shapes with a decode kernel built into this library:
- *   (H, r_k, r_v) = (32, 64, 1024) and (4, 16, 64).  Others -> UNSUPPORTED. */
+ *   H = 32 with r_k in {32, 64} and r_v in {256, 512, 768, 1024} (ranks may
+ *   differ from layer to layer: each layer is its own call), and
+ *   (H, r_k, r_v) = (4, 16, 64).  Others -> STARKV_ERR_UNSUPPORTED.
+ *   starkv_append supports any r_k % 8 == 0 and r_v % 32 == 0 up to 1024. */
 
 /*
  * starkv_append - project new K/V rows into latents and write them into their

@@ -322,17 +322,32 @@ struct AttnInst {
   static constexpr int threads = NW * 64;
 };
 
-// Shapes built into the library.  (H, r_k, r_v, waves per workgroup)
+// Shapes built into the library: (H, r_k, r_v, waves per workgroup).  The
+// method picks ranks per layer (adaptive rank control), so 32-head layers come
+// with r_k in {32, 64} and r_v in {256, 512, 768, 1024}; (4, 16, 64) is the
+// small parity shape.
 #define STARKV_ATTN_SHAPES(X) \
   X(32, 64, 1024, 8)          \
+  X(32, 64, 768, 8)           \
+  X(32, 64, 512, 8)           \
+  X(32, 64, 256, 8)           \
+  X(32, 32, 1024, 8)          \
+  X(32, 32, 768, 8)           \
+  X(32, 32, 512, 8)           \
+  X(32, 32, 256, 8)           \
   X(4, 16, 64, 2)
 
-bool attn_shape_supported(int H, int RK, int RV) {
-#define X(h, rk, rv, nw) if (H == h && RK == rk && RV == rv) return true;
+int attn_shape_index(int H, int RK, int RV) {
+  int i = 0;
+#define X(h, rk, rv, nw)                             \
+  if (H == h && RK == rk && RV == rv) return i;     \
+  ++i;
   STARKV_ATTN_SHAPES(X)
 #undef X
-  return false;
+  return -1;
 }
+
+bool attn_shape_supported(int H, int RK, int RV) { return attn_shape_index(H, RK, RV) >= 0; }
 
 template <typename Inst>
 static int resident_for(int device) {

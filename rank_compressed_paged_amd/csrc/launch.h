@@ -31,6 +31,9 @@ DecodeLayout decode_layout(const Shape& s, int batch, int max_context_len);
 
 // Returns true if a latent attention kernel is built for (H, r_k, r_v).
 bool attn_shape_supported(int H, int RK, int RV);
+// Position of (H, r_k, r_v) among the built shapes (< kMaxAttnShapes), or -1.
+int attn_shape_index(int H, int RK, int RV);
+constexpr int kMaxAttnShapes = 32;
 
 struct DecodeLaunch {
   Shape s;

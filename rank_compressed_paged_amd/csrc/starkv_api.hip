@@ -44,17 +44,13 @@ bool decode_args_ok(const starkv_dims* d, int32_t batch, int32_t max_context_len
 
 // Attention grid per (device, shape), filled on first use.
 constexpr int kMaxDevices = 64;
-std::atomic<int> g_resident[kMaxDevices][4];
-
-int shape_slot(int H, int RK, int RV) {
-  if (H == 32 && RK == 64 && RV == 1024) return 0;
-  if (H == 4 && RK == 16 && RV == 64) return 1;
-  return 3;
-}
+std::atomic<int> g_resident[kMaxDevices][kMaxAttnShapes];
 
 int resident_grid(int H, int RK, int RV, int device) {
-  if (device < 0 || device >= kMaxDevices) return attn_resident_grid(H, RK, RV, device);
-  std::atomic<int>& cell = g_resident[device][shape_slot(H, RK, RV)];
+  const int idx = attn_shape_index(H, RK, RV);
+  if (device < 0 || device >= kMaxDevices || idx < 0 || idx >= kMaxAttnShapes)
+    return attn_resident_grid(H, RK, RV, device);
+  std::atomic<int>& cell = g_resident[device][idx];
   int v = cell.load(std::memory_order_relaxed);
   if (v <= 0) {
     v = attn_resident_grid(H, RK, RV, device);

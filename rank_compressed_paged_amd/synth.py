@@ -7,8 +7,8 @@ sides always see the same bits.
 
 Workloads follow the shapes of the pages' kernel benchmark (32-head MHA,
 head size 128, rank 64, fp16; Proxima landing page, "Decode kernel" section)
-with the V rank, batch sizes and context lengths of the five configurations
-listed below.  The pages measured on real serving traffic with a trained
+with the V rank, batch sizes and context lengths of the configurations listed
+below (the sixth one varies the ranks from layer to layer).  The pages measured on real serving traffic with a trained
 checkpoint; the kernels only ever see latents, so N(0, 1) latents and random
 orthonormal-row projections stand in for those.
 
@@ -47,14 +47,29 @@ class Config:
     seq_range: tuple | None = None  # ragged: inclusive uniform integer range
     layers: int = 1
     table: str = "perm"             # block tables: random permutation of the pool
+    layer_ranks: tuple | None = None  # per-layer (r_k, r_v), overriding rank_k / rank_v
 
     @property
     def seed(self) -> int:
         return BASE_SEED + self.index
 
-    def latent_bytes_per_token(self) -> int:
-        return 2 * (self.heads * self.rank_k + self.rank_v)
+    def ranks(self, layer: int = 0):
+        if self.layer_ranks is not None:
+            return self.layer_ranks[layer]
+        return self.rank_k, self.rank_v
 
+    def latent_bytes_per_token(self, layer: int = 0) -> int:
+        rk, rv = self.ranks(layer)
+        return 2 * (self.heads * rk + rv)
+
+
+# Per-layer ranks of a 32-layer, 32-head stack (adaptive rank control: each
+# layer keeps its own r_k and r_v).  Mean latent width H*r_k + r_v = 2,648 fp16
+# elements per token per layer, within 0.3 % of the ~2,640 implied by the
+# Proxima README's balanced-profile capacity figures (about 169 kB per token
+# over 32 layers).  The split across layers is synthetic: the real profile is a
+# calibration output that is not available.
+MIXED_RANKS_32 = (((64, 1024),) * 9 + ((64, 768),) * 7 + ((64, 512),) * 9 + ((32, 1024),) * 7)
 
 CONFIGS = {
     1: Config(1, "tiny_b1_h4_l256", batch=1, heads=4, head_dim=64, rank_k=16,
@@ -67,6 +82,8 @@ CONFIGS = {
               rank_k=64, rank_v=1024, seq_range=(512, 16384)),
     5: Config(5, "layers32_b4_l32768", batch=4, heads=32, head_dim=128,
               rank_k=64, rank_v=1024, seq=32768, layers=32),
+    6: Config(6, "layers32_b4_l32768_mixed_ranks", batch=4, heads=32, head_dim=128,
+              rank_k=64, rank_v=1024, seq=32768, layers=32, layer_ranks=MIXED_RANKS_32),
 }
 
 
@@ -206,7 +223,8 @@ def make_case(seed: int, batch: int, heads: int, head_dim: int, rank_k: int, ran
 def make_config_case(cfg: Config, layer: int = 0, spare_tokens: int = 0, sentinel: bool = True):
     lens = context_lengths(cfg)
     key = (layer,) if cfg.layers > 1 else ()
-    return make_case(cfg.seed, cfg.batch, cfg.heads, cfg.head_dim, cfg.rank_k, cfg.rank_v,
+    rank_k, rank_v = cfg.ranks(layer)
+    return make_case(cfg.seed, cfg.batch, cfg.heads, cfg.head_dim, rank_k, rank_v,
                      lens, spare_tokens=spare_tokens, key=key, sentinel=sentinel)
 
 

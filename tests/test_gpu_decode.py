@@ -261,3 +261,59 @@ def test_config5_layer_full_size_sampled(layer):
     rows = np.array([0, 3])
     ref = oracle_rows(case, case["context_lens"], scale, rows)
     check(out, ref, rows=rows, what=f"config5 layer {layer}")
+
+
+# ------------------------------------------------------- per-layer ranks
+@pytest.mark.parametrize("rk,rv", [(64, 768), (64, 512), (64, 256), (32, 1024), (32, 768), (32, 512), (32, 256)])
+def test_rank_shapes(rk, rv):
+    """Every (r_k, r_v) the library builds for 32 heads: adaptive rank control
+    gives each layer its own ranks."""
+    dev = gpu()
+    lens = [300, 47, 1000, 129, 0]
+    case = synth.make_case(300 + rk + rv, len(lens), 32, 128, rk, rv, np.array(lens))
+    log(f"ranks r_k={rk} r_v={rv}")
+    for scale in (1.0 / math.sqrt(128), 1.0):
+        out = decode_gpu(to_dev(case, dev), lens, scale, dev)
+        ref = oracle.decode(case["q"], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
+                            case["block_tables"], np.array(lens), scale)
+        got = out.float().cpu().numpy()
+        assert not np.abs(got[4]).any()
+        check(got[:4], ref[:4], what=f"r_k={rk} r_v={rv} scale={scale:.3f}")
+
+
+@pytest.mark.parametrize("rk,rv,per_seq", [(32, 256, 6), (64, 512, 1)])
+def test_append_then_decode_other_ranks(rk, rv, per_seq):
+    """Append (MFMA path at 24 tokens, VALU at 4) then decode, at non-default ranks."""
+    import torch
+    import rank_compressed_paged_amd as starkv
+    dev = gpu()
+    lens = np.array([33, 200, 16, 90])
+    case = synth.make_case(400 + rk, len(lens), 32, 128, rk, rv, lens, spare_tokens=per_seq)
+    g = to_dev(case, dev)
+    seqs = np.repeat(np.arange(len(lens), dtype=np.int32), per_seq)
+    poss = np.concatenate([np.arange(n, n + per_seq, dtype=np.int32) for n in lens])
+    k_new, v_new = synth.make_new_rows(400 + rk, len(seqs), 32, 128)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    starkv.append(t(k_new), t(v_new), g["b_k"], g["b_v"], g["block_tables"], t(seqs), t(poss),
+                  g["k_pool"], g["v_pool"])
+    new_lens = lens + per_seq
+    out = decode_gpu(g, new_lens, 1.0, dev)
+    kp, vp = oracle.append(k_new, v_new, case["b_k"], case["b_v"], case["block_tables"], seqs, poss,
+                           case["k_pool"], case["v_pool"])
+    ref = oracle.decode(case["q"], case["b_k"], case["b_v"], kp, vp, case["block_tables"], new_lens, 1.0)
+    check(out, ref, what=f"append+decode r_k={rk} r_v={rv}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", [12, 28])
+def test_config6_mixed_rank_layer_full_size_sampled(layer):
+    dev = gpu()
+    cfg = synth.CONFIGS[6]
+    case = synth.make_config_case(cfg, layer=layer)
+    rk, rv = cfg.ranks(layer)
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    log(f"config 6 layer {layer}: r_k={rk} r_v={rv}, batch 4, seq 32768")
+    out = decode_gpu(to_dev(case, dev), case["context_lens"], scale, dev)
+    rows = np.array([1, 2])
+    ref = oracle_rows(case, case["context_lens"], scale, rows)
+    check(out, ref, rows=rows, what=f"config6 layer {layer}")
