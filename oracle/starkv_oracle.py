@@ -24,6 +24,11 @@ block_tables[b, t // 16], slot t % 16.  Within a block the library's layout is
   k_pool[p, h, slot, :]  (r_k latents of head h)
   v_pool[p, :, slot]     (r_v joint latents)
 
+Grouped query heads (the pages list GQA model families as supported; Proxima
+README, multi-model remark after the measured results): with H query heads
+and H_kv key/value heads, query head h reads the keys and value columns of
+head h // (H / H_kv); the joint V latent is unchanged.
+
 Decode result.  Reading the latent-space computation (q projected by B_k,
 weights applied to c_v before B_v) as re-association of the same products,
 the method's output is exactly ordinary single-query softmax attention over
@@ -55,26 +60,31 @@ def gather_latents(k_pool, v_pool, table_row, length, block_size=16):
 def decode(q, b_k, b_v, k_pool, v_pool, block_tables, context_lens, scale, block_size=16):
     """Single-token attention for every sequence in the batch.
 
-    q [B, H, d]; b_k [H, r_k, d]; b_v [r_v, H*d]; pools as documented above;
-    block_tables [B, max_blocks]; context_lens [B].  A sequence of length 0
-    yields a zero row (library convention).  Returns fp64 [B, H, d].
+    q [B, H, d]; b_k [H_kv, r_k, d]; b_v [r_v, H_kv*d]; pools as documented
+    above with H_kv key/value heads; block_tables [B, max_blocks];
+    context_lens [B].  With grouped query heads (H a multiple of H_kv), query
+    head h reads key/value head h // (H / H_kv); H_kv = H is plain multi-head
+    attention.  A sequence of length 0 yields a zero row (library convention).
+    Returns fp64 [B, H, d].
     """
     q = np.asarray(q).astype(F64)
     bk = np.asarray(b_k).astype(F64)
     bv = np.asarray(b_v).astype(F64)
     nb, nh, d = q.shape
+    group = nh // bk.shape[0]
     out = np.zeros((nb, nh, d), F64)
     for b in range(nb):
         length = int(context_lens[b])
         if length == 0:
             continue
         c_k, c_v = gather_latents(k_pool, v_pool, block_tables[b], length, block_size)
-        values = c_v @ bv                                  # [L, H*d]
+        values = c_v @ bv                                  # [L, H_kv*d]
         for h in range(nh):
-            keys = c_k[:, h, :] @ bk[h]                    # [L, d]
+            kv = h // group
+            keys = c_k[:, kv, :] @ bk[kv]                  # [L, d]
             scores = float(scale) * (keys @ q[b, h])       # [L]
             w = np.exp(scores - scores.max())
-            out[b, h] = (w @ values[:, h * d:(h + 1) * d]) / w.sum()
+            out[b, h] = (w @ values[:, kv * d:(kv + 1) * d]) / w.sum()
     return out
 
 

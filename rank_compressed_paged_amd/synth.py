@@ -48,6 +48,7 @@ class Config:
     layers: int = 1
     table: str = "perm"             # block tables: random permutation of the pool
     layer_ranks: tuple | None = None  # per-layer (r_k, r_v), overriding rank_k / rank_v
+    kv_heads: int | None = None     # grouped query heads: key/value heads (None = heads)
 
     @property
     def seed(self) -> int:
@@ -58,9 +59,13 @@ class Config:
             return self.layer_ranks[layer]
         return self.rank_k, self.rank_v
 
+    @property
+    def kv(self) -> int:
+        return self.heads if self.kv_heads is None else self.kv_heads
+
     def latent_bytes_per_token(self, layer: int = 0) -> int:
         rk, rv = self.ranks(layer)
-        return 2 * (self.heads * rk + rv)
+        return 2 * (self.kv * rk + rv)
 
 
 # Per-layer ranks of a 32-layer, 32-head stack (adaptive rank control: each
@@ -84,6 +89,9 @@ CONFIGS = {
               rank_k=64, rank_v=1024, seq=32768, layers=32),
     6: Config(6, "layers32_b4_l32768_mixed_ranks", batch=4, heads=32, head_dim=128,
               rank_k=64, rank_v=1024, seq=32768, layers=32, layer_ranks=MIXED_RANKS_32),
+    # grouped query heads, Llama-3-8B-like attention: 32 query heads over 8 key/value heads
+    7: Config(7, "gqa32x8_b64_l8192", batch=64, heads=32, head_dim=128, rank_k=64,
+              rank_v=1024, seq=8192, kv_heads=8),
 }
 
 
@@ -139,9 +147,9 @@ def make_projections(seed: int, heads: int, head_dim: int, rank_k: int, rank_v: 
                      key: tuple = (), dtype=np.float16):
     """Up-projections with orthonormal rows, rounded to `dtype`.
 
-    b_k [H, r_k, d]: row r of head h is the key basis vector for latent r.
-    b_v [r_v, H*d]: row j is the value basis vector for joint latent j;
-    columns [h*d, (h+1)*d) belong to head h.
+    heads = key/value heads.  b_k [H, r_k, d]: row r of head h is the key basis
+    vector for latent r.  b_v [r_v, H*d]: row j is the value basis vector for
+    joint latent j; columns [h*d, (h+1)*d) belong to head h.
     """
     rng = _rng(seed, 1, *key)
     b_k = np.stack([orthonormal_rows(rng, rank_k, head_dim) for _ in range(heads)])
@@ -197,27 +205,29 @@ def poison_unused(k_pool, v_pool, block_tables, context_lens):
 
 def make_case(seed: int, batch: int, heads: int, head_dim: int, rank_k: int, rank_v: int,
               context_lens, *, spare_tokens: int = 0, key: tuple = (),
-              sentinel: bool = True, q_scale: float | None = None):
+              sentinel: bool = True, q_scale: float | None = None, kv_heads: int | None = None):
     """One decode layer's inputs.
 
+    heads = query heads; kv_heads = key/value heads (default: heads).
     spare_tokens: extra table capacity per sequence for later appends (slots
     stay poisoned until something writes them).
     """
+    kvh = heads if kv_heads is None else kv_heads
     context_lens = np.asarray(context_lens, np.int32)
     assert len(context_lens) == batch
     need = (context_lens.astype(np.int64) + spare_tokens + BLOCK_SIZE - 1) // BLOCK_SIZE
     bt, nb = make_block_tables(seed, need, key=key)
-    b_k, b_v = make_projections(seed, heads, head_dim, rank_k, rank_v, key=key)
+    b_k, b_v = make_projections(seed, kvh, head_dim, rank_k, rank_v, key=key)
     if q_scale is None:
         q_scale = 1.0 / math.sqrt(head_dim)
     q = normal_f16(seed, (4, *key), (batch, heads, head_dim), scale=q_scale)
-    k_pool = normal_f16(seed, (5, *key), (nb, heads, BLOCK_SIZE, rank_k))
+    k_pool = normal_f16(seed, (5, *key), (nb, kvh, BLOCK_SIZE, rank_k))
     v_pool = normal_f16(seed, (6, *key), (nb, rank_v, BLOCK_SIZE))
     if sentinel:
         poison_unused(k_pool, v_pool, bt, context_lens)
     return dict(q=q, b_k=b_k, b_v=b_v, k_pool=k_pool, v_pool=v_pool,
                 block_tables=bt, context_lens=context_lens, num_blocks=nb,
-                heads=heads, head_dim=head_dim, rank_k=rank_k, rank_v=rank_v)
+                heads=heads, kv_heads=kvh, head_dim=head_dim, rank_k=rank_k, rank_v=rank_v)
 
 
 def make_config_case(cfg: Config, layer: int = 0, spare_tokens: int = 0, sentinel: bool = True):
@@ -225,7 +235,7 @@ def make_config_case(cfg: Config, layer: int = 0, spare_tokens: int = 0, sentine
     key = (layer,) if cfg.layers > 1 else ()
     rank_k, rank_v = cfg.ranks(layer)
     return make_case(cfg.seed, cfg.batch, cfg.heads, cfg.head_dim, rank_k, rank_v,
-                     lens, spare_tokens=spare_tokens, key=key, sentinel=sentinel)
+                     lens, spare_tokens=spare_tokens, key=key, sentinel=sentinel, kv_heads=cfg.kv)
 
 
 def make_new_rows(seed: int, n: int, heads: int, head_dim: int, key: tuple = ()):

@@ -61,23 +61,26 @@ def random_tables(rng, lens, spare=1):
 
 
 def brute_decode(q, bk, bv, kp, vp, tables, lens, scale):
-    """Scalar loops with exactly rounded sums; walks tables token by token."""
+    """Scalar loops with exactly rounded sums; walks tables token by token.
+    Query head h reads key/value head h * H_kv // H."""
     nbatch, nh, d = q.shape
     rk = bk.shape[1]
     rv = bv.shape[0]
+    nkv = bk.shape[0]
     out = np.zeros((nbatch, nh, d))
     for b in range(nbatch):
         slots = walk_slots(tables[b], lens[b])
         if not slots:
             continue
         for h in range(nh):
+            g = h * nkv // nh
             scores = []
             values = []
             for p, j in slots:
-                key = [math.fsum(float(kp[p, h, j, r]) * float(bk[h, r, i]) for r in range(rk))
+                key = [math.fsum(float(kp[p, g, j, r]) * float(bk[g, r, i]) for r in range(rk))
                        for i in range(d)]
                 scores.append(float(scale) * math.fsum(key[i] * float(q[b, h, i]) for i in range(d)))
-                values.append([math.fsum(float(vp[p, c, j]) * float(bv[c, h * d + i]) for c in range(rv))
+                values.append([math.fsum(float(vp[p, c, j]) * float(bv[c, g * d + i]) for c in range(rv))
                                for i in range(d)])
             top = max(scores)
             w = [math.exp(s - top) for s in scores]
@@ -87,8 +90,8 @@ def brute_decode(q, bk, bv, kp, vp, tables, lens, scale):
     return out
 
 
-def small_case(seed=7, heads=2, head_dim=3, rank_k=2, rank_v=5, lens=(37, 0, 16, 1)):
-    return synth.make_case(seed, len(lens), heads, head_dim, rank_k, rank_v, np.array(lens))
+def small_case(seed=7, heads=2, head_dim=3, rank_k=2, rank_v=5, lens=(37, 0, 16, 1), kv_heads=None):
+    return synth.make_case(seed, len(lens), heads, head_dim, rank_k, rank_v, np.array(lens), kv_heads=kv_heads)
 
 
 def run_oracle(case, scale=None, **over):
@@ -130,6 +133,31 @@ def test_bruteforce_wide_ranks():
     ref = brute_decode(case["q"], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
                        case["block_tables"], case["context_lens"], 0.7)
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_bruteforce_grouped_query_heads():
+    # 6 query heads over 2 key/value heads: heads 0-2 read kv 0, heads 3-5 kv 1
+    case = small_case(seed=13, heads=6, head_dim=3, rank_k=2, rank_v=5, lens=(21, 40), kv_heads=2)
+    assert case["k_pool"].shape[1] == 2 and case["b_v"].shape[1] == 6
+    got = run_oracle(case, 0.8)
+    ref = brute_decode(case["q"], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
+                       case["block_tables"], case["context_lens"], 0.8)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_grouped_heads_equal_multi_head_with_replicated_kv():
+    """GQA over H_kv heads is MHA over H heads whose key latents, B_k and B_v
+    columns are copies of their group's key/value head."""
+    heads, kvh, d = 6, 3, 4
+    case = small_case(seed=14, heads=heads, head_dim=d, rank_k=3, rank_v=7, lens=(35, 9, 64), kv_heads=kvh)
+    grp = heads // kvh
+    mha = dict(case)
+    mha["k_pool"] = np.repeat(case["k_pool"], grp, axis=1)
+    mha["b_k"] = np.repeat(case["b_k"], grp, axis=0)
+    mha["b_v"] = np.concatenate([case["b_v"][:, (h // grp) * d:(h // grp + 1) * d] for h in range(heads)], axis=1)
+    a = run_oracle(case, 1.3)
+    b = run_oracle(mha, 1.3)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-15)
 
 
 def test_full_rank_equals_uncompressed_attention_sdpa():
