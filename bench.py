@@ -157,7 +157,7 @@ def config_report(cfg_id: int, steps: int, warmup: int):
     layers = []
     for layer in range(cfg.layers):
         case = synth.make_config_case(cfg, layer=layer, spare_tokens=spare)
-        k_new, v_new = synth.make_new_rows(cfg.seed, cfg.batch, cfg.heads, cfg.head_dim, key=(layer,))
+        k_new, v_new = synth.make_new_rows(cfg.seed, cfg.batch, cfg.kv, cfg.head_dim, key=(layer,))
         g = {k: torch.from_numpy(v).to(dev) for k, v in case.items() if isinstance(v, np.ndarray)}
         g["k_new"] = torch.from_numpy(k_new).to(dev)
         g["v_new"] = torch.from_numpy(v_new).to(dev)
@@ -168,7 +168,8 @@ def config_report(cfg_id: int, steps: int, warmup: int):
     max_len = int(lens0.max()) + spare
     g0 = layers[0]
     ws_bytes = max(starkv.decode_workspace_size(starkv.dims_of(g["k_pool"], g["v_pool"], g["block_tables"],
-                                                               cfg.head_dim), cfg.batch, max_len) for g in layers)
+                                                               cfg.head_dim, heads=cfg.heads), cfg.batch, max_len)
+                   for g in layers)
     ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
     out = torch.empty_like(g0["q"])
     layer_bytes = [cfg.latent_bytes_per_token(l) for l in range(cfg.layers)]
@@ -209,6 +210,7 @@ def config_report(cfg_id: int, steps: int, warmup: int):
     latent = tokens * sum(layer_bytes)
     line = {
         "config": cfg.index, "workload": cfg.name, "batch": cfg.batch, "layers": cfg.layers,
+        "heads": cfg.heads, "kv_heads": cfg.kv,
         "mean_latent_elems_per_token_layer": sum(layer_bytes) / 2 / cfg.layers,
         "steps": steps, "warmup": warmup, "ms_per_step": total_ms / steps,
         "decode_tokens_per_s": cfg.batch * steps / (total_ms / 1e3),
@@ -231,7 +233,7 @@ def main():
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the HBM read-ceiling probe")
     ap.add_argument("--config", type=int, default=0,
-                    help="time workload 1-6 instead (prints its own JSON line)")
+                    help="time workload 1-7 instead (prints its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr, flush=True)
@@ -252,7 +254,7 @@ def main():
     cfg = synth.CONFIGS[3]
     t_gen = time.perf_counter()
     case = synth.make_config_case(cfg, spare_tokens=1)
-    k_new, v_new = synth.make_new_rows(cfg.seed, cfg.batch, cfg.heads, cfg.head_dim)
+    k_new, v_new = synth.make_new_rows(cfg.seed, cfg.batch, cfg.kv, cfg.head_dim)
     print(f"# inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     g = {k: torch.from_numpy(v).to(dev) for k, v in case.items() if isinstance(v, np.ndarray)}
     kn = torch.from_numpy(k_new).to(dev)
@@ -263,7 +265,7 @@ def main():
     lens = pos + 1
     max_len = int(pos_np.max()) + 1
     scale = 1.0 / math.sqrt(cfg.head_dim)
-    dims = starkv.dims_of(g["k_pool"], g["v_pool"], g["block_tables"], cfg.head_dim)
+    dims = starkv.dims_of(g["k_pool"], g["v_pool"], g["block_tables"], cfg.head_dim, heads=cfg.heads)
     ws = torch.empty(starkv.decode_workspace_size(dims, cfg.batch, max_len) + 256, dtype=torch.uint8, device=dev)
     out = torch.empty_like(g["q"])
 

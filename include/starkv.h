@@ -17,8 +17,12 @@
  * Conventions shared by every call
  *  - All tensors are dense, row-major, in device memory (HBM) unless marked
  *    "host".  fp16 is IEEE binary16; accumulation is fp32.
+ *  - Grouped query heads: H query heads share H_kv key/value heads (H_kv
+ *    divides H; query head h reads key/value head h / (H/H_kv)).  H_kv = H is
+ *    plain multi-head attention.  The latents and projections below are per
+ *    key/value head; q and out are per query head.
  *  - Paged layout (physical block p, slot j = position % 16):
- *      k_cache [num_blocks][H][16][r_k]  fp16  (head-major inside a block)
+ *      k_cache [num_blocks][H_kv][16][r_k]  fp16  (head-major inside a block)
  *      v_cache [num_blocks][r_v][16]     fp16  (latent-dim-major inside a block)
  *    Position t of sequence b lives in block block_tables[b*max_blocks_per_seq
  *    + t/16], slot t%16.
@@ -50,34 +54,39 @@ typedef enum {
 
 /* Host struct, passed by pointer; read during the call only. */
 typedef struct {
-  int32_t num_heads;          /* H (query heads == KV heads)            */
+  int32_t num_heads;          /* H query heads                          */
   int32_t head_dim;           /* d, multiple of 8, <= 256               */
   int32_t rank_k;             /* r_k per head, multiple of 8            */
   int32_t rank_v;             /* r_v joint over heads, multiple of 32, <= 1024 */
   int32_t block_size;         /* tokens per paged block; must be 16     */
   int32_t num_blocks;         /* physical blocks in each pool           */
   int32_t max_blocks_per_seq; /* row stride of block_tables             */
+  int32_t num_kv_heads;       /* H_kv key/value heads, dividing H; 0 means H */
 } starkv_dims;
 
-/* Latent shapes with a decode kernel built into this library:
- *   H = 32 with r_k in {32, 64} and r_v in {256, 512, 768, 1024} (ranks may
- *   differ from layer to layer: each layer is its own call), and
- *   (H, r_k, r_v) = (4, 16, 64).  Others -> STARKV_ERR_UNSUPPORTED.
+/* Latent shapes with a decode kernel built into this library, as
+ * (H, H_kv, r_k, r_v):
+ *   (32, 32, r_k in {32, 64}, r_v in {256, 512, 768, 1024}) - ranks may differ
+ *   from layer to layer: each layer is its own call;
+ *   (32, 8, 64, {256, 512, 1024}), (32, 8, 32, {256, 512}) and
+ *   (32, 4, 64, {256, 512}) - grouped query heads;
+ *   (4, 4, 16, 64) and (8, 2, 32, 64) - small shapes.
+ *   Others -> STARKV_ERR_UNSUPPORTED.
  *   starkv_append supports any r_k % 8 == 0 and r_v % 32 == 0 up to 1024. */
 
 /*
  * starkv_append - project new K/V rows into latents and write them into their
  * paged slots (the method's "stored in a compressed paged format" step).
  *
- *   c_k[i,h,:] = fp16( w_k[h] . k[i,h,:] )      w_k [H][r_k][d]
- *   c_v[i,:]   = fp16( w_v . vec(v[i]) )        w_v [r_v][H*d], vec = heads concatenated
+ *   c_k[i,h,:] = fp16( w_k[h] . k[i,h,:] )      w_k [H_kv][r_k][d]
+ *   c_v[i,:]   = fp16( w_v . vec(v[i]) )        w_v [r_v][H_kv*d], vec = heads concatenated
  * computed with fp32 accumulation and rounded once to fp16 (nearest even).
  * The down-projections are stored output-major (row r is the weight vector of
  * latent r).  With orthonormal-row up-projections B, w = B gives the
  * least-squares latents, so callers may pass b_k / b_v of starkv_decode.
  *
  *   n_tokens     number of rows; 0 is a no-op returning STARKV_OK.
- *   k, v         [n_tokens][H][d] fp16, 16-byte aligned.
+ *   k, v         [n_tokens][H_kv][d] fp16, 16-byte aligned.
  *   block_tables [B][max_blocks_per_seq] int32.  The target block of every
  *                token must already be assigned (allocation is the caller's).
  *   token_seq    [n_tokens] int32: table row of token i.
@@ -85,7 +94,7 @@ typedef struct {
  *                token_pos/16 < max_blocks_per_seq.  (seq, pos) pairs within
  *                one call must be distinct.
  *   k_cache, v_cache  pools (layout above), 16-byte aligned; exactly
- *                H*r_k + r_v fp16 values per token are written, nothing else.
+ *                H_kv*r_k + r_v fp16 values per token are written, nothing else.
  */
 starkv_status starkv_append(const starkv_dims* dims, int32_t n_tokens,
                             const void* k, const void* v,
@@ -106,10 +115,11 @@ size_t starkv_decode_workspace_size(const starkv_dims* dims, int32_t batch,
  * starkv_decode - single-query attention of every sequence in the batch over
  * its latent paged cache (the method's decode step):
  *
- *   K_h = C_k[:,h,:] . B_k[h],  V_h = (C_v . B_v)[:, h*d:(h+1)*d]
- *   out[b,h,:] = softmax(scale * K_h q[b,h]) . V_h      (context_lens[b] tokens)
+ *   K_g = C_k[:,g,:] . B_k[g],  V_g = (C_v . B_v)[:, g*d:(g+1)*d]
+ *   out[b,h,:] = softmax(scale * K_g q[b,h]) . V_g      (context_lens[b] tokens,
+ *                                                        g = h / (H/H_kv))
  *
- * computed in latent space: q is projected by B_k (q~ = scale*log2(e)*B_k[h] q),
+ * computed in latent space: q is projected by B_k (q~ = scale*log2(e)*B_k[g] q),
  * scored against the latents, split into token ranges with a per-range
  * max / sum / weighted latent sum, merged by log-sum-exp and up-projected by
  * B_v.  context_lens[b] == 0 gives a zero output row.
@@ -119,8 +129,8 @@ size_t starkv_decode_workspace_size(const starkv_dims* dims, int32_t batch,
  *                    workspace); 0 <= context_lens[b] <= max_context_len <=
  *                    16*max_blocks_per_seq.
  *   q                [B][H][d] fp16, 16-byte aligned.
- *   b_k              [H][r_k][d] fp16, 16-byte aligned.
- *   b_v              [r_v][H*d] fp16, 2-byte aligned.
+ *   b_k              [H_kv][r_k][d] fp16, 16-byte aligned.
+ *   b_v              [r_v][H_kv*d] fp16, 2-byte aligned.
  *   k_cache, v_cache pools (layout above), 16-byte aligned.  Entries of a
  *                    table row at index >= ceil(len/16), and slots >= len%16 of
  *                    the last block, are never read.

@@ -39,11 +39,14 @@ class Dims(ctypes.Structure):
         ("block_size", ctypes.c_int32),
         ("num_blocks", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
     ]
 
     @classmethod
-    def make(cls, heads, head_dim, rank_k, rank_v, num_blocks, max_blocks_per_seq, block_size=BLOCK_SIZE):
-        return cls(heads, head_dim, rank_k, rank_v, block_size, num_blocks, max_blocks_per_seq)
+    def make(cls, heads, head_dim, rank_k, rank_v, num_blocks, max_blocks_per_seq, block_size=BLOCK_SIZE,
+             kv_heads=None):
+        return cls(heads, head_dim, rank_k, rank_v, block_size, num_blocks, max_blocks_per_seq,
+                   heads if kv_heads is None else kv_heads)
 
 
 _lib = None
@@ -119,10 +122,12 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
-def dims_of(k_cache, v_cache, block_tables, head_dim):
-    nb, heads, bs, rank_k = k_cache.shape
+def dims_of(k_cache, v_cache, block_tables, head_dim, heads=None):
+    """Dims from the cache shapes; `heads` = query heads (default: the cache's key/value heads)."""
+    nb, kv_heads, bs, rank_k = k_cache.shape
     rank_v = v_cache.shape[1]
-    return Dims.make(heads, head_dim, rank_k, rank_v, nb, block_tables.shape[1], block_size=bs)
+    return Dims.make(kv_heads if heads is None else heads, head_dim, rank_k, rank_v, nb, block_tables.shape[1],
+                     block_size=bs, kv_heads=kv_heads)
 
 
 def decode_workspace_size(dims: Dims, batch: int, max_context_len: int) -> int:
@@ -133,15 +138,17 @@ def decode(q, b_k, b_v, k_cache, v_cache, block_tables, context_lens, scale, *,
            max_context_len=None, workspace=None, out=None, stream=None):
     """out[b, h, :] of single-query attention over the latent paged cache.
 
-    q [B, H, d] fp16; b_k [H, r_k, d] fp16; b_v [r_v, H*d] fp16;
-    k_cache [NB, H, 16, r_k] fp16; v_cache [NB, r_v, 16] fp16;
+    q [B, H, d] fp16; b_k [H_kv, r_k, d] fp16; b_v [r_v, H_kv*d] fp16;
+    k_cache [NB, H_kv, 16, r_k] fp16; v_cache [NB, r_v, 16] fp16 (H_kv = H,
+    or a divisor of H for grouped query heads);
     block_tables [B, MB] int32; context_lens [B] int32.  max_context_len
     defaults to 16*MB (no host sync).  Returns out [B, H, d] fp16.
     """
     import torch
     lib = load_library()
     batch, heads, d = q.shape
-    dims = dims_of(k_cache, v_cache, block_tables, d)
+    dims = dims_of(k_cache, v_cache, block_tables, d, heads=heads)
+    kvh = dims.num_kv_heads
     if max_context_len is None:
         max_context_len = BLOCK_SIZE * block_tables.shape[1]
     ptrs = [
@@ -152,7 +159,9 @@ def decode(q, b_k, b_v, k_cache, v_cache, block_tables, context_lens, scale, *,
     ]
     if block_tables.shape[0] != batch or context_lens.shape[0] != batch:
         raise ValueError("block_tables / context_lens rows must match q's batch")
-    if tuple(b_k.shape) != (heads, dims.rank_k, d) or tuple(b_v.shape) != (dims.rank_v, heads * d):
+    if kvh < 1 or heads % kvh != 0:
+        raise ValueError("query heads must be a multiple of the cache's key/value heads")
+    if tuple(b_k.shape) != (kvh, dims.rank_k, d) or tuple(b_v.shape) != (dims.rank_v, kvh * d):
         raise ValueError("projection shapes do not match the caches")
     if tuple(v_cache.shape) != (dims.num_blocks, dims.rank_v, BLOCK_SIZE) or k_cache.shape[2] != BLOCK_SIZE:
         raise ValueError("cache shapes do not match the paged layout")
@@ -176,13 +185,15 @@ def decode(q, b_k, b_v, k_cache, v_cache, block_tables, context_lens, scale, *,
 def append(k, v, w_k, w_v, block_tables, token_seq, token_pos, k_cache, v_cache, *, stream=None):
     """Project new rows into latents and scatter them into the paged caches (in place).
 
-    k, v [n, H, d] fp16; w_k [H, r_k, d] fp16; w_v [r_v, H*d] fp16 (output-major
-    down-projections); token_seq / token_pos [n] int32.
+    k, v [n, H_kv, d] fp16; w_k [H_kv, r_k, d] fp16; w_v [r_v, H_kv*d] fp16
+    (output-major down-projections); token_seq / token_pos [n] int32.
     """
     import torch
     lib = load_library()
     n, heads, d = k.shape
     dims = dims_of(k_cache, v_cache, block_tables, d)
+    if heads != dims.num_kv_heads:
+        raise ValueError("k rows must have the cache's key/value heads")
     ptrs = [
         _need(k, "k", torch.float16, 3), _need(v, "v", torch.float16, 3),
         _need(w_k, "w_k", torch.float16, 3), _need(w_v, "w_v", torch.float16, 2),

@@ -228,14 +228,15 @@ hipError_t append_enqueue(const AppendLaunch& a) {
   const f16* wv = static_cast<const f16*>(a.w_v);
   f16* kc = static_cast<f16*>(a.k_cache);
   f16* vc = static_cast<f16*>(a.v_cache);
-  const int K = s.H * s.D;
+  // new rows, w_k and the K pool are per key/value head
+  const int K = s.KV * s.D;
   if (a.n >= 16 && s.RK % 32 == 0 && s.D % 16 == 0) {
-    const int grid = ((a.n + 31) / 32) * s.H * (s.RK / 32);
-    hipLaunchKernelGGL(append_k_mfma_kernel, dim3(grid), dim3(64), 0, a.stream, k, wk, a.n, s.H, s.D, s.RK,
+    const int grid = ((a.n + 31) / 32) * s.KV * (s.RK / 32);
+    hipLaunchKernelGGL(append_k_mfma_kernel, dim3(grid), dim3(64), 0, a.stream, k, wk, a.n, s.KV, s.D, s.RK,
                        where, kc);
   } else {
-    const int grid = (a.n * s.H * s.RK + 255) / 256;
-    hipLaunchKernelGGL(append_k_valu_kernel, dim3(grid), dim3(256), 0, a.stream, k, wk, a.n, s.H, s.D, s.RK,
+    const int grid = (a.n * s.KV * s.RK + 255) / 256;
+    hipLaunchKernelGGL(append_k_valu_kernel, dim3(grid), dim3(256), 0, a.stream, k, wk, a.n, s.KV, s.D, s.RK,
                        where, kc);
   }
   hipError_t err = hipGetLastError();

@@ -3,8 +3,10 @@
 //
 // Every workgroup owns an equal range of 16-token blocks of the ragged batch
 // (the plan written by the query-projection launch).  Per block:
-//   scores   s[h,t] = q~[h] . c_k[t,h]  - VALU dot products over 16-byte
-//            latent loads, DPP reductions across the lanes of one token;
+//   scores   s[h,t] = q~[h] . c_k[t,g(h)]  - VALU dot products over 16-byte
+//            latent loads, DPP reductions across the lanes of one token; with
+//            grouped query heads every key latent loaded is scored against
+//            all H/H_kv query heads of its group (g(h) = h / (H/H_kv));
 //   softmax  running max / sum per head in the log2 domain, rescaled only when
 //            a block raises a head's maximum by more than kRescaleTau;
 //   values   z[h,:] += P[h,t] . c_v[t,:] - one 32x32x16 f16 MFMA per 32 latent
@@ -30,34 +32,34 @@ namespace starkv {
 // 2. latent attention over a range of paged blocks
 // ---------------------------------------------------------------------------
 
-template <int H, int RK, int RV, int NW>
+template <int H, int HKV, int RK, int RV, int NW>
 struct AttnCfg {
+  static constexpr int G = H / HKV;                       // query heads per key/value head
   static constexpr int kThreads = NW * 64;
-  static constexpr int kBlockKHalves = H * kBlock * RK;   // one block's K latents
+  static constexpr int kBlockKHalves = HKV * kBlock * RK; // one block's K latents
   static constexpr int kPieces = kBlockKHalves / 512;     // 1 KiB pieces (one wave load each)
   static constexpr int PPW = kPieces / NW;                // pieces per wave
   static constexpr int LPT = RK / 8;                      // lanes sharing one token's dot
   static constexpr int kHeadHalves = kBlock * RK;
-  static constexpr int PPH = kHeadHalves >= 512 ? kHeadHalves / 512 : 1;  // pieces per head
   static constexpr int TILES = RV / 32;                   // 32-wide MFMA tiles of the V latent
   static constexpr int TPW = TILES / NW;
   static_assert(H >= 1 && H <= 32, "heads are MFMA rows");
+  static_assert(HKV >= 1 && H % HKV == 0, "query heads split evenly over key/value heads");
   static_assert(kBlockKHalves % 512 == 0 && kPieces % NW == 0 && PPW >= 1, "K pieces per wave");
   static_assert(LPT >= 2 && LPT <= 16 && 512 % RK == 0, "r_k in {16, 32, 64}");
-  static_assert(PPW % PPH == 0, "a wave scores whole heads");
   static_assert(RV % 32 == 0 && TILES % NW == 0 && TPW >= 1, "V tiles per wave");
 };
 
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-template <int H, int RK, int RV, int NW>
+template <int H, int HKV, int RK, int RV, int NW>
 __global__ void __launch_bounds__(NW * 64)
 attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f16* __restrict__ vpool,
             const int32_t* __restrict__ block_tables, int mb_stride,
             const int32_t* __restrict__ context_lens, const int32_t* __restrict__ plan, int batch,
             float* __restrict__ part_z, float* __restrict__ part_ml, float tau) {
-  using C = AttnCfg<H, RK, RV, NW>;
+  using C = AttnCfg<H, HKV, RK, RV, NW>;
   __shared__ float s_lds[2][32][kBlock];
   constexpr int QCAP = 2;            // sequences whose q~ is staged up front
   __shared__ __attribute__((aligned(16))) float q_lds[QCAP][H * RK];
@@ -103,7 +105,7 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
 
   // lane roles for the key scores
   const int c8 = lane % C::LPT;                     // which 8 latents of a token
-  auto piece_head = [&](int j) { return ((w * C::PPW + j) * 512 + lane * 8) / C::kHeadHalves; };
+  auto piece_head = [&](int j) { return ((w * C::PPW + j) * 512 + lane * 8) / C::kHeadHalves; };  // key/value head
   auto piece_tok = [&](int j) { return (((w * C::PPW + j) * 512 + lane * 8) / RK) % kBlock; };
 
   // Latents are read exactly once: non-temporal loads stream them past the
@@ -215,19 +217,25 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     // latent-key scores of this block -> LDS
 #pragma unroll
     for (int j = 0; j < C::PPW; ++j) {
-      const half8 kx = kb[BUF][j];
-      const floatx4* qp = reinterpret_cast<const floatx4*>(qcur + piece_head(j) * RK + c8 * 8);
-      const floatx4 q0 = qp[0], q1 = qp[1];
-      float s = q0[0] * (float)kx[0];
-      s += q0[1] * (float)kx[1];
-      s += q0[2] * (float)kx[2];
-      s += q0[3] * (float)kx[3];
-      s += q1[0] * (float)kx[4];
-      s += q1[1] * (float)kx[5];
-      s += q1[2] * (float)kx[6];
-      s += q1[3] * (float)kx[7];
-      s = group_sum<C::LPT>(s);
-      if (c8 == 0) s_lds[BUF][piece_head(j)][piece_tok(j)] = s;
+      float kx[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kx[e] = (float)kb[BUF][j][e];
+#pragma unroll
+      for (int g = 0; g < C::G; ++g) {
+        const int qh = piece_head(j) * C::G + g;
+        const floatx4* qp = reinterpret_cast<const floatx4*>(qcur + qh * RK + c8 * 8);
+        const floatx4 q0 = qp[0], q1 = qp[1];
+        float s = q0[0] * kx[0];
+        s += q0[1] * kx[1];
+        s += q0[2] * kx[2];
+        s += q0[3] * kx[3];
+        s += q1[0] * kx[4];
+        s += q1[1] * kx[5];
+        s += q1[2] * kx[6];
+        s += q1[3] * kx[7];
+        s = group_sum<C::LPT>(s);
+        if (c8 == 0) s_lds[BUF][qh][piece_tok(j)] = s;
+      }
     }
     const bool more = pf.gi < end;
     const int pphys = more ? phys_of(pf) : cphys;
@@ -316,38 +324,47 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
 // host side
 // ---------------------------------------------------------------------------
 
-template <int H, int RK, int RV, int NW>
+template <int H, int HKV, int RK, int RV, int NW>
 struct AttnInst {
-  static constexpr auto kernel = attn_kernel<H, RK, RV, NW>;
+  static constexpr auto kernel = attn_kernel<H, HKV, RK, RV, NW>;
   static constexpr int threads = NW * 64;
 };
 
-// Shapes built into the library: (H, r_k, r_v, waves per workgroup).  The
-// method picks ranks per layer (adaptive rank control), so 32-head layers come
-// with r_k in {32, 64} and r_v in {256, 512, 768, 1024}; (4, 16, 64) is the
-// small parity shape.
+// Shapes built into the library: (H, H_kv, r_k, r_v, waves per workgroup).
+// The method picks ranks per layer (adaptive rank control), so 32-head layers
+// come with r_k in {32, 64} and r_v in {256, 512, 768, 1024}; grouped-query
+// layers (32 query heads over 8 or 4 key/value heads) with r_v up to the value
+// width H_kv*d; (4, 4, 16, 64) and (8, 2, 32, 64) are the small parity shapes.
 #define STARKV_ATTN_SHAPES(X) \
-  X(32, 64, 1024, 8)          \
-  X(32, 64, 768, 8)           \
-  X(32, 64, 512, 8)           \
-  X(32, 64, 256, 8)           \
-  X(32, 32, 1024, 8)          \
-  X(32, 32, 768, 8)           \
-  X(32, 32, 512, 8)           \
-  X(32, 32, 256, 8)           \
-  X(4, 16, 64, 2)
+  X(32, 32, 64, 1024, 8)      \
+  X(32, 32, 64, 768, 8)       \
+  X(32, 32, 64, 512, 8)       \
+  X(32, 32, 64, 256, 8)       \
+  X(32, 32, 32, 1024, 8)      \
+  X(32, 32, 32, 768, 8)       \
+  X(32, 32, 32, 512, 8)       \
+  X(32, 32, 32, 256, 8)       \
+  X(32, 8, 64, 1024, 8)       \
+  X(32, 8, 64, 512, 8)        \
+  X(32, 8, 64, 256, 8)        \
+  X(32, 8, 32, 512, 8)        \
+  X(32, 8, 32, 256, 8)        \
+  X(32, 4, 64, 512, 8)        \
+  X(32, 4, 64, 256, 8)        \
+  X(4, 4, 16, 64, 2)          \
+  X(8, 2, 32, 64, 2)
 
-int attn_shape_index(int H, int RK, int RV) {
+int attn_shape_index(int H, int KV, int RK, int RV) {
   int i = 0;
-#define X(h, rk, rv, nw)                             \
-  if (H == h && RK == rk && RV == rv) return i;     \
+#define X(h, kv, rk, rv, nw)                                  \
+  if (H == h && KV == kv && RK == rk && RV == rv) return i; \
   ++i;
   STARKV_ATTN_SHAPES(X)
 #undef X
   return -1;
 }
 
-bool attn_shape_supported(int H, int RK, int RV) { return attn_shape_index(H, RK, RV) >= 0; }
+bool attn_shape_supported(int H, int KV, int RK, int RV) { return attn_shape_index(H, KV, RK, RV) >= 0; }
 
 template <typename Inst>
 static int resident_for(int device) {
@@ -361,9 +378,9 @@ static int resident_for(int device) {
   return per_cu * cus;
 }
 
-int attn_resident_grid(int H, int RK, int RV, int device) {
-#define X(h, rk, rv, nw) \
-  if (H == h && RK == rk && RV == rv) return resident_for<AttnInst<h, rk, rv, nw>>(device);
+int attn_resident_grid(int H, int KV, int RK, int RV, int device) {
+#define X(h, kv, rk, rv, nw) \
+  if (H == h && KV == kv && RK == rk && RV == rv) return resident_for<AttnInst<h, kv, rk, rv, nw>>(device);
   STARKV_ATTN_SHAPES(X)
 #undef X
   return 1;
@@ -379,10 +396,10 @@ static void launch_attn(const DecodeLaunch& a, const float* qt, int32_t* plan, f
 hipError_t launch_attn_kernel(const DecodeLaunch& a, const float* qt, int32_t* plan, float* pz, float* pml) {
   const Shape& s = a.s;
   bool launched = false;
-#define X(h, rk, rv, nw)                                                   \
-  if (!launched && s.H == h && s.RK == rk && s.RV == rv) {                 \
-    launch_attn<AttnInst<h, rk, rv, nw>>(a, qt, plan, pz, pml);            \
-    launched = true;                                                       \
+#define X(h, kv, rk, rv, nw)                                                          \
+  if (!launched && s.H == h && s.KV == kv && s.RK == rk && s.RV == rv) {          \
+    launch_attn<AttnInst<h, kv, rk, rv, nw>>(a, qt, plan, pz, pml);               \
+    launched = true;                                                              \
   }
   STARKV_ATTN_SHAPES(X)
 #undef X

@@ -91,7 +91,7 @@ __device__ void build_plan(const int32_t* __restrict__ lens, int batch, int grid
 // (head, 32-latent) output tiles; both operands are contiguous along d.
 __global__ void __launch_bounds__(256)
 qproj_plan_mfma_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, float* __restrict__ qt,
-                       int batch, int H, int D, int RK, float scale2,
+                       int batch, int H, int KV, int D, int RK, float scale2,
                        const int32_t* __restrict__ lens, int grid, int32_t* __restrict__ plan) {
   if (blockIdx.x == gridDim.x - 1) {
     build_plan(lens, batch, grid, plan);
@@ -112,7 +112,7 @@ qproj_plan_mfma_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, fl
   // all operand loads of eight k-steps are in flight before the first MFMA
   const bool brow = b < batch;
   const f16* qrow = q + ((size_t)(brow ? b : batch - 1) * H + head) * D + kofs;
-  const f16* brw = bk + ((size_t)head * RK + r) * D + kofs;
+  const f16* brw = bk + ((size_t)(head / (H / KV)) * RK + r) * D + kofs;   // group's key head
   const int ksteps = D / 16;
   floatx16 acc = {};
   for (int c = 0; c < ksteps; c += 8) {
@@ -137,7 +137,7 @@ qproj_plan_mfma_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, fl
 // VALU path (small batches): one thread per (b, h, r).
 __global__ void __launch_bounds__(256)
 qproj_plan_valu_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, float* __restrict__ qt,
-                       int batch, int H, int D, int RK, float scale2,
+                       int batch, int H, int KV, int D, int RK, float scale2,
                        const int32_t* __restrict__ lens, int grid, int32_t* __restrict__ plan) {
   if (blockIdx.x == gridDim.x - 1) {
     build_plan(lens, batch, grid, plan);
@@ -149,7 +149,7 @@ qproj_plan_valu_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, fl
   const int head = (idx / RK) % H;
   const int b = idx / (RK * H);
   const f16* qp = q + ((size_t)b * H + head) * D;
-  const f16* bp = bk + ((size_t)head * RK + r) * D;
+  const f16* bp = bk + ((size_t)(head / (H / KV)) * RK + r) * D;
   float acc = 0.f;
   for (int i = 0; i < D; i += 8) {
     half8 x = *reinterpret_cast<const half8*>(qp + i);
@@ -273,7 +273,7 @@ constexpr int kUpPad = 8;
 
 __global__ void __launch_bounds__(kUpWaves * 64)
 upproj_mfma_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
-                   int batch, int H, int D, int RV) {
+                   int batch, int H, int KV, int D, int RV) {
   __shared__ __attribute__((aligned(16))) f16 bt[kUpWaves][32][kUpMaxSpan + kUpPad];
   __shared__ float red[kUpWaves][16][64];
   const int lane = threadIdx.x & 63;
@@ -292,11 +292,12 @@ upproj_mfma_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
   const bool brow = b < batch;
   const int n = nt * 32 + (lane & 31);
   const int kofs = (lane >> 5) * 8;
-  const size_t ld = (size_t)H * D;
+  const size_t ld = (size_t)KV * D;
+  const int kvh = h / (H / KV);          // value columns of the group's key/value head
   const int kspan = RV / kUpWaves;       // multiple of 16
   const int kbase = w * kspan;
   // B_v slice rows kbase.., 32 dims from h*D + nt*32: lane -> (row l/4, 8 dims)
-  const f16* bsrc = bv + (size_t)(kbase + (lane >> 2)) * ld + (size_t)h * D + nt * 32 + (lane & 3) * 8;
+  const f16* bsrc = bv + (size_t)(kbase + (lane >> 2)) * ld + (size_t)kvh * D + nt * 32 + (lane & 3) * 8;
   const float* zrow = zf + ((size_t)(brow ? b : batch - 1) * H + h) * RV + kbase + kofs;
   half8 braw[kUpMaxSpan / 16];
   floatx4 za[kUpMaxSpan / 16][2];
@@ -354,7 +355,7 @@ constexpr int kUpvMaxRV = 1024;
 
 __global__ void __launch_bounds__(256)
 upproj_valu_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
-                   int batch, int H, int D, int RV) {
+                   int batch, int H, int KV, int D, int RV) {
   __shared__ __attribute__((aligned(16))) float zl[kSmallBatch][kUpvMaxRV];
   __shared__ float red[64][4][33];
   const int t = threadIdx.x;
@@ -366,12 +367,13 @@ upproj_valu_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
   const bool nlive = n0 + nsub < D;              // D % 8 == 0: a chunk is all in or all out
   const int row0 = blockIdx.y * kSmallBatch;
   const int rows = min(kSmallBatch, batch - row0);
-  const size_t ld = (size_t)H * D;
+  const size_t ld = (size_t)KV * D;
+  const int kvh = h / (H / KV);          // value columns of the group's key/value head
   half8 bvr[kUpvMaxRV / 64];
 #pragma unroll
   for (int i = 0; i < kUpvMaxRV / 64; ++i) {
     const int k = krow + 64 * i;
-    bvr[i] = (nlive && k < RV) ? *reinterpret_cast<const half8*>(bv + (size_t)k * ld + (size_t)h * D + n0 + nsub)
+    bvr[i] = (nlive && k < RV) ? *reinterpret_cast<const half8*>(bv + (size_t)k * ld + (size_t)kvh * D + n0 + nsub)
                                : half8{};
   }
   for (int idx = t; idx < rows * (RV / 4); idx += 256) {
@@ -457,13 +459,13 @@ hipError_t decode_enqueue(const DecodeLaunch& a) {
     const int groups = (s.H * (s.RK / 32) + 3) / 4;
     const int nq = ((a.batch + 31) / 32) * groups;
     hipLaunchKernelGGL(qproj_plan_mfma_kernel, dim3(nq + 1), dim3(256), 0, a.stream,
-                       static_cast<const f16*>(a.q), static_cast<const f16*>(a.b_k), qt, a.batch, s.H, s.D, s.RK,
-                       scale2, a.context_lens, a.grid, plan);
+                       static_cast<const f16*>(a.q), static_cast<const f16*>(a.b_k), qt, a.batch, s.H, s.KV, s.D,
+                       s.RK, scale2, a.context_lens, a.grid, plan);
   } else {
     const int nq = (a.batch * s.H * s.RK + 255) / 256;
     hipLaunchKernelGGL(qproj_plan_valu_kernel, dim3(nq + 1), dim3(256), 0, a.stream,
-                       static_cast<const f16*>(a.q), static_cast<const f16*>(a.b_k), qt, a.batch, s.H, s.D, s.RK,
-                       scale2, a.context_lens, a.grid, plan);
+                       static_cast<const f16*>(a.q), static_cast<const f16*>(a.b_k), qt, a.batch, s.H, s.KV, s.D,
+                       s.RK, scale2, a.context_lens, a.grid, plan);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -493,11 +495,11 @@ hipError_t decode_enqueue(const DecodeLaunch& a) {
     const int groups = ((a.batch + 31) / 32) * s.H;
     const int grid = ((groups + 7) / 8) * 8 * (s.D / 32);
     hipLaunchKernelGGL(upproj_mfma_kernel, dim3(grid), dim3(kUpWaves * 64), 0, a.stream, zf,
-                       static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H, s.D, s.RV);
+                       static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H, s.KV, s.D, s.RV);
   } else {
     const int grid = s.H * ((s.D + 31) / 32);
     hipLaunchKernelGGL(upproj_valu_kernel, dim3(grid, (a.batch + kSmallBatch - 1) / kSmallBatch), dim3(256), 0, a.stream, zf,
-                       static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H, s.D, s.RV);
+                       static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H, s.KV, s.D, s.RV);
   }
   return hipGetLastError();
 }

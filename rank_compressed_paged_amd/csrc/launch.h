@@ -18,6 +18,7 @@ constexpr float kRescaleTau = 8.0f;
 
 struct Shape {
   int H, D, RK, RV, MB;
+  int KV;                 // key/value heads (H for multi-head attention)
 };
 
 // Workspace carving for one decode call.
@@ -29,10 +30,10 @@ struct DecodeLayout {
 
 DecodeLayout decode_layout(const Shape& s, int batch, int max_context_len);
 
-// Returns true if a latent attention kernel is built for (H, r_k, r_v).
-bool attn_shape_supported(int H, int RK, int RV);
-// Position of (H, r_k, r_v) among the built shapes (< kMaxAttnShapes), or -1.
-int attn_shape_index(int H, int RK, int RV);
+// Returns true if a latent attention kernel is built for (H, H_kv, r_k, r_v).
+bool attn_shape_supported(int H, int KV, int RK, int RV);
+// Position of (H, H_kv, r_k, r_v) among the built shapes (< kMaxAttnShapes), or -1.
+int attn_shape_index(int H, int KV, int RK, int RV);
 constexpr int kMaxAttnShapes = 32;
 
 struct DecodeLaunch {
@@ -56,7 +57,7 @@ struct DecodeLaunch {
 };
 
 // Occupancy-derived attention grid for this device (workgroups resident at once).
-int attn_resident_grid(int H, int RK, int RV, int device);
+int attn_resident_grid(int H, int KV, int RK, int RV, int device);
 
 hipError_t decode_enqueue(const DecodeLaunch& a);
 

@@ -21,6 +21,8 @@ starkv_status check_dims(const starkv_dims* d) {
   if (d->num_heads <= 0 || d->head_dim <= 0 || d->rank_k <= 0 || d->rank_v <= 0 || d->block_size <= 0 ||
       d->num_blocks <= 0 || d->max_blocks_per_seq <= 0)
     return STARKV_ERR_INVALID_ARG;
+  if (d->num_kv_heads < 0 || (d->num_kv_heads > 0 && d->num_heads % d->num_kv_heads != 0))
+    return STARKV_ERR_INVALID_ARG;
   if (d->block_size != kBlock) return STARKV_ERR_UNSUPPORTED;
   if (d->head_dim % 8 != 0 || d->head_dim > 256 || d->rank_k % 8 != 0 || d->rank_v % 32 != 0 ||
       d->rank_v > 1024)
@@ -32,7 +34,8 @@ starkv_status check_dims(const starkv_dims* d) {
 }
 
 Shape shape_of(const starkv_dims* d) {
-  return Shape{d->num_heads, d->head_dim, d->rank_k, d->rank_v, d->max_blocks_per_seq};
+  return Shape{d->num_heads, d->head_dim, d->rank_k, d->rank_v, d->max_blocks_per_seq,
+               d->num_kv_heads > 0 ? d->num_kv_heads : d->num_heads};
 }
 
 bool decode_args_ok(const starkv_dims* d, int32_t batch, int32_t max_context_len) {
@@ -46,14 +49,14 @@ bool decode_args_ok(const starkv_dims* d, int32_t batch, int32_t max_context_len
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_resident[kMaxDevices][kMaxAttnShapes];
 
-int resident_grid(int H, int RK, int RV, int device) {
-  const int idx = attn_shape_index(H, RK, RV);
+int resident_grid(int H, int KV, int RK, int RV, int device) {
+  const int idx = attn_shape_index(H, KV, RK, RV);
   if (device < 0 || device >= kMaxDevices || idx < 0 || idx >= kMaxAttnShapes)
-    return attn_resident_grid(H, RK, RV, device);
+    return attn_resident_grid(H, KV, RK, RV, device);
   std::atomic<int>& cell = g_resident[device][idx];
   int v = cell.load(std::memory_order_relaxed);
   if (v <= 0) {
-    v = attn_resident_grid(H, RK, RV, device);
+    v = attn_resident_grid(H, KV, RK, RV, device);
     cell.store(v, std::memory_order_relaxed);
   }
   return v;
@@ -100,14 +103,14 @@ starkv_status starkv_decode(const starkv_dims* dims, int32_t batch, int32_t max_
       !aligned(workspace, 256) || !aligned(out, 2))
     return STARKV_ERR_INVALID_ARG;
   if (!(scale == scale)) return STARKV_ERR_INVALID_ARG;  // NaN scale
-  if (!attn_shape_supported(dims->num_heads, dims->rank_k, dims->rank_v)) return STARKV_ERR_UNSUPPORTED;
   const Shape s = shape_of(dims);
+  if (!attn_shape_supported(s.H, s.KV, s.RK, s.RV)) return STARKV_ERR_UNSUPPORTED;
   const DecodeLayout lay = decode_layout(s, batch, max_context_len);
   if (workspace_bytes < lay.bytes) return STARKV_ERR_WORKSPACE;
 
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) return STARKV_ERR_HIP;
-  int grid = resident_grid(s.H, s.RK, s.RV, device);
+  int grid = resident_grid(s.H, s.KV, s.RK, s.RV, device);
   if (grid > lay.grid_cap) grid = lay.grid_cap;
   if (grid < 1) grid = 1;
 

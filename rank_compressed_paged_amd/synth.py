@@ -89,9 +89,10 @@ CONFIGS = {
               rank_k=64, rank_v=1024, seq=32768, layers=32),
     6: Config(6, "layers32_b4_l32768_mixed_ranks", batch=4, heads=32, head_dim=128,
               rank_k=64, rank_v=1024, seq=32768, layers=32, layer_ranks=MIXED_RANKS_32),
-    # grouped query heads, Llama-3-8B-like attention: 32 query heads over 8 key/value heads
+    # grouped query heads, Llama-3-8B-like attention: 32 query heads over 8
+    # key/value heads; r_k 64 of 128 and r_v 512 of 1024 halve the cache
     7: Config(7, "gqa32x8_b64_l8192", batch=64, heads=32, head_dim=128, rank_k=64,
-              rank_v=1024, seq=8192, kv_heads=8),
+              rank_v=512, seq=8192, kv_heads=8),
 }
 
 

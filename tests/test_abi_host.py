@@ -106,6 +106,19 @@ def test_decode_rejects_before_touching_the_device(lib):
     assert call_decode(lib, d, ws_bytes=1024) == WORKSPACE
 
 
+def test_grouped_heads_checks(lib):
+    assert ctypes.sizeof(starkv.Dims) == 8 * 4                     # eight int32 fields, no padding
+    assert call_decode(lib, main_dims(kv_heads=5)) == INVALID         # must divide the query heads
+    assert call_decode(lib, main_dims(kv_heads=-1)) == INVALID
+    assert call_decode(lib, main_dims(kv_heads=16)) == UNSUPPORTED    # valid, no kernel built
+    assert call_decode(lib, main_dims(kv_heads=8), ws_bytes=1024) == WORKSPACE   # (32, 8, 64, 1024) is built
+    zero = main_dims()
+    zero.num_kv_heads = 0                                             # 0 means "same as num_heads"
+    assert ws_size(lib, zero, 64, 8192) == ws_size(lib, main_dims(), 64, 8192)
+    # partial states are per query head: grouping does not shrink the workspace
+    assert ws_size(lib, main_dims(kv_heads=8), 64, 8192) == ws_size(lib, main_dims(), 64, 8192)
+
+
 def test_append_rejects_before_touching_the_device(lib):
     d = main_dims()
     p = ctypes.c_void_p(0x1000)
