@@ -102,10 +102,6 @@ append_k_valu_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int 
 // reduce through LDS.
 constexpr int kAppendVWaves = 4;
 
-__device__ __forceinline__ floatx4 mfma16x16x32(half8 a, half8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
 __global__ void __launch_bounds__(kAppendVWaves * 64)
 append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
                      SlotOf where, f16* __restrict__ vc) {

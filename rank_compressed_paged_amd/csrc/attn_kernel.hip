@@ -3,10 +3,13 @@
 //
 // Every workgroup owns an equal range of 16-token blocks of the ragged batch
 // (the plan written by the query-projection launch).  Per block:
-//   scores   s[h,t] = q~[h] . c_k[t,g(h)]  - VALU dot products over 16-byte
-//            latent loads, DPP reductions across the lanes of one token; with
-//            grouped query heads every key latent loaded is scored against
-//            all H/H_kv query heads of its group (g(h) = h / (H/H_kv));
+//   scores   s[h,t] = q~[h] . c_k[t,g(h)]  (g(h) = h / (H/H_kv)).  Multi-head
+//            layers: VALU dot products over 16-byte latent loads, DPP
+//            reductions across the lanes of one token.  Grouped heads: a
+//            16x16x32 f16 MFMA per key/value head and 32 latent dims (rows =
+//            the group's query heads, columns = the block's 16 tokens), whose
+//            B operand is one 16-byte load of the token-major K block and
+//            whose A operand is q~ split into fp16 high and low parts;
 //   softmax  running max / sum per head in the log2 domain, rescaled only when
 //            a block raises a head's maximum by more than kRescaleTau;
 //   values   z[h,:] += P[h,t] . c_v[t,:] - one 32x32x16 f16 MFMA per 32 latent
@@ -43,6 +46,23 @@ struct AttnCfg {
   static constexpr int kHeadHalves = kBlock * RK;
   static constexpr int TILES = RV / 32;                   // 32-wide MFMA tiles of the V latent
   static constexpr int TPW = TILES / NW;
+  // Blocks in flight per workgroup: enough that about 128 KiB of latents are
+  // outstanding per CU (one resident workgroup), so small blocks (grouped
+  // heads, low ranks) still cover the HBM latency.
+  static constexpr int kBlockBytes = 2 * (kBlockKHalves + RV * kBlock);
+  static constexpr int NBUF = kBlockBytes >= 64 * 1024 ? 2 : (kBlockBytes >= 43 * 1024 ? 3 : 4);
+  // Grouped heads score on MFMA: a wave owns KPW key/value heads and KSW of
+  // the RK/32 k-steps of each; WPK waves split one head's k-steps and the
+  // softmax adds their SPLIT partial score tiles.
+  static constexpr bool kMfmaScores = G > 1;
+  static constexpr int KSTEPS = RK / 32;
+  static constexpr int WPK = NW >= HKV ? NW / HKV : 1;
+  static constexpr int KPW = HKV >= NW ? HKV / NW : 1;
+  static constexpr int KSW = KSTEPS >= WPK ? KSTEPS / WPK : 1;
+  static constexpr int SPLIT = kMfmaScores ? WPK : 1;
+  static_assert(!kMfmaScores || (G <= 16 && RK % 32 == 0 && (NW % HKV == 0 || HKV % NW == 0) &&
+                                 KSTEPS % WPK == 0 && KPW * KSW == PPW),
+                "grouped-head MFMA score tiling");
   static_assert(H >= 1 && H <= 32, "heads are MFMA rows");
   static_assert(HKV >= 1 && H % HKV == 0, "query heads split evenly over key/value heads");
   static_assert(kBlockKHalves % 512 == 0 && kPieces % NW == 0 && PPW >= 1, "K pieces per wave");
@@ -60,7 +80,8 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
             const int32_t* __restrict__ context_lens, const int32_t* __restrict__ plan, int batch,
             float* __restrict__ part_z, float* __restrict__ part_ml, float tau) {
   using C = AttnCfg<H, HKV, RK, RV, NW>;
-  __shared__ float s_lds[2][32][kBlock];
+  constexpr int NB = C::NBUF;
+  __shared__ float s_lds[NB][C::SPLIT][32][kBlock];
   constexpr int QCAP = 2;            // sequences whose q~ is staged up front
   __shared__ __attribute__((aligned(16))) float q_lds[QCAP][H * RK];
   // Partial-state stash.  On gfx9 stores share the in-order vector-memory
@@ -103,10 +124,15 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     return block_tables[(size_t)it.b * mb_stride + (it.gi - it.lo)];
   };
 
-  // lane roles for the key scores
+  // lane roles for the key scores.  VALU path: a wave reads PPW contiguous
+  // 1 KiB pieces of the block, LPT lanes per token.  MFMA path: key/value head
+  // kv_of(u), k-step ks_of(s); lane l reads token l%16, latents 8*(l/16)..+7
+  // of that k-step.
   const int c8 = lane % C::LPT;                     // which 8 latents of a token
-  auto piece_head = [&](int j) { return ((w * C::PPW + j) * 512 + lane * 8) / C::kHeadHalves; };  // key/value head
+  auto piece_head = [&](int j) { return ((w * C::PPW + j) * 512 + lane * 8) / C::kHeadHalves; };
   auto piece_tok = [&](int j) { return (((w * C::PPW + j) * 512 + lane * 8) / RK) % kBlock; };
+  auto kv_of = [&](int u) { return C::WPK > 1 ? w / C::WPK : w * C::KPW + u; };
+  auto ks_of = [&](int s) { return (w % C::WPK) * C::KSW + s; };
 
   // Latents are read exactly once: non-temporal loads stream them past the
   // caches instead of evicting the small reused data (q~, tables, partials).
@@ -114,10 +140,25 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
   // below) make every wave read the same first piece of a block it already
   // holds, so they cost one cached 1 KiB row per wave instead of a block.
   auto load_k = [&](half8 (&dst)[C::PPW], int phys, bool spare) {
-    const half8* base = reinterpret_cast<const half8*>(kpool + (size_t)phys * C::kBlockKHalves) +
-                        (spare ? 0 : (w * C::PPW) * 64) + lane;
+    if constexpr (C::kMfmaScores) {
+      // spare loads take the pieces wave 0 would read: distinct addresses, so
+      // the compiler cannot merge them and every path issues PPW loads
+      const f16* blk = kpool + (size_t)phys * C::kBlockKHalves + (lane & 15) * RK + (lane >> 4) * 8;
 #pragma unroll
-    for (int j = 0; j < C::PPW; ++j) dst[j] = __builtin_nontemporal_load(base + j * 64);
+      for (int u = 0; u < C::KPW; ++u)
+#pragma unroll
+        for (int s = 0; s < C::KSW; ++s) {
+          const int j = u * C::KSW + s;
+          const int kvh = spare ? j / C::KSTEPS : kv_of(u);
+          const int ks = spare ? j % C::KSTEPS : ks_of(s);
+          dst[j] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(blk + kvh * kBlock * RK + ks * 32));
+        }
+    } else {
+      const half8* base = reinterpret_cast<const half8*>(kpool + (size_t)phys * C::kBlockKHalves) +
+                          (spare ? 0 : (w * C::PPW) * 64) + lane;
+#pragma unroll
+      for (int j = 0; j < C::PPW; ++j) dst[j] = __builtin_nontemporal_load(base + j * 64);
+    }
   };
   auto load_v = [&](half8 (&dst)[C::TPW], int phys, bool spare) {
     const half8* base = reinterpret_cast<const half8*>(vpool + (size_t)phys * (RV * kBlock)) +
@@ -126,8 +167,8 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     for (int t = 0; t < C::TPW; ++t) dst[t] = __builtin_nontemporal_load(base + t * 64);
   };
 
-  half8 kb[2][C::PPW];
-  half8 vb[2][C::TPW];
+  half8 kb[NB][C::PPW];
+  half8 vb[NB][C::TPW];
   floatx16 acc[C::TPW];
   float m_run = -INFINITY, l_run = 0.f;
   int seq_len = 0, slot = 0;
@@ -150,7 +191,34 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
   __syncthreads();
   const float* qcur = q_lds[0];
 
-  // Block i is consumed from buffer (i - start) & 1 while blocks i+1 and i+2
+  // MFMA path: the wave's A operands (q~ of its group's query heads, rows
+  // beyond the group zero) as fp16 high + low parts, held for a segment.
+  // x - hi is exact in fp32, so hi + lo carries q~ to about 2^-22 relative.
+  half8 qa_hi[C::KPW * C::KSW], qa_lo[C::KPW * C::KSW];
+  auto load_qa = [&]() {
+    const int i = lane & 15;
+#pragma unroll
+    for (int u = 0; u < C::KPW; ++u)
+#pragma unroll
+      for (int s = 0; s < C::KSW; ++s) {
+        half8 hi{}, lo{};
+        if (i < C::G) {
+          const floatx4* qp =
+              reinterpret_cast<const floatx4*>(qcur + (kv_of(u) * C::G + i) * RK + ks_of(s) * 32 + (lane >> 4) * 8);
+          const floatx4 q0 = qp[0], q1 = qp[1];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = e < 4 ? q0[e] : q1[e - 4];
+            hi[e] = (f16)x;
+            lo[e] = (f16)(x - (float)hi[e]);
+          }
+        }
+        qa_hi[u * C::KSW + s] = hi;
+        qa_lo[u * C::KSW + s] = lo;
+      }
+  };
+
+  // Block i is consumed from buffer (i - start) % NB while the next NB blocks
   // are in flight.  Every body issues the same loads on every path (past the
   // range end they are `spare` re-reads), so the compiler's in-order wait
   // counts stay exact instead of collapsing to a full drain.
@@ -159,11 +227,12 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
   load_k(kb[0], phys0, false);
   load_v(vb[0], phys0, false);
   advance(pf);
-  {
+#pragma unroll
+  for (int u = 1; u < NB; ++u) {
     const bool more = pf.gi < end;
-    const int phys1 = more ? phys_of(pf) : phys0;
-    load_k(kb[1], phys1, !more);
-    load_v(vb[1], phys1, !more);
+    const int physu = more ? phys_of(pf) : phys0;
+    load_k(kb[u], physu, !more);
+    load_v(vb[u], physu, !more);
     if (more) advance(pf);
   }
 
@@ -207,6 +276,7 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
         __syncthreads();
         qcur = q_lds[0];
       }
+      if constexpr (C::kMfmaScores) load_qa();
       m_run = -INFINITY;
       l_run = 0.f;
 #pragma unroll
@@ -215,26 +285,38 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     const int nvalid = min(kBlock, seq_len - lb * kBlock);
 
     // latent-key scores of this block -> LDS
+    if constexpr (C::kMfmaScores) {
 #pragma unroll
-    for (int j = 0; j < C::PPW; ++j) {
-      float kx[8];
+      for (int u = 0; u < C::KPW; ++u) {
+        floatx4 sc{};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kx[e] = (float)kb[BUF][j][e];
+        for (int s = 0; s < C::KSW; ++s) {
+          sc = mfma16x16x32(qa_hi[u * C::KSW + s], kb[BUF][u * C::KSW + s], sc);
+          sc = mfma16x16x32(qa_lo[u * C::KSW + s], kb[BUF][u * C::KSW + s], sc);
+        }
+        // register r of lane l: query head row 4*(l/16)+r of the group, token l%16
 #pragma unroll
-      for (int g = 0; g < C::G; ++g) {
-        const int qh = piece_head(j) * C::G + g;
-        const floatx4* qp = reinterpret_cast<const floatx4*>(qcur + qh * RK + c8 * 8);
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * (lane >> 4) + r;
+          if (i < C::G) s_lds[BUF][w % C::WPK][kv_of(u) * C::G + i][lane & 15] = sc[r];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::PPW; ++j) {
+        const half8 kx = kb[BUF][j];
+        const floatx4* qp = reinterpret_cast<const floatx4*>(qcur + piece_head(j) * RK + c8 * 8);
         const floatx4 q0 = qp[0], q1 = qp[1];
-        float s = q0[0] * kx[0];
-        s += q0[1] * kx[1];
-        s += q0[2] * kx[2];
-        s += q0[3] * kx[3];
-        s += q1[0] * kx[4];
-        s += q1[1] * kx[5];
-        s += q1[2] * kx[6];
-        s += q1[3] * kx[7];
+        float s = q0[0] * (float)kx[0];
+        s += q0[1] * (float)kx[1];
+        s += q0[2] * (float)kx[2];
+        s += q0[3] * (float)kx[3];
+        s += q1[0] * (float)kx[4];
+        s += q1[1] * (float)kx[5];
+        s += q1[2] * (float)kx[6];
+        s += q1[3] * (float)kx[7];
         s = group_sum<C::LPT>(s);
-        if (c8 == 0) s_lds[BUF][qh][piece_tok(j)] = s;
+        if (c8 == 0) s_lds[BUF][0][piece_head(j)][piece_tok(j)] = s;
       }
     }
     const bool more = pf.gi < end;
@@ -245,8 +327,13 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     // online softmax in the MFMA A-operand layout: row h, tokens 8*half_..+7
     float sv[8];
     {
-      const floatx4 s0 = *reinterpret_cast<const floatx4*>(&s_lds[BUF][h][half_ * 8]);
-      const floatx4 s1 = *reinterpret_cast<const floatx4*>(&s_lds[BUF][h][half_ * 8 + 4]);
+      floatx4 s0 = *reinterpret_cast<const floatx4*>(&s_lds[BUF][0][h][half_ * 8]);
+      floatx4 s1 = *reinterpret_cast<const floatx4*>(&s_lds[BUF][0][h][half_ * 8 + 4]);
+#pragma unroll
+      for (int sp = 1; sp < C::SPLIT; ++sp) {
+        s0 += *reinterpret_cast<const floatx4*>(&s_lds[BUF][sp][h][half_ * 8]);
+        s1 += *reinterpret_cast<const floatx4*>(&s_lds[BUF][sp][h][half_ * 8 + 4]);
+      }
       sv[0] = s0[0]; sv[1] = s0[1]; sv[2] = s0[2]; sv[3] = s0[3];
       sv[4] = s1[0]; sv[5] = s1[1]; sv[6] = s1[2]; sv[7] = s1[3];
     }
@@ -309,13 +396,27 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     advance(cur);
   };
 
-  // pairs keep the loop body free of conditional loads (see above)
+  // whole rings of NB bodies keep the loop free of conditional loads (see
+  // above); the last partial ring runs its bodies while blocks remain
+  static_assert(NB >= 2 && NB <= 4, "ring of 2 to 4 buffers");
   int i = start;
-  for (; i + 1 < end; i += 2) {
+  for (; i + NB - 1 < end; i += NB) {
     body(IC<0>{});
     body(IC<1>{});
+    if constexpr (NB > 2) body(IC<2>{});
+    if constexpr (NB > 3) body(IC<3>{});
   }
-  if (i < end) body(IC<0>{});
+  if (i < end) {
+    body(IC<0>{});
+    if constexpr (NB > 2) {
+      if (i + 1 < end) {
+        body(IC<1>{});
+        if constexpr (NB > 3) {
+          if (i + 2 < end) body(IC<2>{});
+        }
+      }
+    }
+  }
   if (stash_slot >= 0)
     store_partial(stash_slot, [&](int t, int r) { return stash[w][t][r][lane]; }, stash_m, stash_l);
 }

@@ -26,6 +26,13 @@ __device__ __forceinline__ constexpr int mfma_row(int r, int lane) {
   return (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
 }
 
+// 16x16x32 f16 MFMA (gfx950): D[16x16] += A[16x32] * B[32x16], fp32 accumulate.
+// Lane l supplies row (A) / column (B) l%16 and the eight k values
+// 8*(l/16) .. 8*(l/16)+7; result register r of lane l is D[4*(l/16) + r][l%16].
+__device__ __forceinline__ floatx4 mfma16x16x32(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 // DPP sum over groups of G consecutive lanes (G = 1, 2, 4, 8, 16); every lane
 // of a group ends with the group total.
 template <int G>
