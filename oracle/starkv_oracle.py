@@ -33,8 +33,9 @@ Decode result.  Reading the latent-space computation (q projected by B_k,
 weights applied to c_v before B_v) as re-association of the same products,
 the method's output is exactly ordinary single-query softmax attention over
 the reconstructed keys and values.  So the oracle reconstructs K and V in
-fp64 and runs textbook attention.  Every pin of this file lives in
-tests/test_oracle.py.
+fp64 and runs textbook attention.  Prefill (a chunk of new tokens per
+sequence) is the same attention with a causal mask.  Every pin of this file
+lives in tests/test_oracle.py.
 """
 
 from __future__ import annotations
@@ -85,6 +86,47 @@ def decode(q, b_k, b_v, k_pool, v_pool, block_tables, context_lens, scale, block
             scores = float(scale) * (keys @ q[b, h])       # [L]
             w = np.exp(scores - scores.max())
             out[b, h] = (w @ values[:, kv * d:(kv + 1) * d]) / w.sum()
+    return out
+
+
+def prefill(q, b_k, b_v, k_pool, v_pool, block_tables, query_start, context_lens, scale, block_size=16):
+    """Causal attention of a chunk of new tokens per sequence (prefill / chunked prefill).
+
+    Serving engines run a compute-bound prefill phase next to memory-bound
+    decode and batch the two together (scifaro related-papers list, entry on
+    hybrid prefill/decode batching; the Proxima pages wire STAR-KV into a
+    continuous-batching engine).  Reading: the chunk's tokens have already been
+    written into the latent cache, and each of them attends, like a decode
+    query, to every position up to and including its own.
+
+    q [N, H, d]: sequence b owns rows query_start[b] .. query_start[b+1]-1
+    (n_b rows, n_b <= context_lens[b] = L_b); row query_start[b] + i is the
+    token at position L_b - n_b + i and sees positions 0 .. L_b - n_b + i.
+    Other arguments as in decode().  Returns fp64 [N, H, d].
+    """
+    q = np.asarray(q).astype(F64)
+    bk = np.asarray(b_k).astype(F64)
+    bv = np.asarray(b_v).astype(F64)
+    nrows, nh, d = q.shape
+    group = nh // bk.shape[0]
+    out = np.zeros((nrows, nh, d), F64)
+    for b in range(len(context_lens)):
+        r0, r1 = int(query_start[b]), int(query_start[b + 1])
+        n = r1 - r0
+        if n == 0:
+            continue
+        length = int(context_lens[b])
+        assert 0 < n <= length, "a chunk cannot be longer than its sequence"
+        c_k, c_v = gather_latents(k_pool, v_pool, block_tables[b], length, block_size)
+        values = c_v @ bv                                  # [L, H_kv*d]
+        pos = length - n + np.arange(n)                    # positions of the chunk's tokens
+        visible = np.arange(length)[None, :] <= pos[:, None]
+        for h in range(nh):
+            kv = h // group
+            keys = c_k[:, kv, :] @ bk[kv]                  # [L, d]
+            scores = np.where(visible, float(scale) * (q[r0:r1, h] @ keys.T), -np.inf)
+            w = np.exp(scores - scores.max(axis=1, keepdims=True))
+            out[r0:r1, h] = (w @ values[:, kv * d:(kv + 1) * d]) / w.sum(axis=1, keepdims=True)
     return out
 
 

@@ -412,3 +412,107 @@ def test_append_rounds_once_from_exact_value():
     kp2, vp2 = oracle.append(x, x, w_k, w_v, np.array([[0]], np.int32), [0], [4], kp, vp)
     assert kp2.view(np.uint16)[0, 0, 4, 0] == 0x3C01
     assert vp2.view(np.uint16)[0, 0, 4] == 0x3C01
+
+
+# ------------------------------------------------------------ prefill pins
+def chunk_case(seed, lens, chunks, heads=2, head_dim=3, rank_k=2, rank_v=5, kv_heads=None):
+    """A decode-style case plus per-sequence chunk sizes and their query rows."""
+    case = synth.make_case(seed, len(lens), heads, head_dim, rank_k, rank_v, np.array(lens), kv_heads=kv_heads)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    rng = np.random.default_rng(seed + 1000)
+    q = rng.standard_normal((int(qs[-1]), heads, head_dim)).astype(np.float16)
+    return case, qs, q
+
+
+def run_prefill(case, qs, q, scale, **over):
+    c = dict(case)
+    c.update(over)
+    return oracle.prefill(q, c["b_k"], c["b_v"], c["k_pool"], c["v_pool"], c["block_tables"], qs,
+                          c["context_lens"], scale)
+
+
+@pytest.mark.parametrize("scale", [0.6, 2.0])
+def test_prefill_bruteforce_rows(scale):
+    """Every row against scalar loops over exactly the positions it may see
+    (table walked with a counter up to its own position)."""
+    lens, chunks = (37, 16, 20), (5, 16, 1)
+    case, qs, q = chunk_case(61, lens, chunks, heads=3, head_dim=3, rank_k=2, rank_v=4)
+    got = run_prefill(case, qs, q, scale)
+    for b, (n_b, L) in enumerate(zip(chunks, lens)):
+        for i in range(n_b):
+            row = qs[b] + i
+            pos = L - n_b + i
+            ref = brute_decode(q[row][None], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
+                               case["block_tables"][b][None], [pos + 1], scale)
+            np.testing.assert_allclose(got[row], ref[0], rtol=1e-12, atol=1e-14)
+
+
+def test_prefill_grouped_heads_bruteforce():
+    lens, chunks = (33, 18), (7, 18)
+    case, qs, q = chunk_case(62, lens, chunks, heads=4, head_dim=3, rank_k=2, rank_v=5, kv_heads=2)
+    got = run_prefill(case, qs, q, 0.9)
+    for b, (n_b, L) in enumerate(zip(chunks, lens)):
+        for i in range(n_b):
+            ref = brute_decode(q[qs[b] + i][None], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
+                               case["block_tables"][b][None], [L - n_b + i + 1], 0.9)
+            np.testing.assert_allclose(got[qs[b] + i], ref[0], rtol=1e-12, atol=1e-14)
+
+
+def test_prefill_whole_prompt_equals_causal_sdpa():
+    """Full-rank orthogonal B: a chunk covering the whole prompt is causal
+    attention over the original keys and values (torch SDPA, is_causal, fp64)."""
+    rng = np.random.default_rng(63)
+    heads, d = 2, 8
+    lens = [29, 17]
+    bt, nb = random_tables(rng, lens)
+    bk = np.stack([synth.orthonormal_rows(rng, d, d) for _ in range(heads)])
+    bv = synth.orthonormal_rows(rng, heads * d, heads * d)
+    ks = [rng.standard_normal((n, heads, d)) for n in lens]
+    vs = [rng.standard_normal((n, heads, d)) for n in lens]
+    qs_rows = [rng.standard_normal((n, heads, d)) for n in lens]
+    cks = [np.einsum("thi,hri->thr", k, bk) for k in ks]
+    cvs = [v.reshape(len(v), -1) @ bv.T for v in vs]
+    kp, vp = scatter_pools(cks, cvs, bt, nb)
+    qs = np.array([0, lens[0], lens[0] + lens[1]], np.int32)
+    scale = 0.41
+    got = oracle.prefill(np.concatenate(qs_rows), bk, bv, kp, vp, bt, qs, np.array(lens), scale)
+    for b, n in enumerate(lens):
+        for h in range(heads):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(np.ascontiguousarray(qs_rows[b][:, h])[None, None]),
+                torch.from_numpy(np.ascontiguousarray(ks[b][:, h])[None, None]),
+                torch.from_numpy(np.ascontiguousarray(vs[b][:, h])[None, None]),
+                is_causal=True, scale=scale)
+            np.testing.assert_allclose(got[qs[b]:qs[b + 1], h], ref.numpy()[0, 0], rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_single_query_chunks_equal_decode():
+    lens = (40, 1, 23)
+    case, qs, q = chunk_case(64, lens, (1, 1, 1))
+    got = run_prefill(case, qs, q, 0.7)
+    ref = oracle.decode(q, case["b_k"], case["b_v"], case["k_pool"], case["v_pool"], case["block_tables"],
+                        case["context_lens"], 0.7)
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-15)
+
+
+def test_prefill_chunking_is_invisible():
+    """A 30-token chunk gives the same rows as a 12-token chunk (context 30)
+    followed by an 18-token chunk (context 48)."""
+    case, qs, q = chunk_case(65, (48,), (30,))
+    whole = run_prefill(case, qs, q, 1.1)
+    first = run_prefill(case, np.array([0, 12], np.int32), q[:12], 1.1, context_lens=np.array([30]))
+    second = run_prefill(case, np.array([0, 18], np.int32), q[12:], 1.1)
+    np.testing.assert_allclose(np.concatenate([first, second]), whole, rtol=1e-13, atol=1e-15)
+
+
+def test_prefill_first_token_sees_only_itself_and_empty_chunks_skip():
+    """A whole-prompt chunk: row 0 sees position 0 only, so it is that token's
+    value row; a sequence with no queries produces no rows."""
+    case, qs, q = chunk_case(66, (19, 25), (0, 25))
+    got = run_prefill(case, qs, q, 3.0)
+    assert got.shape[0] == 25
+    p = case["block_tables"][1, 0]
+    v_row = case["v_pool"][p, :, 0].astype(F64) @ case["b_v"].astype(F64)
+    d = case["head_dim"]
+    for h in range(case["heads"]):
+        np.testing.assert_allclose(got[0, h], v_row[h * d:(h + 1) * d], rtol=1e-13, atol=1e-15)
