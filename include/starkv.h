@@ -149,15 +149,63 @@ starkv_status starkv_decode(const starkv_dims* dims, int32_t batch, int32_t max_
                             float scale, void* workspace, size_t workspace_bytes,
                             void* out, void* stream);
 
+/*
+ * starkv_prefill_workspace_size - bytes of device scratch starkv_prefill needs
+ * for this (dims, batch, num_queries, max_context_len).  Host-only; returns 0
+ * if the arguments are invalid.
+ */
+size_t starkv_prefill_workspace_size(const starkv_dims* dims, int32_t batch, int32_t num_queries,
+                                     int32_t max_context_len);
+
+/*
+ * starkv_prefill - causal attention of a chunk of new tokens per sequence over
+ * the latent paged cache (prefill and chunked prefill; a serving engine batches
+ * this compute-bound phase next to decode: scifaro related-papers list, entry
+ * on hybrid prefill/decode batching).  The chunk's latents must already be in
+ * the cache (starkv_append), and each chunk token attends to every position up
+ * to and including its own:
+ *
+ *   sequence b owns query rows query_start[b] .. query_start[b+1]-1 (n_b rows);
+ *   row query_start[b] + i is the token at position p = L_b - n_b + i
+ *   (L_b = context_lens[b]) and
+ *   out[row,h,:] = softmax(scale * K_g[0..p] q[row,h]) . V_g[0..p]
+ *   with K_g, V_g reconstructed from the latents as in starkv_decode.
+ *
+ * Computed in latent space like decode; scores and P . c_v run on MFMA with
+ * 64 query rows of one head per workgroup.
+ *
+ *   batch            B >= 1 sequences (rows of block_tables, query_start has
+ *                    B+1 entries, context_lens B).
+ *   num_queries      N = query_start[B] rows of q and out; 0 is a no-op.
+ *   max_context_len  host upper bound of context_lens (sizes the launch and the
+ *                    workspace); 1 <= max_context_len <= 16*max_blocks_per_seq.
+ *   q, out           [N][H][d] fp16 (q 16-byte aligned, out 2-byte aligned).
+ *   b_k, b_v, k_cache, v_cache, block_tables, scale: as in starkv_decode.
+ *   query_start      [B+1] int32, device: 0 = query_start[0] <= ... <=
+ *                    query_start[B] = N.
+ *   context_lens     [B] int32, device: n_b <= context_lens[b] <= max_context_len.
+ *   workspace        device scratch of >= starkv_prefill_workspace_size() bytes,
+ *                    256-byte aligned; garbage afterwards.
+ * Built for r_k in {32, 64} and r_v in {256, 512, 768, 1024} with any H and
+ * H_kv dividing it; other ranks -> STARKV_ERR_UNSUPPORTED.  The device-side
+ * contracts on query_start and context_lens are the caller's.
+ */
+starkv_status starkv_prefill(const starkv_dims* dims, int32_t batch, int32_t num_queries, int32_t max_context_len,
+                             const void* q, const void* b_k, const void* b_v,
+                             const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* query_start,
+                             const int32_t* context_lens, float scale, void* workspace,
+                             size_t workspace_bytes, void* out, void* stream);
+
 /* Static, human-readable name of a status code (host-only). */
 const char* starkv_status_string(starkv_status status);
 
 /*
  * Measurement hooks (host-only, process-wide, not for use while another
  * thread is decoding).  Between starkv_profile_begin() and
- * starkv_profile_end(), every starkv_decode call brackets its latent
- * attention kernel with a pair of HIP events on its own stream (up to 4096
- * calls).  starkv_profile_end() waits for those events, writes the summed
+ * starkv_profile_end(), every starkv_decode and starkv_prefill call brackets
+ * its latent attention kernel with a pair of HIP events on its own stream (up
+ * to 4096 calls).  starkv_profile_end() waits for those events, writes the summed
  * kernel time in milliseconds and the number of bracketed launches, and
  * releases the events.  Returns STARKV_ERR_HIP if an event call failed.
  */

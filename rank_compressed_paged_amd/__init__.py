@@ -13,7 +13,8 @@ import os
 
 __all__ = [
     "Dims", "StarkvError", "load_library", "library_path", "status_string",
-    "decode_workspace_size", "decode", "append", "profile_begin", "profile_end", "stream_read_probe",
+    "decode_workspace_size", "decode", "append", "prefill_workspace_size", "prefill", "profile_begin",
+    "profile_end", "stream_read_probe",
     "BLOCK_SIZE",
 ]
 
@@ -73,6 +74,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.starkv_decode_workspace_size.restype = sz
     lib.starkv_decode.argtypes = [dp, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, vp, sz, vp, vp]
     lib.starkv_decode.restype = ctypes.c_int
+    lib.starkv_prefill_workspace_size.argtypes = [dp, i32, i32, i32]
+    lib.starkv_prefill_workspace_size.restype = sz
+    lib.starkv_prefill.argtypes = [dp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, sz, vp, vp]
+    lib.starkv_prefill.restype = ctypes.c_int
     lib.starkv_append.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.starkv_append.restype = ctypes.c_int
     lib.starkv_profile_begin.argtypes = []
@@ -179,6 +184,59 @@ def decode(q, b_k, b_v, k_cache, v_cache, block_tables, context_lens, scale, *,
                              float(scale), ctypes.c_void_p(ws_ptr + pad), workspace.numel() - pad,
                              ctypes.c_void_p(optr), _stream(stream))
     _check(code, "starkv_decode")
+    return out
+
+
+def prefill_workspace_size(dims: Dims, batch: int, num_queries: int, max_context_len: int) -> int:
+    return int(load_library().starkv_prefill_workspace_size(ctypes.byref(dims), batch, num_queries,
+                                                              max_context_len))
+
+
+def prefill(q, b_k, b_v, k_cache, v_cache, block_tables, query_start, context_lens, scale, *,
+            max_context_len=None, workspace=None, out=None, stream=None):
+    """Causal attention of each sequence's chunk of new tokens over the latent cache.
+
+    q [N, H, d] fp16: rows query_start[b] .. query_start[b+1]-1 belong to
+    sequence b and are its last n_b positions (their latents already appended);
+    query_start [B+1] int32, context_lens [B] int32 (device).  Other arguments
+    as in decode().  max_context_len defaults to 16*MB.  Returns out [N, H, d].
+    """
+    import torch
+    lib = load_library()
+    rows, heads, d = q.shape
+    batch = block_tables.shape[0]
+    dims = dims_of(k_cache, v_cache, block_tables, d, heads=heads)
+    kvh = dims.num_kv_heads
+    if max_context_len is None:
+        max_context_len = BLOCK_SIZE * block_tables.shape[1]
+    ptrs = [
+        _need(q, "q", torch.float16, 3), _need(b_k, "b_k", torch.float16, 3),
+        _need(b_v, "b_v", torch.float16, 2), _need(k_cache, "k_cache", torch.float16, 4),
+        _need(v_cache, "v_cache", torch.float16, 3), _need(block_tables, "block_tables", torch.int32, 2),
+        _need(query_start, "query_start", torch.int32, 1), _need(context_lens, "context_lens", torch.int32, 1),
+    ]
+    if query_start.shape[0] != batch + 1 or context_lens.shape[0] != batch:
+        raise ValueError("query_start needs B+1 entries and context_lens B")
+    if kvh < 1 or heads % kvh != 0:
+        raise ValueError("query heads must be a multiple of the cache's key/value heads")
+    if tuple(b_k.shape) != (kvh, dims.rank_k, d) or tuple(b_v.shape) != (dims.rank_v, kvh * d):
+        raise ValueError("projection shapes do not match the caches")
+    if out is None:
+        out = torch.empty_like(q)
+    if rows == 0:
+        return out
+    need = lib.starkv_prefill_workspace_size(ctypes.byref(dims), batch, rows, int(max_context_len))
+    if need == 0:
+        _check(1, "starkv_prefill_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+    ws_ptr = _need(workspace, "workspace", torch.uint8, 1)
+    pad = (-ws_ptr) % 256
+    optr = _need(out, "out", torch.float16, 3)
+    code = lib.starkv_prefill(ctypes.byref(dims), batch, rows, int(max_context_len), *[ctypes.c_void_p(p) for p in ptrs],
+                              float(scale), ctypes.c_void_p(ws_ptr + pad), workspace.numel() - pad,
+                              ctypes.c_void_p(optr), _stream(stream))
+    _check(code, "starkv_prefill")
     return out
 
 

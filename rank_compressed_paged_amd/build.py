@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libstarkv.so")
-SOURCES = ["starkv_api.hip", "decode_kernels.hip", "attn_kernel.hip", "append_kernels.hip", "probe_kernels.hip"]
+SOURCES = ["starkv_api.hip", "decode_kernels.hip", "attn_kernel.hip", "append_kernels.hip", "prefill_kernels.hip",
+           "probe_kernels.hip"]
 ARCH = "gfx950"
 
 

@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(256)
 qproj_plan_mfma_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, float* __restrict__ qt,
                        int batch, int H, int KV, int D, int RK, float scale2,
                        const int32_t* __restrict__ lens, int grid, int32_t* __restrict__ plan) {
-  if (blockIdx.x == gridDim.x - 1) {
+  if (lens != nullptr && blockIdx.x == gridDim.x - 1) {
     build_plan(lens, batch, grid, plan);
     return;
   }
@@ -139,7 +139,7 @@ __global__ void __launch_bounds__(256)
 qproj_plan_valu_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, float* __restrict__ qt,
                        int batch, int H, int KV, int D, int RK, float scale2,
                        const int32_t* __restrict__ lens, int grid, int32_t* __restrict__ plan) {
-  if (blockIdx.x == gridDim.x - 1) {
+  if (lens != nullptr && blockIdx.x == gridDim.x - 1) {
     build_plan(lens, batch, grid, plan);
     return;
   }
@@ -445,6 +445,51 @@ DecodeLayout decode_layout(const Shape& s, int batch, int max_context_len) {
 }
 
 
+hipError_t launch_qproj(const Shape& s, int rows, const void* q, const void* b_k, float scale2, float* qt,
+                        const int32_t* plan_lens, int plan_grid, int32_t* plan, hipStream_t st) {
+  const int extra = plan_lens ? 1 : 0;      // last workgroup builds the decode plan
+  if (rows >= kSmallBatch && s.RK % 32 == 0 && s.D % 16 == 0) {
+    const int groups = (s.H * (s.RK / 32) + 3) / 4;
+    const int nq = ((rows + 31) / 32) * groups;
+    hipLaunchKernelGGL(qproj_plan_mfma_kernel, dim3(nq + extra), dim3(256), 0, st, static_cast<const f16*>(q),
+                       static_cast<const f16*>(b_k), qt, rows, s.H, s.KV, s.D, s.RK, scale2, plan_lens, plan_grid,
+                       plan);
+  } else {
+    const int nq = (rows * s.H * s.RK + 255) / 256;
+    hipLaunchKernelGGL(qproj_plan_valu_kernel, dim3(nq + extra), dim3(256), 0, st, static_cast<const f16*>(q),
+                       static_cast<const f16*>(b_k), qt, rows, s.H, s.KV, s.D, s.RK, scale2, plan_lens, plan_grid,
+                       plan);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const Shape& s, int rows, const float* pz, const float* pml, const int32_t* plan,
+                        const int32_t* lens, float* zf, hipStream_t st) {
+  // few (row, head) pairs -> long sequences split into many ranges
+  const bool few = (long long)rows * s.H < 512;
+  if (few)
+    hipLaunchKernelGGL(merge_kernel<4>, dim3(rows * s.H * ((s.RV + 255) / 256)), dim3(256), 0, st, pz, pml, plan,
+                       lens, rows, s.H, s.RV, zf);
+  else
+    hipLaunchKernelGGL(merge_kernel<1>, dim3(rows * s.H * ((s.RV + 1023) / 1024)), dim3(256), 0, st, pz, pml, plan,
+                       lens, rows, s.H, s.RV, zf);
+  return hipGetLastError();
+}
+
+hipError_t launch_upproj(const Shape& s, int rows, const float* zf, const void* b_v, void* out, hipStream_t st) {
+  if (rows >= kSmallBatch && s.D % 32 == 0 && s.RV % (16 * kUpWaves) == 0 && s.RV <= kUpWaves * kUpMaxSpan) {
+    const int groups = ((rows + 31) / 32) * s.H;
+    const int grid = ((groups + 7) / 8) * 8 * (s.D / 32);
+    hipLaunchKernelGGL(upproj_mfma_kernel, dim3(grid), dim3(kUpWaves * 64), 0, st, zf,
+                       static_cast<const f16*>(b_v), static_cast<f16*>(out), rows, s.H, s.KV, s.D, s.RV);
+  } else {
+    const int grid = s.H * ((s.D + 31) / 32);
+    hipLaunchKernelGGL(upproj_valu_kernel, dim3(grid, (rows + kSmallBatch - 1) / kSmallBatch), dim3(256), 0, st, zf,
+                       static_cast<const f16*>(b_v), static_cast<f16*>(out), rows, s.H, s.KV, s.D, s.RV);
+  }
+  return hipGetLastError();
+}
+
 hipError_t decode_enqueue(const DecodeLaunch& a) {
   const Shape& s = a.s;
   int32_t* plan = reinterpret_cast<int32_t*>(a.ws + a.lay.off_plan);
@@ -455,19 +500,7 @@ hipError_t decode_enqueue(const DecodeLaunch& a) {
   const float scale2 = a.scale * kLog2e;
 
   // 1. query projection + plan (plan = last workgroup)
-  if (a.batch >= kSmallBatch && s.RK % 32 == 0 && s.D % 16 == 0) {
-    const int groups = (s.H * (s.RK / 32) + 3) / 4;
-    const int nq = ((a.batch + 31) / 32) * groups;
-    hipLaunchKernelGGL(qproj_plan_mfma_kernel, dim3(nq + 1), dim3(256), 0, a.stream,
-                       static_cast<const f16*>(a.q), static_cast<const f16*>(a.b_k), qt, a.batch, s.H, s.KV, s.D,
-                       s.RK, scale2, a.context_lens, a.grid, plan);
-  } else {
-    const int nq = (a.batch * s.H * s.RK + 255) / 256;
-    hipLaunchKernelGGL(qproj_plan_valu_kernel, dim3(nq + 1), dim3(256), 0, a.stream,
-                       static_cast<const f16*>(a.q), static_cast<const f16*>(a.b_k), qt, a.batch, s.H, s.KV, s.D,
-                       s.RK, scale2, a.context_lens, a.grid, plan);
-  }
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch_qproj(s, a.batch, a.q, a.b_k, scale2, qt, a.context_lens, a.grid, plan, a.stream);
   if (err != hipSuccess) return err;
 
   // 2. latent attention
@@ -478,30 +511,10 @@ hipError_t decode_enqueue(const DecodeLaunch& a) {
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
-  // 3. merge
-  // few (sequence, head) pairs -> long sequences split into many ranges
-  const bool few = (long long)a.batch * s.H < 512;
-  if (few)
-    hipLaunchKernelGGL(merge_kernel<4>, dim3(a.batch * s.H * ((s.RV + 255) / 256)), dim3(256), 0, a.stream, pz,
-                       pml, plan, a.context_lens, a.batch, s.H, s.RV, zf);
-  else
-    hipLaunchKernelGGL(merge_kernel<1>, dim3(a.batch * s.H * ((s.RV + 1023) / 1024)), dim3(256), 0, a.stream, pz,
-                       pml, plan, a.context_lens, a.batch, s.H, s.RV, zf);
-  err = hipGetLastError();
+  // 3. merge, 4. up-projection
+  err = launch_merge(s, a.batch, pz, pml, plan, a.context_lens, zf, a.stream);
   if (err != hipSuccess) return err;
-
-  // 4. up-projection
-  if (a.batch >= kSmallBatch && s.D % 32 == 0 && s.RV % (16 * kUpWaves) == 0 && s.RV <= kUpWaves * kUpMaxSpan) {
-    const int groups = ((a.batch + 31) / 32) * s.H;
-    const int grid = ((groups + 7) / 8) * 8 * (s.D / 32);
-    hipLaunchKernelGGL(upproj_mfma_kernel, dim3(grid), dim3(kUpWaves * 64), 0, a.stream, zf,
-                       static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H, s.KV, s.D, s.RV);
-  } else {
-    const int grid = s.H * ((s.D + 31) / 32);
-    hipLaunchKernelGGL(upproj_valu_kernel, dim3(grid, (a.batch + kSmallBatch - 1) / kSmallBatch), dim3(256), 0, a.stream, zf,
-                       static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H, s.KV, s.D, s.RV);
-  }
-  return hipGetLastError();
+  return launch_upproj(s, a.batch, zf, a.b_v, a.out, a.stream);
 }
 
 }  // namespace starkv

@@ -1,0 +1,511 @@
+// STAR-KV chunked prefill over the latent paged cache, gfx950 (MI355X).
+//
+// A prefill call attends a chunk of new tokens per sequence (already appended
+// to the latent cache) to every cached position up to and including its own.
+// Five launches on the caller's stream:
+//   1. prefill_plan   one workgroup: 64-row query tiles of every chunk, the
+//                     context ranges of each tile, and the partial-state slots
+//                     of each query row;
+//   2. qproj          q~ = scale*log2(e) * B_k[g(h)] q for every query row
+//                     (shared with decode);
+//   3. prefill_attn   per (tile, context range, query head): scores on MFMA,
+//                     causal online softmax, z += P . c_v on MFMA;
+//   4. merge          log-sum-exp merge of each row's range partials (shared);
+//   5. upproj         out = Z . B_v column block (shared).
+//
+// Method: Proxima README text on wpnews ("Show HN: Proxima ..."), opening
+// description of STAR-KV (head-wise K latents, one joint V latent, compressed
+// paged storage, served by a continuous-batching engine); prefill as the
+// compute-bound phase batched next to decode per the scifaro related-papers
+// list (hybrid prefill/decode batching entry).
+//
+// Work split.  The joint V latent is shared by every head and every query, so
+// a workgroup takes 64 query rows of ONE head: each V block it reads (16
+// tokens x r_v) serves 64 rows, and the 32 heads of a (tile, range) run on the
+// same XCD so the block comes from that XCD's L2 after the first read.  The
+// per-row state is r_v wide (z), which bounds a workgroup to 64 rows: eight
+// waves each hold 128 latent dims of all 64 rows (128 accumulator VGPRs).
+//
+// Per 16-token block:
+//   waves 0-3   S[16 rows x 16 tokens] = q~ . c_k^T on 16x16x32 MFMA (q~ as
+//               fp16 high + low parts, B fragment = one 16-byte load of the
+//               token-major K block), causal mask, online softmax with lazy
+//               rescale; P (fp16) and the rows' rescale factors go to LDS;
+//   all waves   z[64 rows x own 128 dims] += P . c_v on 32x32x16 MFMA (B
+//               fragment = one 16-byte load of the dim-major V block).
+// Scores of block i+1 are computed after block i's MFMAs are issued, so the
+// VALU softmax of waves 0-3 overlaps the MFMAs of waves 4-7; one barrier per
+// block.
+
+#include <math.h>
+
+#include <atomic>
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace starkv {
+
+// ---------------------------------------------------------------------------
+// plan
+// ---------------------------------------------------------------------------
+
+__device__ static int pf_block_scan(int v, int* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int t = (tid >= off) ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += t;
+    __syncthreads();
+  }
+  return sh[tid];
+}
+
+// Inclusive positions: row i of sequence b (0 <= i < n_b) sits at position
+// L_b - n_b + i.  Tile j of sequence b holds rows j*64 .. min(n_b, j*64+64)-1
+// and needs context blocks 0 .. (position of its last row)/16.
+__global__ void __launch_bounds__(256)
+prefill_plan_kernel(const int32_t* __restrict__ qs, const int32_t* __restrict__ lens, int batch, int rows,
+                    int range_blocks, int tile_cap, int32_t* __restrict__ plan) {
+  __shared__ int sh[256];
+  const int tid = threadIdx.x;
+  const PrefillPlan P{plan, rows, tile_cap};
+  int32_t* slot_base = P.slot_base_w();
+  int32_t* row_len = P.row_len_w();
+  int32_t* tile_seq = P.tile_seq_w();
+  int32_t* tile_j = P.tile_j_w();
+  int32_t* tile_items = P.tile_items_w();
+
+  // 1. tiles of every sequence
+  int carry = 0;
+  for (int base = 0; base < batch; base += 256) {
+    const int i = base + tid;
+    const int n = (i < batch) ? qs[i + 1] - qs[i] : 0;
+    const int nt = (n + kPfRows - 1) / kPfRows;
+    const int x = pf_block_scan(nt, sh);
+    const int chunk = sh[255];
+    for (int j = 0; j < nt; ++j) {
+      const int t = carry + x - nt + j;
+      if (t < tile_cap) {
+        tile_seq[t] = i;
+        tile_j[t] = j;
+      }
+    }
+    carry += chunk;
+    __syncthreads();
+  }
+  const int tiles = min(carry, tile_cap);
+
+  // 2. context ranges of every tile -> items
+  int items = 0;
+  for (int base = 0; base < tiles; base += 256) {
+    const int t = base + tid;
+    int nr = 0;
+    if (t < tiles) {
+      const int b = tile_seq[t], j = tile_j[t];
+      const int n = qs[b + 1] - qs[b];
+      const int last = max(0, lens[b] - n + min((j + 1) * kPfRows, n) - 1);   // position of the tile's last row
+      const int blocks = last / kBlock + 1;
+      nr = (blocks + range_blocks - 1) / range_blocks;
+    }
+    const int x = pf_block_scan(nr, sh);
+    const int chunk = sh[255];
+    if (t < tiles) tile_items[t] = items + x - nr;
+    items += chunk;
+    __syncthreads();
+  }
+
+  // 3. partial slots of every query row: one per range its context reaches
+  int slots = 0;
+  for (int base = 0; base < rows; base += 256) {
+    const int r = base + tid;
+    int ns = 0;
+    if (r < rows) {
+      int lo = 0, hi = batch;                 // last b with qs[b] <= r
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (qs[mid] <= r) lo = mid; else hi = mid;
+      }
+      const int n = qs[lo + 1] - qs[lo];
+      const int pos = max(0, lens[lo] - n + (r - qs[lo]));
+      ns = (pos / kBlock + range_blocks) / range_blocks;   // ceil((pos/16 + 1) / RB)
+      row_len[r] = pos + 1;
+    }
+    const int x = pf_block_scan(ns, sh);
+    const int chunk = sh[255];
+    if (r < rows) slot_base[r] = slots + x - ns;
+    slots += chunk;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    plan[0] = range_blocks;
+    plan[1] = items;
+    plan[2] = tiles;
+    tile_items[tiles] = items;
+    slot_base[rows] = slots;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------
+
+template <int RK, int RV>
+struct PfCfg {
+  static constexpr int KS = RK / 32;               // 16x16x32 k-steps of a score tile
+  static constexpr int TPW = RV / 32 / kPfWaves;   // 32-dim V tiles per wave
+  static_assert(RK % 32 == 0 && KS >= 1 && KS <= 2, "r_k in {32, 64}");
+  static_assert(RV % (32 * kPfWaves) == 0 && TPW >= 1 && TPW <= 4, "r_v in {256, 512, 768, 1024}");
+};
+
+template <int N>
+using PfIC = std::integral_constant<int, N>;
+
+// max over the 16 lanes of a DPP row (lanes 16g .. 16g+15)
+__device__ __forceinline__ float group_max16(float x) {
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)));
+  return x;
+}
+
+template <int RK, int RV>
+__global__ void __launch_bounds__(kPfWaves * 64)
+prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f16* __restrict__ vpool,
+                    const int32_t* __restrict__ block_tables, int mb_stride, const int32_t* __restrict__ qs,
+                    const int32_t* __restrict__ lens, const int32_t* __restrict__ plan, int rows, int tile_cap,
+                    int H, int G, int HKV, float* __restrict__ part_z, float* __restrict__ part_ml, float tau) {
+  using C = PfCfg<RK, RV>;
+  __shared__ __attribute__((aligned(16))) f16 p_lds[2][kPfRows][kBlock];
+  __shared__ float a_lds[2][kPfRows];
+  __shared__ int flag_lds[2][4];
+  __shared__ int slot_lds[kPfRows];
+  // score A operands of the scorer waves (each lane reads back only its own)
+  __shared__ half8 qa_lds[4][C::KS][2][64];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int c32 = lane & 31;
+  const int half_ = lane >> 5;
+  const bool scorer = w < 4;               // waves 0-3 score 16 rows each
+  const PrefillPlan P{const_cast<int32_t*>(plan), rows, tile_cap};
+  const int range_blocks = plan[0];
+  const int items = plan[1];
+  const int tiles = plan[2];
+  const int32_t* __restrict__ tile_items = P.tile_items_w();
+  const int32_t* __restrict__ slot_base = P.slot_base_w();
+  const long long units = (long long)((items + 7) & ~7) * H;
+
+  for (long long u = blockIdx.x; u < units; u += gridDim.x) {
+    // XCD-aware order: the H heads of an item share u % 8, hence one XCD
+    const int x = (int)(u % 8);
+    const long long sidx = u / 8;
+    const int h = (int)(sidx % H);
+    const int item = (int)(sidx / H) * 8 + x;
+    if (item >= items) continue;
+    int lo = 0, hi = tiles;                  // last tile with tile_items[t] <= item
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_items[mid] <= item) lo = mid; else hi = mid;
+    }
+    const int k = item - tile_items[lo];
+    const int b = P.tile_seq_w()[lo];
+    const int j = P.tile_j_w()[lo];
+    const int n_b = qs[b + 1] - qs[b];
+    const int L = lens[b];
+    const int row0 = qs[b] + j * kPfRows;
+    const int nrows = min(kPfRows, n_b - j * kPfRows);
+    const int pos0 = L - n_b + j * kPfRows;  // position of tile row 0
+    const int ctx_blocks = (pos0 + nrows - 1) / kBlock + 1;
+    const int blk_lo = k * range_blocks;
+    const int nblk = min(ctx_blocks, blk_lo + range_blocks) - blk_lo;
+    const int kvh = h / G;
+    const int32_t* __restrict__ table = block_tables + (size_t)b * mb_stride + blk_lo;
+
+    if (threadIdx.x < kPfRows) {
+      const int r = threadIdx.x;
+      const bool reach = r < nrows && (pos0 + r) / kBlock >= blk_lo;
+      slot_lds[r] = reach ? slot_base[row0 + r] + k : -1;
+    }
+
+    // score operands: lane l of scorer wave w owns tile row w*16 + l%16 and
+    // latent dims 8*(l/16) .. +7 of every 32-dim k-step; q~ as fp16 high +
+    // low parts (x - hi is exact in fp32, so hi + lo keeps ~22 bits)
+    if (scorer) {
+      const int rr = w * 16 + (lane & 15);
+      const bool live = rr < nrows;
+      const float* qrow = qt + ((size_t)(live ? row0 + rr : 0) * H + h) * RK + (lane >> 4) * 8;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        half8 hi8{}, lo8{};
+        if (live) {
+          const floatx4 q0 = *reinterpret_cast<const floatx4*>(qrow + ks * 32);
+          const floatx4 q1 = *reinterpret_cast<const floatx4*>(qrow + ks * 32 + 4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = e < 4 ? q0[e] : q1[e - 4];
+            hi8[e] = (f16)v;
+            lo8[e] = (f16)(v - (float)hi8[e]);
+          }
+        }
+        qa_lds[w][ks][0][lane] = hi8;
+        qa_lds[w][ks][1][lane] = lo8;
+      }
+    }
+
+    const f16* kbase = kpool + ((size_t)kvh * kBlock + (lane & 15)) * RK + (lane >> 4) * 8;
+    const f16* vbase = vpool + ((size_t)(w * C::TPW * 32 + c32)) * kBlock + 8 * half_;
+    auto load_k = [&](half8 (&dst)[C::KS], int phys) {
+      const f16* p = kbase + (size_t)phys * HKV * kBlock * RK;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) dst[ks] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(p + ks * 32));
+    };
+    auto load_v = [&](half8 (&dst)[C::TPW], int phys) {
+      const f16* p = vbase + (size_t)phys * RV * kBlock;
+#pragma unroll
+      for (int t = 0; t < C::TPW; ++t)
+        dst[t] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(p + t * 32 * kBlock));
+    };
+
+    half8 kb[2][C::KS];
+    half8 vb[2][C::TPW];
+    floatx16 acc[2][C::TPW];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int t = 0; t < C::TPW; ++t) acc[rt][t] = floatx16{};
+    float m_run[4], l_run[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m_run[i] = -INFINITY;
+      l_run[i] = 0.f;
+    }
+
+    // scores, causal mask and online softmax of block ib (scorer waves)
+    auto score = [&](auto bufc, int ib) {
+      constexpr int BUF = decltype(bufc)::value;
+      floatx4 sc{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        sc = mfma16x16x32(qa_lds[w][ks][0][lane], kb[BUF][ks], sc);
+        sc = mfma16x16x32(qa_lds[w][ks][1][lane], kb[BUF][ks], sc);
+      }
+      const int tpos = (blk_lo + ib) * kBlock + (lane & 15);
+      bool any_need = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rrow = w * 16 + 4 * (lane >> 4) + i;      // register i: row 4*(l/16)+i, token l%16
+        const bool valid = rrow < nrows && tpos <= pos0 + rrow;
+        const float s = valid ? sc[i] : -INFINITY;
+        const float bm = group_max16(s);
+        const bool need = bm > m_run[i] + tau;
+        const float m_new = need ? bm : m_run[i];
+        const float alpha = need ? fast_exp2(m_run[i] - m_new) : 1.f;
+        const float p = valid ? fast_exp2(s - m_new) : 0.f;
+        const f16 p16 = (f16)p;
+        l_run[i] = l_run[i] * alpha + group_sum<16>((float)p16);
+        m_run[i] = m_new;
+        any_need |= need;
+        p_lds[BUF][rrow][lane & 15] = p16;
+        if ((lane & 15) == 0) a_lds[BUF][rrow] = alpha;
+      }
+      const bool wave_need = __any(any_need);
+      if (lane == 0) flag_lds[BUF][w] = wave_need ? 1 : 0;
+    };
+
+    // z += P . c_v of block ib (all waves)
+    auto accumulate = [&](auto bufc, int ib) {
+      constexpr int BUF = decltype(bufc)::value;
+      if (flag_lds[BUF][0] | flag_lds[BUF][1] | flag_lds[BUF][2] | flag_lds[BUF][3]) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float a = a_lds[BUF][rt * 32 + mfma_row(r, lane)];
+#pragma unroll
+            for (int t = 0; t < C::TPW; ++t) acc[rt][t][r] *= a;
+          }
+      }
+      const int tail = L - (blk_lo + ib) * kBlock;          // slots past the sequence end may hold anything
+      if (tail < kBlock) {
+#pragma unroll
+        for (int t = 0; t < C::TPW; ++t)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (8 * half_ + e >= tail) vb[BUF][t][e] = (f16)0.f;
+      }
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const half8 pa = *reinterpret_cast<const half8*>(&p_lds[BUF][rt * 32 + c32][8 * half_]);
+#pragma unroll
+        for (int t = 0; t < C::TPW; ++t) acc[rt][t] = mfma32x32x16(pa, vb[BUF][t], acc[rt][t]);
+      }
+    };
+
+    // Prologue: K and V of blocks 0 and 1 in flight, scores of block 0.
+    // Loads past the range re-read block 0 (always in range), so every path
+    // issues the same loads and the in-order wait counts stay exact.
+    const int phys0 = table[0];
+    const int phys1 = nblk > 1 ? table[1] : phys0;
+    load_k(kb[0], phys0);
+    load_k(kb[1], phys1);
+    load_v(vb[0], phys0);
+    load_v(vb[1], phys1);
+    if (scorer) score(PfIC<0>{}, 0);
+    load_k(kb[0], nblk > 2 ? table[2] : phys0);
+    __syncthreads();
+
+    auto step = [&](auto bufc, int ib) {
+      constexpr int BUF = decltype(bufc)::value;
+      accumulate(bufc, ib);
+      load_v(vb[BUF], ib + 2 < nblk ? table[ib + 2] : phys0);
+      if (scorer && ib + 1 < nblk) score(PfIC<1 - BUF>{}, ib + 1);
+      load_k(kb[1 - BUF], ib + 3 < nblk ? table[ib + 3] : phys0);
+      __syncthreads();
+    };
+    int ib = 0;
+    for (; ib + 1 < nblk; ib += 2) {
+      step(PfIC<0>{}, ib);
+      step(PfIC<1>{}, ib + 1);
+    }
+    if (ib < nblk) step(PfIC<0>{}, ib);
+
+    // partial state of every row whose context reaches this range
+    if (scorer && (lane & 15) == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rrow = w * 16 + 4 * (lane >> 4) + i;
+        const int sl = slot_lds[rrow];
+        if (sl >= 0) {
+          part_ml[((size_t)sl * H + h) * 2 + 0] = m_run[i];
+          part_ml[((size_t)sl * H + h) * 2 + 1] = l_run[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int sl = slot_lds[rt * 32 + mfma_row(r, lane)];
+        if (sl >= 0) {
+          float* zp = part_z + ((size_t)sl * H + h) * RV + w * C::TPW * 32 + c32;
+#pragma unroll
+          for (int t = 0; t < C::TPW; ++t) zp[t * 32] = acc[rt][t][r];
+        }
+      }
+    __syncthreads();                         // LDS is reused by the next item
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+#define STARKV_PREFILL_SHAPES(X) \
+  X(64, 1024)                    \
+  X(64, 768)                     \
+  X(64, 512)                     \
+  X(64, 256)                     \
+  X(32, 1024)                    \
+  X(32, 768)                     \
+  X(32, 512)                     \
+  X(32, 256)
+
+bool prefill_shape_supported(int RK, int RV) {
+#define X(rk, rv) \
+  if (RK == rk && RV == rv) return true;
+  STARKV_PREFILL_SHAPES(X)
+#undef X
+  return false;
+}
+
+static size_t pf_align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+PrefillLayout prefill_layout(const Shape& s, int batch, int rows, int max_context_len) {
+  PrefillLayout L{};
+  const int max_blocks = max(1, (max_context_len + kBlock - 1) / kBlock);
+  L.tile_cap = min(batch, rows) + rows / kPfRows + 1;
+  // Ranges: only as many as it takes to give ~kPfTargetUnits (tile, range,
+  // head) units; each range writes 64 rows x r_v fp32 of partial state per
+  // head, so short ranges would cost more traffic than they save in balance.
+  const long long units_per_range = (long long)L.tile_cap * s.H;
+  int ranges = (int)((kPfTargetUnits + units_per_range - 1) / units_per_range);
+  ranges = max(1, min(ranges, kPfMaxRanges));
+  L.range_blocks = max(kPfMinRangeBlocks, (max_blocks + ranges - 1) / ranges);
+  L.max_ranges = (max_blocks + L.range_blocks - 1) / L.range_blocks;
+  L.max_slots = (long long)rows * L.max_ranges;
+  size_t off = 0;
+  L.off_plan = off;
+  off = pf_align256(off + sizeof(int32_t) * PrefillPlan::ints(rows, L.tile_cap));
+  L.off_qt = off;
+  off = pf_align256(off + sizeof(float) * (size_t)rows * s.H * s.RK);
+  L.off_ml = off;
+  off = pf_align256(off + sizeof(float) * (size_t)L.max_slots * s.H * 2);
+  L.off_z = off;
+  off = pf_align256(off + sizeof(float) * (size_t)L.max_slots * s.H * s.RV);
+  L.off_zf = off;
+  off = pf_align256(off + sizeof(float) * (size_t)rows * s.H * s.RV);
+  L.bytes = off;
+  return L;
+}
+
+template <int RK, int RV>
+static hipError_t launch_pf_attn(const PrefillLaunch& a, const float* qt, const int32_t* plan, float* pz,
+                                 float* pml, int device) {
+  const auto kernel = prefill_attn_kernel<RK, RV>;
+  static std::atomic<int> resident[64];
+  int res = (device >= 0 && device < 64) ? resident[device].load(std::memory_order_relaxed) : 0;
+  if (res <= 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kPfWaves * 64, 0) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1) cus = 1;
+    res = per_cu * cus;
+    if (device >= 0 && device < 64) resident[device].store(res, std::memory_order_relaxed);
+  }
+  const Shape& s = a.s;
+  const long long units_ub = (long long)(((long long)a.lay.tile_cap * a.lay.max_ranges + 7) / 8) * 8 * s.H;
+  long long grid = units_ub < res ? units_ub : res;
+  grid = ((grid + 7) / 8) * 8;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPfWaves * 64), 0, a.stream, qt,
+                     static_cast<const f16*>(a.k_cache), static_cast<const f16*>(a.v_cache), a.block_tables, s.MB,
+                     a.query_start, a.context_lens, plan, a.rows, a.lay.tile_cap, s.H, s.H / s.KV, s.KV, pz, pml,
+                     kRescaleTau);
+  return hipGetLastError();
+}
+
+hipError_t prefill_enqueue(const PrefillLaunch& a, int device) {
+  const Shape& s = a.s;
+  int32_t* plan = reinterpret_cast<int32_t*>(a.ws + a.lay.off_plan);
+  float* qt = reinterpret_cast<float*>(a.ws + a.lay.off_qt);
+  float* pml = reinterpret_cast<float*>(a.ws + a.lay.off_ml);
+  float* pz = reinterpret_cast<float*>(a.ws + a.lay.off_z);
+  float* zf = reinterpret_cast<float*>(a.ws + a.lay.off_zf);
+
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(256), 0, a.stream, a.query_start, a.context_lens, a.batch,
+                     a.rows, a.lay.range_blocks, a.lay.tile_cap, plan);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  err = launch_qproj(s, a.rows, a.q, a.b_k, a.scale * kLog2e, qt, nullptr, 0, nullptr, a.stream);
+  if (err != hipSuccess) return err;
+
+  if (a.ev_attn_start && hipEventRecord(a.ev_attn_start, a.stream) != hipSuccess) return hipErrorUnknown;
+  err = hipErrorInvalidValue;
+#define X(rk, rv) \
+  if (s.RK == rk && s.RV == rv) err = launch_pf_attn<rk, rv>(a, qt, plan, pz, pml, device);
+  STARKV_PREFILL_SHAPES(X)
+#undef X
+  if (err != hipSuccess) return err;
+  if (a.ev_attn_stop && hipEventRecord(a.ev_attn_stop, a.stream) != hipSuccess) return hipErrorUnknown;
+
+  const PrefillPlan P{plan, a.rows, a.lay.tile_cap};
+  err = launch_merge(s, a.rows, pz, pml, plan, P.row_len_w(), zf, a.stream);
+  if (err != hipSuccess) return err;
+  return launch_upproj(s, a.rows, zf, a.b_v, a.out, a.stream);
+}
+
+}  // namespace starkv

@@ -69,6 +69,28 @@ bool g_prof_err = false;
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_prof_events;
 constexpr size_t kMaxProfiled = 4096;
 
+// While profiling is on, hands out a fresh pair of events that the call
+// records around its attention kernel (nullptr otherwise).
+void profile_events(hipEvent_t& start, hipEvent_t& stop) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on || g_prof_events.size() >= kMaxProfiled) return;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
+    g_prof_events.emplace_back(e0, e1);
+    start = e0;
+    stop = e1;
+  } else {
+    g_prof_err = true;
+    if (e0) (void)hipEventDestroy(e0);
+  }
+}
+
+bool prefill_args_ok(const starkv_dims* d, int32_t batch, int32_t num_queries, int32_t max_context_len) {
+  if (batch < 1 || batch > (1 << 20) || num_queries < 1 || num_queries > (1 << 22)) return false;
+  if (max_context_len < 1 || (long long)max_context_len > (long long)kBlock * d->max_blocks_per_seq) return false;
+  return (long long)num_queries * ((max_context_len + kBlock - 1) / kBlock) < (1LL << 40);
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,21 +153,59 @@ starkv_status starkv_decode(const starkv_dims* dims, int32_t batch, int32_t max_
   a.out = out;
   a.stream = static_cast<hipStream_t>(stream);
 
-  {
-    std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (g_prof_on && g_prof_events.size() < kMaxProfiled) {
-      hipEvent_t e0 = nullptr, e1 = nullptr;
-      if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
-        g_prof_events.emplace_back(e0, e1);
-        a.ev_attn_start = e0;
-        a.ev_attn_stop = e1;
-      } else {
-        g_prof_err = true;
-        if (e0) (void)hipEventDestroy(e0);
-      }
-    }
-  }
+  profile_events(a.ev_attn_start, a.ev_attn_stop);
   return decode_enqueue(a) == hipSuccess ? STARKV_OK : STARKV_ERR_HIP;
+}
+
+size_t starkv_prefill_workspace_size(const starkv_dims* dims, int32_t batch, int32_t num_queries,
+                                     int32_t max_context_len) {
+  if (check_dims(dims) != STARKV_OK || !prefill_args_ok(dims, batch, num_queries, max_context_len)) return 0;
+  return prefill_layout(shape_of(dims), batch, num_queries, max_context_len).bytes;
+}
+
+starkv_status starkv_prefill(const starkv_dims* dims, int32_t batch, int32_t num_queries, int32_t max_context_len,
+                             const void* q, const void* b_k, const void* b_v, const void* k_cache,
+                             const void* v_cache, const int32_t* block_tables, const int32_t* query_start,
+                             const int32_t* context_lens, float scale, void* workspace, size_t workspace_bytes,
+                             void* out, void* stream) {
+  const starkv_status ds = check_dims(dims);
+  if (ds != STARKV_OK) return ds;
+  if (num_queries == 0 && batch >= 1) return STARKV_OK;
+  if (!prefill_args_ok(dims, batch, num_queries, max_context_len)) return STARKV_ERR_INVALID_ARG;
+  if (!q || !b_k || !b_v || !k_cache || !v_cache || !block_tables || !query_start || !context_lens || !workspace ||
+      !out)
+    return STARKV_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(b_k, 16) || !aligned(b_v, 2) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(block_tables, 4) || !aligned(query_start, 4) ||
+      !aligned(context_lens, 4) || !aligned(workspace, 256) || !aligned(out, 2))
+    return STARKV_ERR_INVALID_ARG;
+  if (!(scale == scale)) return STARKV_ERR_INVALID_ARG;
+  const Shape s = shape_of(dims);
+  if (!prefill_shape_supported(s.RK, s.RV)) return STARKV_ERR_UNSUPPORTED;
+  const PrefillLayout lay = prefill_layout(s, batch, num_queries, max_context_len);
+  if (workspace_bytes < lay.bytes) return STARKV_ERR_WORKSPACE;
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return STARKV_ERR_HIP;
+
+  PrefillLaunch a{};
+  a.s = s;
+  a.batch = batch;
+  a.rows = num_queries;
+  a.q = q;
+  a.b_k = b_k;
+  a.b_v = b_v;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.query_start = query_start;
+  a.context_lens = context_lens;
+  a.scale = scale;
+  a.ws = static_cast<char*>(workspace);
+  a.lay = lay;
+  a.out = out;
+  a.stream = static_cast<hipStream_t>(stream);
+  profile_events(a.ev_attn_start, a.ev_attn_stop);
+  return prefill_enqueue(a, device) == hipSuccess ? STARKV_OK : STARKV_ERR_HIP;
 }
 
 starkv_status starkv_append(const starkv_dims* dims, int32_t n_tokens, const void* k, const void* v,

@@ -231,6 +231,25 @@ def make_case(seed: int, batch: int, heads: int, head_dim: int, rank_k: int, ran
                 heads=heads, kv_heads=kvh, head_dim=head_dim, rank_k=rank_k, rank_v=rank_v)
 
 
+def make_prefill_case(seed: int, heads: int, head_dim: int, rank_k: int, rank_v: int, context_lens, chunks, *,
+                      kv_heads: int | None = None, key: tuple = (), sentinel: bool = True, spare_tokens: int = 0):
+    """A prefill call's inputs: the decode case's cache plus one chunk per sequence.
+
+    chunks[b] <= context_lens[b] query rows belong to sequence b (its last
+    chunks[b] positions); q is [sum(chunks), H, d], query_start [B+1].
+    """
+    context_lens = np.asarray(context_lens, np.int32)
+    chunks = np.asarray(chunks, np.int32)
+    assert len(chunks) == len(context_lens) and (chunks <= context_lens).all() and (chunks >= 0).all()
+    case = make_case(seed, len(context_lens), heads, head_dim, rank_k, rank_v, context_lens, kv_heads=kv_heads,
+                     key=key, sentinel=sentinel, spare_tokens=spare_tokens)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    case["q"] = normal_f16(seed, (10, *key), (int(qs[-1]), heads, head_dim), scale=1.0 / math.sqrt(head_dim))
+    case["query_start"] = qs
+    case["chunks"] = chunks
+    return case
+
+
 def make_config_case(cfg: Config, layer: int = 0, spare_tokens: int = 0, sentinel: bool = True):
     lens = context_lengths(cfg)
     key = (layer,) if cfg.layers > 1 else ()

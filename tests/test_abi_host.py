@@ -141,3 +141,39 @@ def test_profile_hooks_without_launches(lib):
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         starkv.load_library(str(tmp_path / "nope.so"))
+
+
+def call_prefill(lib, dims, batch=2, rows=8, max_len=64, ptr=0x1000, ws_bytes=1 << 30, scale=0.1):
+    p = ctypes.c_void_p(ptr)
+    return lib.starkv_prefill(ctypes.byref(dims) if dims is not None else None, batch, rows, max_len,
+                              p, p, p, p, p, p, p, p, scale, p, ws_bytes, p, None)
+
+
+def test_prefill_rejects_before_touching_the_device(lib):
+    d = main_dims()
+    assert call_prefill(lib, None) == INVALID
+    assert call_prefill(lib, d, rows=0, ptr=0) == OK                 # no queries: no-op
+    assert call_prefill(lib, d, ptr=0) == INVALID
+    assert call_prefill(lib, d, ptr=0x1008) == INVALID               # 16-byte alignment
+    assert call_prefill(lib, d, batch=0) == INVALID
+    assert call_prefill(lib, d, rows=-1) == INVALID
+    assert call_prefill(lib, d, max_len=0) == INVALID
+    assert call_prefill(lib, d, max_len=512 * 16 + 1) == INVALID
+    assert call_prefill(lib, d, scale=float("nan")) == INVALID
+    assert call_prefill(lib, main_dims(rank_k=16)) == UNSUPPORTED     # score k-steps need r_k % 32 == 0
+    assert call_prefill(lib, main_dims(rank_v=128)) == UNSUPPORTED
+    assert call_prefill(lib, main_dims(kv_heads=5)) == INVALID
+    assert call_prefill(lib, d, ws_bytes=1024) == WORKSPACE
+
+
+def test_prefill_workspace_size(lib):
+    d = main_dims()
+    f = lib.starkv_prefill_workspace_size
+    a = f(ctypes.byref(d), 4, 2048, 8192)
+    assert a > 0 and a % 256 == 0
+    # q~ and the merged latent rows alone: rows * H * (r_k + r_v) fp32
+    assert a >= 2048 * 32 * (64 + 1024) * 4
+    assert f(ctypes.byref(d), 4, 512, 8192) < a
+    assert f(ctypes.byref(d), 0, 512, 8192) == 0
+    assert f(ctypes.byref(d), 4, 0, 8192) == 0
+    assert f(ctypes.byref(d), 4, 512, 512 * 16 + 1) == 0
