@@ -13,7 +13,8 @@ Prints one JSON line.  Options:
   --gpus N                 only 1 is supported (one GPU per box)
   --no-cpu-baseline        skip the oracle timing
   --no-ceiling             skip the HBM read-ceiling probe
-  --config N               time workload N (1-6) instead; own JSON line
+  --config N               time decode workload N (1-7) instead; own JSON line
+  --prefill N              time prefill workload N (1-3) instead; own JSON line
   --calib-copy             run only a plain device copy of known size (for
                            scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
 """
@@ -224,6 +225,74 @@ def config_report(cfg_id: int, steps: int, warmup: int):
     print(json.dumps(line), flush=True)
 
 
+PEAK_MFMA_F16_TFLOPS = 2500.0
+
+
+def prefill_report(cfg_id: int, steps: int, warmup: int):
+    """Time prefill workload N: a step appends every sequence's chunk (its K/V
+    rows into the latent cache) and runs the causal prefill of the chunk.
+
+    The attention kernel is compute-bound: algorithmic flops are 2 H (r_k +
+    r_v) per (query row, visible position) pair - the latent scores and the
+    P . c_v accumulation - reported against the dense f16 MFMA peak.
+    """
+    import torch
+
+    import rank_compressed_paged_amd as starkv
+    from rank_compressed_paged_amd import synth
+
+    dev = torch.device("cuda:0")
+    cfg = synth.PREFILL_CONFIGS[cfg_id]
+    lens = np.full(cfg.batch, cfg.seq, np.int32)
+    chunks = np.full(cfg.batch, cfg.chunk, np.int32)
+    case = synth.make_prefill_case(cfg.seed, cfg.heads, cfg.head_dim, cfg.rank_k, cfg.rank_v, lens, chunks,
+                                   kv_heads=cfg.kv)
+    n = int(chunks.sum())
+    k_new, v_new = synth.make_new_rows(cfg.seed, n, cfg.kv, cfg.head_dim)
+    g = {k: torch.from_numpy(v).to(dev) for k, v in case.items() if isinstance(v, np.ndarray)}
+    kn = torch.from_numpy(k_new).to(dev)
+    vn = torch.from_numpy(v_new).to(dev)
+    seqs = torch.from_numpy(np.repeat(np.arange(cfg.batch, dtype=np.int32), cfg.chunk)).to(dev)
+    pos = torch.from_numpy(np.tile(np.arange(cfg.seq - cfg.chunk, cfg.seq, dtype=np.int32), cfg.batch)).to(dev)
+    dims = starkv.dims_of(g["k_pool"], g["v_pool"], g["block_tables"], cfg.head_dim, heads=cfg.heads)
+    ws = torch.empty(starkv.prefill_workspace_size(dims, cfg.batch, n, cfg.seq) + 256, dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty_like(g["q"])
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+
+    def step():
+        starkv.append(kn, vn, g["b_k"], g["b_v"], g["block_tables"], seqs, pos, g["k_pool"], g["v_pool"])
+        starkv.prefill(g["q"], g["b_k"], g["b_v"], g["k_pool"], g["v_pool"], g["block_tables"], g["query_start"],
+                       g["context_lens"], scale, max_context_len=cfg.seq, workspace=ws, out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starkv.profile_begin()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    e1.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    attn_ms, launches = starkv.profile_end()
+    flops = 2.0 * cfg.heads * (cfg.rank_k + cfg.rank_v) * cfg.pairs()
+    attn_s = attn_ms / launches / 1e3
+    line = {
+        "prefill_config": cfg.index, "workload": cfg.name, "batch": cfg.batch, "chunk": cfg.chunk,
+        "context": cfg.seq, "heads": cfg.heads, "kv_heads": cfg.kv, "rank_k": cfg.rank_k, "rank_v": cfg.rank_v,
+        "steps": steps, "warmup": warmup, "ms_per_step": total_ms / steps,
+        "prefill_tokens_per_s": n * steps / (total_ms / 1e3),
+        "attn_kernel_us_per_launch": attn_s * 1e6,
+        "attn_algorithmic_tflops": flops / attn_s / 1e12,
+        "attn_frac_of_f16_mfma_peak": flops / attn_s / 1e12 / PEAK_MFMA_F16_TFLOPS,
+        "pairs_per_launch": cfg.pairs(),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +303,8 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true", help="skip the HBM read-ceiling probe")
     ap.add_argument("--config", type=int, default=0,
                     help="time workload 1-7 instead (prints its own JSON line)")
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="time prefill workload 1-3 instead (prints its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr, flush=True)
@@ -243,6 +314,9 @@ def main():
         return
     if args.config:
         config_report(args.config, args.steps, args.warmup)
+        return
+    if args.prefill:
+        prefill_report(args.prefill, args.steps, args.warmup)
         return
 
     import torch

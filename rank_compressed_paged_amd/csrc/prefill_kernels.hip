@@ -33,9 +33,11 @@
 //               rescale; P (fp16) and the rows' rescale factors go to LDS;
 //   all waves   z[64 rows x own 128 dims] += P . c_v on 32x32x16 MFMA (B
 //               fragment = one 16-byte load of the dim-major V block).
-// Scores of block i+1 are computed after block i's MFMAs are issued, so the
-// VALU softmax of waves 0-3 overlaps the MFMAs of waves 4-7; one barrier per
-// block.
+// Scores run two blocks ahead of the accumulation (three P buffers in LDS):
+// the score MFMAs of block i+2 enter each SIMD's MFMA pipe before block i's z
+// MFMAs, and their softmax runs while those drain; one barrier per block.
+// K and V use plain loads: every block is re-read by the other heads'
+// workgroups on the same XCD and should stay in its L2.
 
 #include <math.h>
 
@@ -180,9 +182,11 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
                     const int32_t* __restrict__ lens, const int32_t* __restrict__ plan, int rows, int tile_cap,
                     int H, int G, int HKV, float* __restrict__ part_z, float* __restrict__ part_ml, float tau) {
   using C = PfCfg<RK, RV>;
-  __shared__ __attribute__((aligned(16))) f16 p_lds[2][kPfRows][kBlock];
-  __shared__ float a_lds[2][kPfRows];
-  __shared__ int flag_lds[2][4];
+  // P, rescale factors and rescale flags of three blocks in flight: scores
+  // run two blocks ahead of the z accumulation
+  __shared__ __attribute__((aligned(16))) f16 p_lds[3][kPfRows][kBlock];
+  __shared__ float a_lds[3][kPfRows];
+  __shared__ __attribute__((aligned(16))) int flag_lds[3][4];
   __shared__ int slot_lds[kPfRows];
   // score A operands of the scorer waves (each lane reads back only its own)
   __shared__ half8 qa_lds[4][C::KS][2][64];
@@ -257,18 +261,21 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
       }
     }
 
+    // Plain (temporal) loads: unlike decode, every K and V block here is
+    // re-read by the other heads' workgroups on this XCD and must stay in L2
+    // (non-temporal loads cost 25% at 4 x 512 rows over 8192 positions).
     const f16* kbase = kpool + ((size_t)kvh * kBlock + (lane & 15)) * RK + (lane >> 4) * 8;
     const f16* vbase = vpool + ((size_t)(w * C::TPW * 32 + c32)) * kBlock + 8 * half_;
     auto load_k = [&](half8 (&dst)[C::KS], int phys) {
       const f16* p = kbase + (size_t)phys * HKV * kBlock * RK;
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) dst[ks] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(p + ks * 32));
+      for (int ks = 0; ks < C::KS; ++ks) dst[ks] = *reinterpret_cast<const half8*>(p + ks * 32);
     };
     auto load_v = [&](half8 (&dst)[C::TPW], int phys) {
       const f16* p = vbase + (size_t)phys * RV * kBlock;
 #pragma unroll
       for (int t = 0; t < C::TPW; ++t)
-        dst[t] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(p + t * 32 * kBlock));
+        dst[t] = *reinterpret_cast<const half8*>(p + t * 32 * kBlock);
     };
 
     half8 kb[2][C::KS];
@@ -278,15 +285,17 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int t = 0; t < C::TPW; ++t) acc[rt][t] = floatx16{};
-    float m_run[4], l_run[4];
+    // running max of each of the lane's 4 rows, and the lane's share of the
+    // row sums (one token per lane; reduced over the 16 lanes at the end)
+    float m_run[4], l_part[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       m_run[i] = -INFINITY;
-      l_run[i] = 0.f;
+      l_part[i] = 0.f;
     }
 
-    // scores, causal mask and online softmax of block ib (scorer waves)
-    auto score = [&](auto bufc, int ib) {
+    // scores of a block held in kb[BUF] (scorer waves)
+    auto score_mfma = [&](auto bufc) -> floatx4 {
       constexpr int BUF = decltype(bufc)::value;
       floatx4 sc{};
 #pragma unroll
@@ -294,38 +303,60 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
         sc = mfma16x16x32(qa_lds[w][ks][0][lane], kb[BUF][ks], sc);
         sc = mfma16x16x32(qa_lds[w][ks][1][lane], kb[BUF][ks], sc);
       }
+      return sc;
+    };
+    // causal mask and online softmax of block ib (scorer waves) -> P, rescale
+    // factors and flag in LDS buffer PB
+    auto softmax = [&](int PB, const floatx4 sc, int ib) {
       const int tpos = (blk_lo + ib) * kBlock + (lane & 15);
-      bool any_need = false;
+      float s[4];
+      bool exceed = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rrow = w * 16 + 4 * (lane >> 4) + i;      // register i: row 4*(l/16)+i, token l%16
         const bool valid = rrow < nrows && tpos <= pos0 + rrow;
-        const float s = valid ? sc[i] : -INFINITY;
-        const float bm = group_max16(s);
-        const bool need = bm > m_run[i] + tau;
-        const float m_new = need ? bm : m_run[i];
-        const float alpha = need ? fast_exp2(m_run[i] - m_new) : 1.f;
-        const float p = valid ? fast_exp2(s - m_new) : 0.f;
-        const f16 p16 = (f16)p;
-        l_run[i] = l_run[i] * alpha + group_sum<16>((float)p16);
-        m_run[i] = m_new;
-        any_need |= need;
-        p_lds[BUF][rrow][lane & 15] = p16;
-        if ((lane & 15) == 0) a_lds[BUF][rrow] = alpha;
+        s[i] = valid ? sc[i] : -INFINITY;
+        exceed |= s[i] > m_run[i] + tau;
       }
-      const bool wave_need = __any(any_need);
-      if (lane == 0) flag_lds[BUF][w] = wave_need ? 1 : 0;
+      // Lazy rescale: while no score beats its row's running max by more than
+      // tau, P = exp2(s - m) <= 2^tau needs no row reduction at all.
+      const bool rescale = __any(exceed);
+      if (rescale) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rrow = w * 16 + 4 * (lane >> 4) + i;
+          const float bm = group_max16(s[i]);
+          const bool need = bm > m_run[i] + tau;
+          const float m_new = need ? bm : m_run[i];
+          const float alpha = need ? fast_exp2(m_run[i] - m_new) : 1.f;
+          l_part[i] *= alpha;
+          m_run[i] = m_new;
+          if ((lane & 15) == 0) a_lds[PB][rrow] = alpha;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rrow = w * 16 + 4 * (lane >> 4) + i;
+        const f16 p16 = s[i] != -INFINITY ? (f16)fast_exp2(s[i] - m_run[i]) : (f16)0.f;
+        l_part[i] += (float)p16;
+        p_lds[PB][rrow][lane & 15] = p16;
+      }
+      if (lane == 0) flag_lds[PB][w] = rescale ? 1 : 0;
     };
 
-    // z += P . c_v of block ib (all waves)
-    auto accumulate = [&](auto bufc, int ib) {
+    // z += P . c_v of block ib (all waves): V in vb[BUF], P in LDS buffer PB
+    auto accumulate = [&](auto bufc, int PB, int ib) {
       constexpr int BUF = decltype(bufc)::value;
-      if (flag_lds[BUF][0] | flag_lds[BUF][1] | flag_lds[BUF][2] | flag_lds[BUF][3]) {
+      half8 pa[2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) pa[rt] = *reinterpret_cast<const half8*>(&p_lds[PB][rt * 32 + c32][8 * half_]);
+      const int4 fl = *reinterpret_cast<const int4*>(&flag_lds[PB][0]);
+      if (fl.x | fl.y | fl.z | fl.w) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float a = a_lds[BUF][rt * 32 + mfma_row(r, lane)];
+            const float a = a_lds[PB][rt * 32 + mfma_row(r, lane)];
 #pragma unroll
             for (int t = 0; t < C::TPW; ++t) acc[rt][t][r] *= a;
           }
@@ -339,32 +370,40 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
             if (8 * half_ + e >= tail) vb[BUF][t][e] = (f16)0.f;
       }
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const half8 pa = *reinterpret_cast<const half8*>(&p_lds[BUF][rt * 32 + c32][8 * half_]);
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int t = 0; t < C::TPW; ++t) acc[rt][t] = mfma32x32x16(pa, vb[BUF][t], acc[rt][t]);
-      }
+        for (int t = 0; t < C::TPW; ++t) acc[rt][t] = mfma32x32x16(pa[rt], vb[BUF][t], acc[rt][t]);
     };
 
-    // Prologue: K and V of blocks 0 and 1 in flight, scores of block 0.
-    // Loads past the range re-read block 0 (always in range), so every path
-    // issues the same loads and the in-order wait counts stay exact.
+    // Prologue: K and V of blocks 0 and 1 in flight; scores of blocks 0 and
+    // 1.  K of block b lives in kb[b & 1], V in vb[b & 1], P in LDS buffer
+    // b % 3.  Loads past the range re-read block 0 (always in range), so every
+    // path issues the same loads and the in-order wait counts stay exact.
     const int phys0 = table[0];
     const int phys1 = nblk > 1 ? table[1] : phys0;
     load_k(kb[0], phys0);
     load_k(kb[1], phys1);
     load_v(vb[0], phys0);
     load_v(vb[1], phys1);
-    if (scorer) score(PfIC<0>{}, 0);
+    if (scorer) softmax(0, score_mfma(PfIC<0>{}), 0);
     load_k(kb[0], nblk > 2 ? table[2] : phys0);
+    if (scorer && nblk > 1) softmax(1, score_mfma(PfIC<1>{}), 1);
+    load_k(kb[1], nblk > 3 ? table[3] : phys0);
     __syncthreads();
 
+    // Step ib: scores of block ib+2 go into the MFMA pipe first, then block
+    // ib's z MFMAs; the softmax of block ib+2 runs while those drain.
+    int pb = 0;                              // ib % 3
     auto step = [&](auto bufc, int ib) {
       constexpr int BUF = decltype(bufc)::value;
-      accumulate(bufc, ib);
+      floatx4 sc{};
+      if (scorer) sc = score_mfma(bufc);     // block ib+2 (a spare block past the end)
+      accumulate(bufc, pb, ib);
       load_v(vb[BUF], ib + 2 < nblk ? table[ib + 2] : phys0);
-      if (scorer && ib + 1 < nblk) score(PfIC<1 - BUF>{}, ib + 1);
-      load_k(kb[1 - BUF], ib + 3 < nblk ? table[ib + 3] : phys0);
+      const int pb2 = pb == 0 ? 2 : pb - 1;  // (ib + 2) % 3
+      if (scorer && ib + 2 < nblk) softmax(pb2, sc, ib + 2);
+      load_k(kb[BUF], ib + 4 < nblk ? table[ib + 4] : phys0);
+      pb = pb == 2 ? 0 : pb + 1;
       __syncthreads();
     };
     int ib = 0;
@@ -375,14 +414,15 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
     if (ib < nblk) step(PfIC<0>{}, ib);
 
     // partial state of every row whose context reaches this range
-    if (scorer && (lane & 15) == 0) {
+    if (scorer) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        const float l_row = group_sum<16>(l_part[i]);
         const int rrow = w * 16 + 4 * (lane >> 4) + i;
         const int sl = slot_lds[rrow];
-        if (sl >= 0) {
+        if ((lane & 15) == 0 && sl >= 0) {
           part_ml[((size_t)sl * H + h) * 2 + 0] = m_run[i];
-          part_ml[((size_t)sl * H + h) * 2 + 1] = l_run[i];
+          part_ml[((size_t)sl * H + h) * 2 + 1] = l_row;
         }
       }
     }

@@ -96,6 +96,48 @@ CONFIGS = {
 }
 
 
+@dataclass(frozen=True)
+class PrefillConfig:
+    """A prefill workload: every sequence appends a chunk of `chunk` tokens
+    that ends at position seq-1, then attends it over its cache."""
+    index: int
+    name: str
+    batch: int
+    heads: int
+    head_dim: int
+    rank_k: int
+    rank_v: int
+    seq: int
+    chunk: int
+    kv_heads: int | None = None
+
+    @property
+    def seed(self) -> int:
+        return BASE_SEED + 100 + self.index
+
+    @property
+    def kv(self) -> int:
+        return self.heads if self.kv_heads is None else self.kv_heads
+
+    def pairs(self) -> int:
+        """(query row, visible position) pairs of one prefill call."""
+        first = self.seq - self.chunk + 1                 # visible positions of the chunk's first row
+        return self.batch * (first + self.seq) * self.chunk // 2
+
+
+PREFILL_CONFIGS = {
+    # chunked prefill at serving size: 512-token chunks of 8192-token contexts
+    1: PrefillConfig(1, "prefill_b4_c512_l8192", batch=4, heads=32, head_dim=128, rank_k=64, rank_v=1024,
+                     seq=8192, chunk=512),
+    # one whole 4096-token prompt
+    2: PrefillConfig(2, "prefill_prompt_b1_l4096", batch=1, heads=32, head_dim=128, rank_k=64, rank_v=1024,
+                     seq=4096, chunk=4096),
+    # grouped heads, chunked
+    3: PrefillConfig(3, "prefill_gqa32x8_b4_c512_l8192", batch=4, heads=32, head_dim=128, rank_k=64,
+                     rank_v=512, seq=8192, chunk=512, kv_heads=8),
+}
+
+
 def _seq(seed: int, *key: int) -> np.random.SeedSequence:
     return np.random.SeedSequence(entropy=seed, spawn_key=tuple(int(k) for k in key))
 
