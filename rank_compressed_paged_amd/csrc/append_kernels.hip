@@ -156,6 +156,56 @@ append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
   }
 }
 
+// V side, many tokens (prefill chunks): a workgroup of eight waves computes a
+// [64 tokens x 128 latents] tile, so each v row is read by 4 waves and each
+// w_v row by 2 instead of once per 16x16 tile.  Wave w owns tokens 32*(w&1)
+// and latents 32*(w>>1) of the tile: A = v rows, B = w_v rows (both contiguous
+// along the contraction), eight k-steps of loads in flight.  All token tiles of
+// one latent tile share its w_v rows and run on one XCD.
+constexpr int kAppendRowsTok = 64;
+constexpr int kAppendRowsLat = 128;
+
+__global__ void __launch_bounds__(512)
+append_v_rows_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
+                     SlotOf where, f16* __restrict__ vc) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int ttiles = (n + kAppendRowsTok - 1) / kAppendRowsTok;
+  const int x = blockIdx.x % 8, y = blockIdx.x / 8;
+  const int tt = y % ttiles;
+  const int jt = (y / ttiles) * 8 + x;
+  if (jt * kAppendRowsLat >= RV) return;
+  const int t = tt * kAppendRowsTok + (w & 1) * 32 + (lane & 31);
+  const int j = jt * kAppendRowsLat + (w >> 1) * 32 + (lane & 31);
+  const int kofs = (lane >> 5) * 8;
+  const f16* xrow = v + (size_t)min(t, n - 1) * K + kofs;
+  const f16* wrow = wv + (size_t)j * K + kofs;
+  const int ksteps = K / 16;
+  floatx16 acc = {};
+  for (int c = 0; c < ksteps; c += 8) {
+    half8 a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k0 = min(c + u, ksteps - 1) * 16;
+      a[u] = *reinterpret_cast<const half8*>(xrow + k0);
+      b[u] = *reinterpret_cast<const half8*>(wrow + k0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c + u < ksteps) acc = mfma32x32x16(a[u], b[u], acc);
+  }
+  // register r of lane l: token row mfma_row(r, l) of the wave's 32, latent j
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int ti = tt * kAppendRowsTok + (w & 1) * 32 + mfma_row(r, lane);
+    if (ti < n) {
+      int phys, slot;
+      where(ti, phys, slot);
+      vc[((size_t)phys * RV + j) * kBlock + slot] = (f16)acc[r];
+    }
+  }
+}
+
 // V side, VALU (fewer than 16 tokens): a workgroup of eight waves owns eight
 // joint latents and up to four tokens.  The tokens' v rows are staged in LDS
 // once; each wave fetches its whole w_v row with 16-byte loads before any
@@ -237,7 +287,11 @@ hipError_t append_enqueue(const AppendLaunch& a) {
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (a.n >= 16 && s.RV % 16 == 0 && K % (32 * kAppendVWaves) == 0) {
+  if (a.n >= 256 && s.RV % kAppendRowsLat == 0 && K % 16 == 0) {
+    const int ttiles = (a.n + kAppendRowsTok - 1) / kAppendRowsTok;
+    const int grid = ttiles * ((s.RV / kAppendRowsLat + 7) / 8) * 8;
+    hipLaunchKernelGGL(append_v_rows_kernel, dim3(grid), dim3(512), 0, a.stream, v, wv, a.n, K, s.RV, where, vc);
+  } else if (a.n >= 16 && s.RV % 16 == 0 && K % (32 * kAppendVWaves) == 0) {
     const int grid = ((s.RV / 16 + 7) / 8) * 8 * ((a.n + 15) / 16);
     hipLaunchKernelGGL(append_v_mfma_kernel, dim3(grid), dim3(kAppendVWaves * 64), 0, a.stream, v, wv, a.n, K,
                        s.RV, where, vc);

@@ -345,6 +345,77 @@ upproj_mfma_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
   }
 }
 
+// Many-row path (prefill): a workgroup computes a [64 rows x 128 dims] tile of
+// one head, so every Z row is read once and the head's B_v slice is shared by
+// all its row tiles, which run on one XCD.  Wave w owns output tile
+// (rows 32*(w&1), dims 32*(w>>1)); the B_v slice streams through LDS in chunks
+// of 128 latent rows, transposed so each lane's MFMA fragment (8 consecutive
+// k of one output dim) is one 16-byte LDS read.  Z enters as fp16 hi + lo.
+constexpr int kUpRowsTile = 64;
+constexpr int kUpRowsChunk = 128;
+constexpr int kUpRowsPad = 8;
+
+__global__ void __launch_bounds__(512)
+upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
+                   int rows, int H, int KV, int RV) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(16))) f16 bt[D][kUpRowsChunk + kUpRowsPad];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int rtiles = (rows + kUpRowsTile - 1) / kUpRowsTile;
+  const int x = blockIdx.x % 8, y = blockIdx.x / 8;
+  const int rtile = y % rtiles;
+  const int h = (y / rtiles) * 8 + x;
+  if (h >= H) return;                     // whole workgroup: no barrier skipped unevenly
+  const int kvh = h / (H / KV);
+  const size_t ld = (size_t)KV * D;
+  const int rt = w & 1, nt = w >> 1;
+  const int row = rtile * kUpRowsTile + rt * 32 + (lane & 31);
+  const bool live = row < rows;
+  const float* zrow = zf + ((size_t)(live ? row : 0) * H + h) * RV + (lane >> 5) * 8;
+  // staging: thread t loads B_v row (k0 + t/16 + 32 i), dims 8*(t%16) .. +7
+  const int sk = threadIdx.x >> 4, sn = (threadIdx.x & 15) * 8;
+  const f16* bsrc = bv + (size_t)kvh * D + sn;
+  floatx16 acc = {};
+  for (int k0 = 0; k0 < RV; k0 += kUpRowsChunk) {
+    half8 braw[kUpRowsChunk / 32];
+#pragma unroll
+    for (int i = 0; i < kUpRowsChunk / 32; ++i)
+      braw[i] = *reinterpret_cast<const half8*>(bsrc + (size_t)(k0 + sk + 32 * i) * ld);
+    floatx4 za[kUpRowsChunk / 16][2];
+#pragma unroll
+    for (int u = 0; u < kUpRowsChunk / 16; ++u) {
+      za[u][0] = *reinterpret_cast<const floatx4*>(zrow + k0 + u * 16);
+      za[u][1] = *reinterpret_cast<const floatx4*>(zrow + k0 + u * 16 + 4);
+    }
+    __syncthreads();                      // previous chunk's readers are done
+#pragma unroll
+    for (int i = 0; i < kUpRowsChunk / 32; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bt[sn + e][sk + 32 * i] = braw[i][e];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kUpRowsChunk / 16; ++u) {
+      const half8 bb = *reinterpret_cast<const half8*>(&bt[nt * 32 + (lane & 31)][u * 16 + (lane >> 5) * 8]);
+      half8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float z = live ? za[u][e >> 2][e & 3] : 0.f;
+        hi[e] = (f16)z;
+        lo[e] = (f16)(z - (float)hi[e]);
+      }
+      acc = mfma32x32x16(hi, bb, acc);
+      acc = mfma32x32x16(lo, bb, acc);
+    }
+  }
+  const int n = nt * 32 + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int ri = rtile * kUpRowsTile + rt * 32 + mfma_row(r, lane);
+    if (ri < rows) out[((size_t)ri * H + h) * D + n] = (f16)acc[r];
+  }
+}
+
 // VALU path (batch < 16): a workgroup owns 32 output dims of one head and up to
 // 16 rows.  Lane group (t & 3) owns 8 dims, t >> 2 picks the r_v rows
 // t/4 + 64 i: all of the workgroup's B_v slice is fetched with 16-byte loads
@@ -477,6 +548,13 @@ hipError_t launch_merge(const Shape& s, int rows, const float* pz, const float* 
 }
 
 hipError_t launch_upproj(const Shape& s, int rows, const float* zf, const void* b_v, void* out, hipStream_t st) {
+  if (rows >= 256 && s.D == 128 && s.RV % kUpRowsChunk == 0) {
+    const int rtiles = (rows + kUpRowsTile - 1) / kUpRowsTile;
+    const int grid = rtiles * ((s.H + 7) / 8) * 8;
+    hipLaunchKernelGGL(upproj_rows_kernel, dim3(grid), dim3(512), 0, st, zf, static_cast<const f16*>(b_v),
+                       static_cast<f16*>(out), rows, s.H, s.KV, s.RV);
+    return hipGetLastError();
+  }
   if (rows >= kSmallBatch && s.D % 32 == 0 && s.RV % (16 * kUpWaves) == 0 && s.RV <= kUpWaves * kUpMaxSpan) {
     const int groups = ((rows + 31) / 32) * s.H;
     const int grid = ((groups + 7) / 8) * 8 * (s.D / 32);

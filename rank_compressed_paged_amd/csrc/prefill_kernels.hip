@@ -180,7 +180,8 @@ __global__ void __launch_bounds__(kPfWaves * 64)
 prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f16* __restrict__ vpool,
                     const int32_t* __restrict__ block_tables, int mb_stride, const int32_t* __restrict__ qs,
                     const int32_t* __restrict__ lens, const int32_t* __restrict__ plan, int rows, int tile_cap,
-                    int H, int G, int HKV, float* __restrict__ part_z, float* __restrict__ part_ml, float tau) {
+                    int H, int G, int HKV, float* __restrict__ part_z, float* __restrict__ part_ml,
+                    float* __restrict__ zdirect, float tau) {
   using C = PfCfg<RK, RV>;
   // P, rescale factors and rescale flags of three blocks in flight: scores
   // run two blocks ahead of the z accumulation
@@ -190,6 +191,7 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
   __shared__ int slot_lds[kPfRows];
   // score A operands of the scorer waves (each lane reads back only its own)
   __shared__ half8 qa_lds[4][C::KS][2][64];
+  __shared__ float lrow_lds[kPfRows];      // row sums, for the single-range direct write
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -413,6 +415,33 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
     }
     if (ib < nblk) step(PfIC<0>{}, ib);
 
+    if (zdirect) {
+      // Every row's context fits one range: write z / l straight into the
+      // merged buffer (no partial state, no merge pass).
+      if (scorer) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float l_row = group_sum<16>(l_part[i]);
+          if ((lane & 15) == 0) lrow_lds[w * 16 + 4 * (lane >> 4) + i] = l_row;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = rt * 32 + mfma_row(r, lane);
+          if (rr < nrows) {
+            const float inv = 1.f / lrow_lds[rr];
+            float* zp = zdirect + ((size_t)(row0 + rr) * H + h) * RV + w * C::TPW * 32 + c32;
+#pragma unroll
+            for (int t = 0; t < C::TPW; ++t) zp[t * 32] = acc[rt][t][r] * inv;
+          }
+        }
+      __syncthreads();                       // LDS is reused by the next item
+      continue;
+    }
+
     // partial state of every row whose context reaches this range
     if (scorer) {
 #pragma unroll
@@ -495,7 +524,7 @@ PrefillLayout prefill_layout(const Shape& s, int batch, int rows, int max_contex
 
 template <int RK, int RV>
 static hipError_t launch_pf_attn(const PrefillLaunch& a, const float* qt, const int32_t* plan, float* pz,
-                                 float* pml, int device) {
+                                 float* pml, float* zdirect, int device) {
   const auto kernel = prefill_attn_kernel<RK, RV>;
   static std::atomic<int> resident[64];
   int res = (device >= 0 && device < 64) ? resident[device].load(std::memory_order_relaxed) : 0;
@@ -514,7 +543,7 @@ static hipError_t launch_pf_attn(const PrefillLaunch& a, const float* qt, const 
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPfWaves * 64), 0, a.stream, qt,
                      static_cast<const f16*>(a.k_cache), static_cast<const f16*>(a.v_cache), a.block_tables, s.MB,
                      a.query_start, a.context_lens, plan, a.rows, a.lay.tile_cap, s.H, s.H / s.KV, s.KV, pz, pml,
-                     kRescaleTau);
+                     zdirect, kRescaleTau);
   return hipGetLastError();
 }
 
@@ -535,16 +564,20 @@ hipError_t prefill_enqueue(const PrefillLaunch& a, int device) {
 
   if (a.ev_attn_start && hipEventRecord(a.ev_attn_start, a.stream) != hipSuccess) return hipErrorUnknown;
   err = hipErrorInvalidValue;
+  // one context range for every row: the attention kernel writes Z itself
+  float* zdirect = a.lay.max_ranges == 1 ? zf : nullptr;
 #define X(rk, rv) \
-  if (s.RK == rk && s.RV == rv) err = launch_pf_attn<rk, rv>(a, qt, plan, pz, pml, device);
+  if (s.RK == rk && s.RV == rv) err = launch_pf_attn<rk, rv>(a, qt, plan, pz, pml, zdirect, device);
   STARKV_PREFILL_SHAPES(X)
 #undef X
   if (err != hipSuccess) return err;
   if (a.ev_attn_stop && hipEventRecord(a.ev_attn_stop, a.stream) != hipSuccess) return hipErrorUnknown;
 
-  const PrefillPlan P{plan, a.rows, a.lay.tile_cap};
-  err = launch_merge(s, a.rows, pz, pml, plan, P.row_len_w(), zf, a.stream);
-  if (err != hipSuccess) return err;
+  if (!zdirect) {
+    const PrefillPlan P{plan, a.rows, a.lay.tile_cap};
+    err = launch_merge(s, a.rows, pz, pml, plan, P.row_len_w(), zf, a.stream);
+    if (err != hipSuccess) return err;
+  }
   return launch_upproj(s, a.rows, zf, a.b_v, a.out, a.stream);
 }
 

@@ -71,11 +71,12 @@ def test_append_golden_bits(golden_dir):
     assert not kb.any() and not vb.any()
 
 
-@pytest.mark.parametrize("n_per_seq", [2, 12])
+@pytest.mark.parametrize("n_per_seq", [2, 12, 120])
 @pytest.mark.parametrize("shape", ["main", "tiny"])
 def test_append_selection_projection_bit_exact(shape, n_per_seq):
     """w = [I | 0]: every latent is a copied input value, so the pool image is exact.
-    n = 8 takes the VALU kernels, n = 48 the MFMA kernels (main shape)."""
+    n = 8 takes the VALU kernels, n = 48 the MFMA kernels and n = 288 the
+    many-token V kernel (main shape)."""
     dev = gpu()
     if shape == "main":
         H, d, rk, rv = 32, 128, 64, 1024
@@ -97,7 +98,7 @@ def test_append_selection_projection_bit_exact(shape, n_per_seq):
     assert np.array_equal(vp.view(np.uint16), ev.view(np.uint16))
 
 
-@pytest.mark.parametrize("n_per_seq", [1, 16])
+@pytest.mark.parametrize("n_per_seq", [1, 16, 150])
 def test_append_general_projection_within_one_step(n_per_seq):
     dev = gpu()
     H, d, rk, rv = 32, 128, 64, 1024

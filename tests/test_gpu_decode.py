@@ -164,7 +164,7 @@ def test_ranges_spanning_many_sequences():
     stages up front, so later sequences take the in-loop q~ staging path."""
     dev = gpu()
     rng = np.random.default_rng(9)
-    lens = rng.integers(1, 40, size=200)
+    lens = rng.integers(1, 40, size=260)         # >= 256 rows: many-row up-projection too
     lens[::17] = 0
     case = small_main_case(107, lens)
     out = decode_gpu(to_dev(case, dev), lens, 1.0, dev)

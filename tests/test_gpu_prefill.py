@@ -48,13 +48,24 @@ def check(got, ref, what, rows=None):
 @pytest.mark.parametrize("scale", [1.0 / math.sqrt(128), 1.0])
 def test_prefill_main_shape(scale):
     """Ragged chunks: 2 tiles + tail, a whole 47-token prompt, a single row;
-    contexts up to 1000 tokens split into two ranges."""
+    contexts up to 1000 tokens split into two ranges; 258 rows take the
+    many-row up-projection."""
     dev = gpu()
-    lens, chunks = [300, 47, 1000, 129], [70, 47, 130, 1]
+    lens, chunks = [300, 47, 1000, 129], [70, 47, 140, 1]
     case = synth.make_prefill_case(701, 32, 128, 64, 1024, lens, chunks)
     log(f"prefill lens={lens} chunks={chunks} scale={scale:.3f}")
     out = prefill_gpu(to_dev(case, dev), case, scale, dev)
     check(out, oracle_prefill(case, scale), f"prefill main scale={scale:.3f}")
+
+
+def test_prefill_single_range_direct_write():
+    """Short contexts over many tiles: every row fits one context range, so the
+    attention kernel writes Z itself and the merge pass is skipped."""
+    dev = gpu()
+    lens, chunks = [400, 300, 256, 120], [400, 150, 256, 60]
+    case = synth.make_prefill_case(705, 32, 128, 64, 1024, lens, chunks)
+    out = prefill_gpu(to_dev(case, dev), case, 1.0, dev)
+    check(out, oracle_prefill(case, 1.0), "prefill single range")
 
 
 @pytest.mark.parametrize("rk,rv", [(64, 768), (64, 512), (64, 256), (32, 1024), (32, 768), (32, 512), (32, 256)])
