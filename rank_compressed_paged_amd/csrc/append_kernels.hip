@@ -160,8 +160,9 @@ append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
 // [64 tokens x 128 latents] tile, so each v row is read by 4 waves and each
 // w_v row by 2 instead of once per 16x16 tile.  Wave w owns tokens 32*(w&1)
 // and latents 32*(w>>1) of the tile: A = v rows, B = w_v rows (both contiguous
-// along the contraction), eight k-steps of loads in flight.  All token tiles of
-// one latent tile share its w_v rows and run on one XCD.
+// along the contraction), two batches of eight k-steps of loads alternating
+// (one in flight while the other multiplies).  All token tiles of one latent
+// tile share its w_v rows and run on one XCD.
 constexpr int kAppendRowsTok = 64;
 constexpr int kAppendRowsLat = 128;
 
@@ -182,18 +183,31 @@ append_v_rows_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
   const f16* wrow = wv + (size_t)j * K + kofs;
   const int ksteps = K / 16;
   floatx16 acc = {};
-  for (int c = 0; c < ksteps; c += 8) {
-    half8 a[8], b[8];
+  // two register batches of eight k-steps: one in flight while the other
+  // multiplies (loads past the end re-read the last k-step)
+  half8 a0[8], b0[8], a1[8], b1[8];
+  auto load = [&](half8 (&a)[8], half8 (&b)[8], int c) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int k0 = min(c + u, ksteps - 1) * 16;
       a[u] = *reinterpret_cast<const half8*>(xrow + k0);
       b[u] = *reinterpret_cast<const half8*>(wrow + k0);
     }
+  };
+  auto mul = [&](const half8 (&a)[8], const half8 (&b)[8], int c) {
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (c + u < ksteps) acc = mfma32x32x16(a[u], b[u], acc);
+  };
+  load(a0, b0, 0);
+  int c = 0;
+  for (; c + 8 < ksteps; c += 16) {
+    load(a1, b1, c + 8);
+    mul(a0, b0, c);
+    load(a0, b0, c + 16);
+    mul(a1, b1, c + 8);
   }
+  if (c < ksteps) mul(a0, b0, c);
   // register r of lane l: token row mfma_row(r, l) of the wave's 32, latent j
 #pragma unroll
   for (int r = 0; r < 16; ++r) {

@@ -11,6 +11,7 @@ typedef _Float16 f16;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 16;                    // tokens per paged block
 constexpr float kLog2e = 1.4426950408889634f;

@@ -348,18 +348,22 @@ upproj_mfma_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
 // Many-row path (prefill): a workgroup computes a [64 rows x 128 dims] tile of
 // one head, so every Z row is read once and the head's B_v slice is shared by
 // all its row tiles, which run on one XCD.  Wave w owns output tile
-// (rows 32*(w&1), dims 32*(w>>1)); the B_v slice streams through LDS in chunks
-// of 128 latent rows, transposed so each lane's MFMA fragment (8 consecutive
-// k of one output dim) is one 16-byte LDS read.  Z enters as fp16 hi + lo.
+// (rows 32*(w&1), dims 32*(w>>1)).  The B_v slice streams through LDS in
+// chunks of 64 latent rows, transposed so each lane's MFMA fragment (8
+// consecutive k of one output dim) is one 16-byte LDS read: a thread packs two
+// adjacent k of one dim into a dword, so a wave writes 32 consecutive dwords of
+// two LDS rows (no bank conflicts).  The next chunk's B_v and Z loads are in
+// flight while a chunk is transposed and multiplied.  Z enters as fp16 hi + lo.
 constexpr int kUpRowsTile = 64;
-constexpr int kUpRowsChunk = 128;
-constexpr int kUpRowsPad = 8;
+constexpr int kUpRowsChunk = 64;
+constexpr int kUpRowsPadDw = 4;          // LDS row = 32 + 4 dwords
 
 __global__ void __launch_bounds__(512)
 upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
                    int rows, int H, int KV, int RV) {
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(16))) f16 bt[D][kUpRowsChunk + kUpRowsPad];
+  constexpr int RowDw = kUpRowsChunk / 2 + kUpRowsPadDw;
+  __shared__ __attribute__((aligned(16))) uint32_t bt[D][RowDw];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int rtiles = (rows + kUpRowsTile - 1) / kUpRowsTile;
@@ -373,41 +377,62 @@ upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
   const int row = rtile * kUpRowsTile + rt * 32 + (lane & 31);
   const bool live = row < rows;
   const float* zrow = zf + ((size_t)(live ? row : 0) * H + h) * RV + (lane >> 5) * 8;
-  // staging: thread t loads B_v row (k0 + t/16 + 32 i), dims 8*(t%16) .. +7
-  const int sk = threadIdx.x >> 4, sn = (threadIdx.x & 15) * 8;
-  const f16* bsrc = bv + (size_t)kvh * D + sn;
-  floatx16 acc = {};
-  for (int k0 = 0; k0 < RV; k0 += kUpRowsChunk) {
-    half8 braw[kUpRowsChunk / 32];
-#pragma unroll
-    for (int i = 0; i < kUpRowsChunk / 32; ++i)
-      braw[i] = *reinterpret_cast<const half8*>(bsrc + (size_t)(k0 + sk + 32 * i) * ld);
-    floatx4 za[kUpRowsChunk / 16][2];
+  // staging: thread t takes latent rows 2*(t%32), 2*(t%32)+1 of the chunk and
+  // output dims 8*(t/32) .. +7
+  const int kp = threadIdx.x & 31, sn = (threadIdx.x >> 5) * 8;
+  const f16* bsrc = bv + (size_t)(2 * kp) * ld + (size_t)kvh * D + sn;
+  const int nchunks = RV / kUpRowsChunk;
+
+  half8 b0[2], b1[2];
+  floatx4 z0[kUpRowsChunk / 16][2], z1[kUpRowsChunk / 16][2];
+  auto load = [&](half8 (&b)[2], floatx4 (&z)[kUpRowsChunk / 16][2], int c) {
+    const int k0 = min(c, nchunks - 1) * kUpRowsChunk;   // past the end: re-read the last chunk
+    b[0] = *reinterpret_cast<const half8*>(bsrc + (size_t)k0 * ld);
+    b[1] = *reinterpret_cast<const half8*>(bsrc + (size_t)(k0 + 1) * ld);
 #pragma unroll
     for (int u = 0; u < kUpRowsChunk / 16; ++u) {
-      za[u][0] = *reinterpret_cast<const floatx4*>(zrow + k0 + u * 16);
-      za[u][1] = *reinterpret_cast<const floatx4*>(zrow + k0 + u * 16 + 4);
+      z[u][0] = *reinterpret_cast<const floatx4*>(zrow + k0 + u * 16);
+      z[u][1] = *reinterpret_cast<const floatx4*>(zrow + k0 + u * 16 + 4);
     }
+  };
+  floatx16 acc = {};
+  auto chunk = [&](half8 (&b)[2], floatx4 (&z)[kUpRowsChunk / 16][2]) {
     __syncthreads();                      // previous chunk's readers are done
+    // dims 2i, 2i+1 of a row sit in dword i (low, high half); the dword of
+    // dim e pairs k = 2kp (low half) with k = 2kp+1 (high half)
+    const u32x4 r0 = __builtin_bit_cast(u32x4, b[0]);
+    const u32x4 r1 = __builtin_bit_cast(u32x4, b[1]);
 #pragma unroll
-    for (int i = 0; i < kUpRowsChunk / 32; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bt[sn + e][sk + 32 * i] = braw[i][e];
+    for (int i = 0; i < 4; ++i) {
+      bt[sn + 2 * i][kp] = (r0[i] & 0xFFFFu) | (r1[i] << 16);
+      bt[sn + 2 * i + 1][kp] = (r0[i] >> 16) | (r1[i] & 0xFFFF0000u);
+    }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kUpRowsChunk / 16; ++u) {
-      const half8 bb = *reinterpret_cast<const half8*>(&bt[nt * 32 + (lane & 31)][u * 16 + (lane >> 5) * 8]);
+      // read back through the type it was written with (uint32), then reinterpret
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(&bt[nt * 32 + (lane & 31)][u * 8 + (lane >> 5) * 4]);
+      const half8 bb = __builtin_bit_cast(half8, raw);
       half8 hi, lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float z = live ? za[u][e >> 2][e & 3] : 0.f;
-        hi[e] = (f16)z;
-        lo[e] = (f16)(z - (float)hi[e]);
+        const float zv = live ? z[u][e >> 2][e & 3] : 0.f;
+        hi[e] = (f16)zv;
+        lo[e] = (f16)(zv - (float)hi[e]);
       }
       acc = mfma32x32x16(hi, bb, acc);
       acc = mfma32x32x16(lo, bb, acc);
     }
+  };
+  load(b0, z0, 0);
+  int c = 0;
+  for (; c + 1 < nchunks; c += 2) {
+    load(b1, z1, c + 1);
+    chunk(b0, z0);
+    load(b0, z0, c + 2);
+    chunk(b1, z1);
   }
+  if (c < nchunks) chunk(b0, z0);
   const int n = nt * 32 + (lane & 31);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
