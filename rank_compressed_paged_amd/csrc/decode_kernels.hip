@@ -348,22 +348,28 @@ upproj_mfma_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
 // Many-row path (prefill): a workgroup computes a [64 rows x 128 dims] tile of
 // one head, so every Z row is read once and the head's B_v slice is shared by
 // all its row tiles, which run on one XCD.  Wave w owns output tile
-// (rows 32*(w&1), dims 32*(w>>1)).  The B_v slice streams through LDS in
-// chunks of 64 latent rows, transposed so each lane's MFMA fragment (8
-// consecutive k of one output dim) is one 16-byte LDS read: a thread packs two
-// adjacent k of one dim into a dword, so a wave writes 32 consecutive dwords of
-// two LDS rows (no bank conflicts).  The next chunk's B_v and Z loads are in
-// flight while a chunk is transposed and multiplied.  Z enters as fp16 hi + lo.
+// (rows 32*(w&1), dims 32*(w>>1)).  The contraction runs in spans of 128
+// latent dims; per span both operands are staged in LDS with every load of a
+// thread issued before its first LDS write (one memory round trip per span):
+//   Z   [64 rows x 128] fp32, coalesced (a wave instruction reads 512 B of
+//       each of two rows); A fragments are split into fp16 hi + lo on the way
+//       to the MFMA;
+//   B_v [128 x 128 dims] transposed to [128 dims][128] so each lane's B
+//       fragment (8 consecutive k of one output dim) is one 16-byte LDS read.
+//       A thread packs two adjacent k of one dim into a dword, so a wave
+//       writes consecutive dwords of one LDS row (no bank conflicts).
 constexpr int kUpRowsTile = 64;
-constexpr int kUpRowsChunk = 64;
-constexpr int kUpRowsPadDw = 4;          // LDS row = 32 + 4 dwords
+constexpr int kUpRowsSpan = 128;         // latent dims staged at once (two workgroups fit a CU's LDS)
+constexpr int kUpRowsPad = 4;            // LDS row padding (floats / dwords)
 
 __global__ void __launch_bounds__(512)
 upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
                    int rows, int H, int KV, int RV) {
   constexpr int D = 128;
-  constexpr int RowDw = kUpRowsChunk / 2 + kUpRowsPadDw;
-  __shared__ __attribute__((aligned(16))) uint32_t bt[D][RowDw];
+  constexpr int BRow = kUpRowsSpan / 2 + kUpRowsPad;     // dwords
+  constexpr int ZRow = kUpRowsSpan + kUpRowsPad;         // floats
+  __shared__ __attribute__((aligned(16))) uint32_t bt[D][BRow];
+  __shared__ __attribute__((aligned(16))) float zl[kUpRowsTile][ZRow];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int rtiles = (rows + kUpRowsTile - 1) / kUpRowsTile;
@@ -374,69 +380,73 @@ upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
   const int kvh = h / (H / KV);
   const size_t ld = (size_t)KV * D;
   const int rt = w & 1, nt = w >> 1;
-  const int row = rtile * kUpRowsTile + rt * 32 + (lane & 31);
-  const bool live = row < rows;
-  const float* zrow = zf + ((size_t)(live ? row : 0) * H + h) * RV + (lane >> 5) * 8;
-  // staging: thread t takes latent rows 2*(t%32), 2*(t%32)+1 of the chunk and
-  // output dims 8*(t/32) .. +7
-  const int kp = threadIdx.x & 31, sn = (threadIdx.x >> 5) * 8;
+  const int row0 = rtile * kUpRowsTile;
+  // B_v staging: thread t takes latent rows 2*(t%P), 2*(t%P)+1 of the span
+  // (P = span/2 pairs) and output dims (span/8)*(t/P) .. +span/8-1
+  constexpr int kPairs = kUpRowsSpan / 2, kNPer = kUpRowsSpan / 8;
+  static_assert(512 / kPairs * kNPer == D && kNPer % 8 == 0, "B_v staging covers the tile");
+  const int kp = threadIdx.x % kPairs, sn = (threadIdx.x / kPairs) * kNPer;
   const f16* bsrc = bv + (size_t)(2 * kp) * ld + (size_t)kvh * D + sn;
-  const int nchunks = RV / kUpRowsChunk;
-
-  half8 b0[2], b1[2];
-  floatx4 z0[kUpRowsChunk / 16][2], z1[kUpRowsChunk / 16][2];
-  auto load = [&](half8 (&b)[2], floatx4 (&z)[kUpRowsChunk / 16][2], int c) {
-    const int k0 = min(c, nchunks - 1) * kUpRowsChunk;   // past the end: re-read the last chunk
-    b[0] = *reinterpret_cast<const half8*>(bsrc + (size_t)k0 * ld);
-    b[1] = *reinterpret_cast<const half8*>(bsrc + (size_t)(k0 + 1) * ld);
-#pragma unroll
-    for (int u = 0; u < kUpRowsChunk / 16; ++u) {
-      z[u][0] = *reinterpret_cast<const floatx4*>(zrow + k0 + u * 16);
-      z[u][1] = *reinterpret_cast<const floatx4*>(zrow + k0 + u * 16 + 4);
-    }
-  };
+  constexpr int kZPieces = kUpRowsTile * kUpRowsSpan / 4 / 512;   // 16-byte Z pieces per thread
   floatx16 acc = {};
-  auto chunk = [&](half8 (&b)[2], floatx4 (&z)[kUpRowsChunk / 16][2]) {
-    __syncthreads();                      // previous chunk's readers are done
-    // dims 2i, 2i+1 of a row sit in dword i (low, high half); the dword of
-    // dim e pairs k = 2kp (low half) with k = 2kp+1 (high half)
-    const u32x4 r0 = __builtin_bit_cast(u32x4, b[0]);
-    const u32x4 r1 = __builtin_bit_cast(u32x4, b[1]);
+  for (int k0 = 0; k0 < RV; k0 += kUpRowsSpan) {
+    half8 braw[2][kNPer / 8];
+    floatx4 zv[kZPieces];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bt[sn + 2 * i][kp] = (r0[i] & 0xFFFFu) | (r1[i] << 16);
-      bt[sn + 2 * i + 1][kp] = (r0[i] >> 16) | (r1[i] & 0xFFFF0000u);
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < kNPer / 8; ++i)
+        braw[j][i] = *reinterpret_cast<const half8*>(bsrc + (size_t)(k0 + j) * ld + 8 * i);
+#pragma unroll
+    for (int i = 0; i < kZPieces; ++i) {
+      const int f = i * 512 + threadIdx.x;
+      const int r = f / (kUpRowsSpan / 4), c4 = (f % (kUpRowsSpan / 4)) * 4;
+      zv[i] = row0 + r < rows ? *reinterpret_cast<const floatx4*>(zf + ((size_t)(row0 + r) * H + h) * RV + k0 + c4)
+                              : floatx4{};
+    }
+    __syncthreads();                      // previous span's readers are done
+#pragma unroll
+    for (int i = 0; i < kZPieces; ++i) {
+      const int f = i * 512 + threadIdx.x;
+      const int r = f / (kUpRowsSpan / 4), c4 = (f % (kUpRowsSpan / 4)) * 4;
+      *reinterpret_cast<floatx4*>(&zl[r][c4]) = zv[i];
+    }
+    // dims 2e, 2e+1 of a loaded row sit in dword e of its half8 (low, high
+    // half); the LDS dword of dim n pairs k = 2kp (low) with k = 2kp+1 (high)
+#pragma unroll
+    for (int i = 0; i < kNPer / 8; ++i) {
+      const u32x4 r0 = __builtin_bit_cast(u32x4, braw[0][i]);
+      const u32x4 r1 = __builtin_bit_cast(u32x4, braw[1][i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bt[sn + 8 * i + 2 * e][kp] = (r0[e] & 0xFFFFu) | (r1[e] << 16);
+        bt[sn + 8 * i + 2 * e + 1][kp] = (r0[e] >> 16) | (r1[e] & 0xFFFF0000u);
+      }
     }
     __syncthreads();
+    const float* za = &zl[rt * 32 + (lane & 31)][(lane >> 5) * 8];
+    const uint32_t* brow = &bt[nt * 32 + (lane & 31)][(lane >> 5) * 4];
 #pragma unroll
-    for (int u = 0; u < kUpRowsChunk / 16; ++u) {
+    for (int u = 0; u < kUpRowsSpan / 16; ++u) {
       // read back through the type it was written with (uint32), then reinterpret
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(&bt[nt * 32 + (lane & 31)][u * 8 + (lane >> 5) * 4]);
-      const half8 bb = __builtin_bit_cast(half8, raw);
+      const half8 bb = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(brow + u * 8));
+      const floatx4 z0 = *reinterpret_cast<const floatx4*>(za + u * 16);
+      const floatx4 z1 = *reinterpret_cast<const floatx4*>(za + u * 16 + 4);
       half8 hi, lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float zv = live ? z[u][e >> 2][e & 3] : 0.f;
-        hi[e] = (f16)zv;
-        lo[e] = (f16)(zv - (float)hi[e]);
+        const float zz = e < 4 ? z0[e] : z1[e - 4];
+        hi[e] = (f16)zz;
+        lo[e] = (f16)(zz - (float)hi[e]);
       }
       acc = mfma32x32x16(hi, bb, acc);
       acc = mfma32x32x16(lo, bb, acc);
     }
-  };
-  load(b0, z0, 0);
-  int c = 0;
-  for (; c + 1 < nchunks; c += 2) {
-    load(b1, z1, c + 1);
-    chunk(b0, z0);
-    load(b0, z0, c + 2);
-    chunk(b1, z1);
   }
-  if (c < nchunks) chunk(b0, z0);
   const int n = nt * 32 + (lane & 31);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int ri = rtile * kUpRowsTile + rt * 32 + mfma_row(r, lane);
+    const int ri = row0 + rt * 32 + mfma_row(r, lane);
     if (ri < rows) out[((size_t)ri * H + h) * D + n] = (f16)acc[r];
   }
 }
@@ -573,7 +583,7 @@ hipError_t launch_merge(const Shape& s, int rows, const float* pz, const float* 
 }
 
 hipError_t launch_upproj(const Shape& s, int rows, const float* zf, const void* b_v, void* out, hipStream_t st) {
-  if (rows >= 256 && s.D == 128 && s.RV % kUpRowsChunk == 0) {
+  if (rows >= 256 && s.D == 128 && s.RV % kUpRowsSpan == 0) {
     const int rtiles = (rows + kUpRowsTile - 1) / kUpRowsTile;
     const int grid = rtiles * ((s.H + 7) / 8) * 8;
     hipLaunchKernelGGL(upproj_rows_kernel, dim3(grid), dim3(512), 0, st, zf, static_cast<const f16*>(b_v),
