@@ -9,6 +9,8 @@
 // slot pos_i % 16 (fixed-size blocks via a block table, botdigit
 // PagedAttention page, block-level management item).
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -157,61 +159,104 @@ append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
 }
 
 // V side, many tokens (prefill chunks): a workgroup of eight waves computes a
-// [64 tokens x 128 latents] tile, so each v row is read by 4 waves and each
-// w_v row by 2 instead of once per 16x16 tile.  Wave w owns tokens 32*(w&1)
-// and latents 32*(w>>1) of the tile: A = v rows, B = w_v rows (both contiguous
-// along the contraction), two batches of eight k-steps of loads alternating
-// (one in flight while the other multiplies).  All token tiles of one latent
-// tile share its w_v rows and run on one XCD.
+// [64 tokens x 128 latents] tile, c = v . w_v^T over K = H_kv*d.  The
+// contraction runs in spans of 128: the span's v rows [64 x 128] and w_v rows
+// [128 x 128] are staged in LDS (both are contiguous along k, so a wave
+// instruction reads 1 KiB = 4 rows x 256 B and the MFMA fragments are plain
+// 16-byte LDS reads).  Loads run four spans ahead in registers and LDS is
+// double-buffered: one barrier per span.  Wave w owns tokens 32*(w&1) and
+// latents 32*(w>>1) of the tile.  All token tiles of one latent tile share its
+// w_v rows and run on one XCD.
 constexpr int kAppendRowsTok = 64;
 constexpr int kAppendRowsLat = 128;
+constexpr int kAppendRowsSpan = 128;
+constexpr int kAppendRowsAhead = 4;
+constexpr int kAppendRowsPad = 8;        // halves of LDS row padding
 
 __global__ void __launch_bounds__(512)
 append_v_rows_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
                      SlotOf where, f16* __restrict__ vc) {
+  constexpr int Row = kAppendRowsSpan + kAppendRowsPad;
+  constexpr int kA = kAppendRowsTok * kAppendRowsSpan / 8 / 512;   // 16-byte v pieces per thread per span
+  constexpr int kB = kAppendRowsLat * kAppendRowsSpan / 8 / 512;   // 16-byte w_v pieces per thread per span
+  constexpr int kPer = kAppendRowsSpan / 8;                         // 16-byte pieces per row per span
+  __shared__ __attribute__((aligned(16))) f16 as[2][kAppendRowsTok][Row];
+  __shared__ __attribute__((aligned(16))) f16 bs[2][kAppendRowsLat][Row];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int ttiles = (n + kAppendRowsTok - 1) / kAppendRowsTok;
   const int x = blockIdx.x % 8, y = blockIdx.x / 8;
   const int tt = y % ttiles;
   const int jt = (y / ttiles) * 8 + x;
-  if (jt * kAppendRowsLat >= RV) return;
-  const int t = tt * kAppendRowsTok + (w & 1) * 32 + (lane & 31);
-  const int j = jt * kAppendRowsLat + (w >> 1) * 32 + (lane & 31);
-  const int kofs = (lane >> 5) * 8;
-  const f16* xrow = v + (size_t)min(t, n - 1) * K + kofs;
-  const f16* wrow = wv + (size_t)j * K + kofs;
-  const int ksteps = K / 16;
-  floatx16 acc = {};
-  // two register batches of eight k-steps: one in flight while the other
-  // multiplies (loads past the end re-read the last k-step)
-  half8 a0[8], b0[8], a1[8], b1[8];
-  auto load = [&](half8 (&a)[8], half8 (&b)[8], int c) {
+  if (jt * kAppendRowsLat >= RV) return;   // whole workgroup: no barrier skipped unevenly
+  const int t0 = tt * kAppendRowsTok, j0 = jt * kAppendRowsLat;
+  const int nspans = K / kAppendRowsSpan;
+  half8 ra[kAppendRowsAhead][kA], rb[kAppendRowsAhead][kB];
+  // piece p = i*512 + thread -> row p / kPer, k offset 8*(p % kPer); token
+  // rows past n re-read row n-1 (their results are never stored); spans past
+  // the end re-read the last span
+  auto load = [&](half8 (&a)[kA], half8 (&b)[kB], int sp) {
+    const int k0 = min(sp, nspans - 1) * kAppendRowsSpan;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k0 = min(c + u, ksteps - 1) * 16;
-      a[u] = *reinterpret_cast<const half8*>(xrow + k0);
-      b[u] = *reinterpret_cast<const half8*>(wrow + k0);
+    for (int i = 0; i < kA; ++i) {
+      const int p = i * 512 + threadIdx.x;
+      a[i] = *reinterpret_cast<const half8*>(v + (size_t)min(t0 + p / kPer, n - 1) * K + k0 + 8 * (p % kPer));
+    }
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const int p = i * 512 + threadIdx.x;
+      b[i] = *reinterpret_cast<const half8*>(wv + (size_t)(j0 + p / kPer) * K + k0 + 8 * (p % kPer));
     }
   };
-  auto mul = [&](const half8 (&a)[8], const half8 (&b)[8], int c) {
+  auto store = [&](const half8 (&a)[kA], const half8 (&b)[kB], int buf) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (c + u < ksteps) acc = mfma32x32x16(a[u], b[u], acc);
+    for (int i = 0; i < kA; ++i) {
+      const int p = i * 512 + threadIdx.x;
+      *reinterpret_cast<half8*>(&as[buf][p / kPer][8 * (p % kPer)]) = a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const int p = i * 512 + threadIdx.x;
+      *reinterpret_cast<half8*>(&bs[buf][p / kPer][8 * (p % kPer)]) = b[i];
+    }
   };
-  load(a0, b0, 0);
-  int c = 0;
-  for (; c + 8 < ksteps; c += 16) {
-    load(a1, b1, c + 8);
-    mul(a0, b0, c);
-    load(a0, b0, c + 16);
-    mul(a1, b1, c + 8);
+  floatx16 acc = {};
+  const f16* arow = &as[0][(w & 1) * 32 + (lane & 31)][(lane >> 5) * 8];
+  const f16* brow = &bs[0][(w >> 1) * 32 + (lane & 31)][(lane >> 5) * 8];
+  auto mul = [&](int buf) {
+    const f16* ap = arow + (size_t)buf * kAppendRowsTok * Row;
+    const f16* bp = brow + (size_t)buf * kAppendRowsLat * Row;
+#pragma unroll
+    for (int u = 0; u < kAppendRowsSpan / 16; ++u)
+      acc = mfma32x32x16(*reinterpret_cast<const half8*>(ap + u * 16), *reinterpret_cast<const half8*>(bp + u * 16),
+                         acc);
+  };
+#pragma unroll
+  for (int q = 0; q < kAppendRowsAhead; ++q) load(ra[q], rb[q], q);
+  // span sp: its loads sit in register set sp % 4, its LDS buffer is sp % 2
+  auto span = [&](auto qc, int sp) {
+    constexpr int Q = decltype(qc)::value;
+    store(ra[Q], rb[Q], Q & 1);
+    __syncthreads();                       // buffer Q&1 complete; buffer (Q&1)^1 free again after the next barrier
+    load(ra[Q], rb[Q], sp + kAppendRowsAhead);
+    mul(Q & 1);
+  };
+  static_assert(kAppendRowsAhead == 4, "unrolled by four below");
+  int sp = 0;
+  for (; sp + 3 < nspans; sp += 4) {
+    span(std::integral_constant<int, 0>{}, sp);
+    span(std::integral_constant<int, 1>{}, sp + 1);
+    span(std::integral_constant<int, 2>{}, sp + 2);
+    span(std::integral_constant<int, 3>{}, sp + 3);
   }
-  if (c < ksteps) mul(a0, b0, c);
+  if (sp < nspans) span(std::integral_constant<int, 0>{}, sp);
+  if (sp + 1 < nspans) span(std::integral_constant<int, 1>{}, sp + 1);
+  if (sp + 2 < nspans) span(std::integral_constant<int, 2>{}, sp + 2);
   // register r of lane l: token row mfma_row(r, l) of the wave's 32, latent j
+  const int j = j0 + (w >> 1) * 32 + (lane & 31);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int ti = tt * kAppendRowsTok + (w & 1) * 32 + mfma_row(r, lane);
+    const int ti = t0 + (w & 1) * 32 + mfma_row(r, lane);
     if (ti < n) {
       int phys, slot;
       where(ti, phys, slot);
@@ -301,7 +346,7 @@ hipError_t append_enqueue(const AppendLaunch& a) {
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (a.n >= 256 && s.RV % kAppendRowsLat == 0 && K % 16 == 0) {
+  if (a.n >= 256 && s.RV % kAppendRowsLat == 0 && K % kAppendRowsSpan == 0) {
     const int ttiles = (a.n + kAppendRowsTok - 1) / kAppendRowsTok;
     const int grid = ttiles * ((s.RV / kAppendRowsLat + 7) / 8) * 8;
     hipLaunchKernelGGL(append_v_rows_kernel, dim3(grid), dim3(512), 0, a.stream, v, wv, a.n, K, s.RV, where, vc);
