@@ -99,7 +99,7 @@ append_k_valu_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int 
 // V side, MFMA: a workgroup computes a [16 tokens x 16 latents] tile with the
 // 16x16x32 f16 MFMA, so one wave load instruction reads 16 rows x 64 bytes
 // (four lanes per row) of w_v and v instead of 32 rows x 32 bytes; the
-// 32x32 tiles spent the launch on address lookups.  Four waves split the H*d
+// 32x32 tiles spent the launch on address lookups.  Four waves split the H_kv*d
 // contraction (eight k-steps of loads in flight before the first MFMA) and
 // reduce through LDS.
 constexpr int kAppendVWaves = 4;
