@@ -13,7 +13,10 @@ Prints one JSON line.  Options:
   --gpus N                 only 1 is supported (one GPU per box)
   --no-cpu-baseline        skip the oracle timing
   --no-ceiling             skip the HBM read-ceiling probe
+  --no-graph               skip the HIP-graph timing of the same step (reported
+                           beside `value` under "graph", never as `value`)
   --config N               time decode workload N (1-7) instead; own JSON line
+  --graph                  with --config: also time HIP-graph replays of the step
   --prefill N              time prefill workload N (1-3) instead; own JSON line
   --calib-copy             run only a plain device copy of known size (for
                            scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
@@ -135,7 +138,49 @@ def cpu_baseline(case, cfg, k_new, v_new, scale, budget_s=12.0):
                       f"{int(lens[0]) + 1} tokens), fp64 numpy, {dt:.1f} s wall"}
 
 
-def config_report(cfg_id: int, steps: int, warmup: int):
+def graph_replay_ms(step, steps: int, out, flush=None) -> float:
+    """Capture one step (every launch of the path) in a HIP graph through
+    torch's CUDAGraph, check that replays reproduce the eager step's output bit
+    for bit (with eager work between the replays), then time `steps` replays
+    (back to back, or one by one around a cache flush).  Returns milliseconds
+    per replay."""
+    import torch
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        out.zero_()                    # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out.view(torch.int16), ref.view(torch.int16)):
+            raise RuntimeError("graph replay differs from the eager step")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    if flush is None:                  # back to back, like the eager timing
+        e0.record()
+        for _ in range(steps):
+            graph.replay()
+        e1.record()
+        e1.synchronize()
+        total = e0.elapsed_time(e1)
+    else:                              # cache written between replays, outside the events
+        total = 0.0
+        for i in range(steps):
+            flush.fill_(i & 0xFF)
+            e0.record()
+            graph.replay()
+            e1.record()
+            e1.synchronize()
+            total += e0.elapsed_time(e1)
+    del graph
+    return total / steps
+
+
+def config_report(cfg_id: int, steps: int, warmup: int, graph: bool = False):
     """Timing of one of the five parity workloads (a separate JSON line).
 
     A step appends one token per sequence, then decodes; for the 32-layer stack
@@ -143,7 +188,8 @@ def config_report(cfg_id: int, steps: int, warmup: int):
     Uniform workloads overwrite the token at position L each step; the ragged
     one grows every sequence by one token per step.  Workloads that fit the
     256 MB last-level cache get a 1 GiB write between steps, outside the timed
-    events.
+    events.  With `graph`, the same step is also captured in a HIP graph and
+    its replays are timed (uniform workloads only).
     """
     import torch
 
@@ -222,6 +268,12 @@ def config_report(cfg_id: int, steps: int, warmup: int):
         "step_latent_gbps": latent / (total_ms / 1e3) / 1e9,
         "cache_flush_between_steps": flush is not None,
     }
+    if graph:
+        if grow:
+            line["graph"] = "not timed: positions change every step"
+        else:
+            ms = graph_replay_ms(lambda: step(warmup), steps, out, flush)
+            line["graph"] = {"ms_per_step": ms, "decode_tokens_per_s": cfg.batch / (ms / 1e3)}
     print(json.dumps(line), flush=True)
 
 
@@ -305,6 +357,9 @@ def main():
                     help="time workload 1-7 instead (prints its own JSON line)")
     ap.add_argument("--prefill", type=int, default=0,
                     help="time prefill workload 1-3 instead (prints its own JSON line)")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --config: also time the step captured in a HIP graph")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph timing of the headline step")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr, flush=True)
@@ -313,7 +368,7 @@ def main():
         calib_copy()
         return
     if args.config:
-        config_report(args.config, args.steps, args.warmup)
+        config_report(args.config, args.steps, args.warmup, args.graph)
         return
     if args.prefill:
         prefill_report(args.prefill, args.steps, args.warmup)
@@ -398,6 +453,10 @@ def main():
         "latent_bytes_per_step": latent_bytes,
         "step_latent_gbps": latent_bytes / (dt / args.steps) / 1e9,
     }
+    if not args.no_graph:
+        ms = graph_replay_ms(step, args.steps, out)
+        line["graph"] = {"ms_per_step": ms, "tokens_per_s": cfg.batch / (ms / 1e3),
+                         "note": "same step captured in one HIP graph; replays timed back to back"}
     if not args.no_ceiling:
         ceiling = read_ceiling(dev)
         line["hbm_read_ceiling"] = ceiling

@@ -84,13 +84,7 @@ append_k_valu_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int 
   const int t = idx / (RK * H);
   const f16* x = k + ((size_t)t * H + h) * D;
   const f16* wrow = wk + ((size_t)h * RK + r) * D;
-  float acc = 0.f;
-  for (int i = 0; i < D; i += 8) {
-    const half8 a = *reinterpret_cast<const half8*>(x + i);
-    const half8 b = *reinterpret_cast<const half8*>(wrow + i);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
-  }
+  const float acc = dot_f16(x, wrow, D);
   int phys, slot;
   where(t, phys, slot);
   kc[(((size_t)phys * H + h) * kBlock + slot) * RK + r] = (f16)acc;
@@ -99,10 +93,13 @@ append_k_valu_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int 
 // V side, MFMA: a workgroup computes a [16 tokens x 16 latents] tile with the
 // 16x16x32 f16 MFMA, so one wave load instruction reads 16 rows x 64 bytes
 // (four lanes per row) of w_v and v instead of 32 rows x 32 bytes; the
-// 32x32 tiles spent the launch on address lookups.  Four waves split the H_kv*d
-// contraction (eight k-steps of loads in flight before the first MFMA) and
-// reduce through LDS.
-constexpr int kAppendVWaves = 4;
+// 32x32 tiles spent the launch on address lookups.  Eight waves split the
+// H_kv*d contraction and reduce through LDS; each wave issues the loads of up
+// to sixteen k-steps (its whole share at H_kv*d = 4096) before its first
+// MFMA, so the launch costs about one memory round trip instead of one per
+// batch of k-steps.
+constexpr int kAppendVWaves = 8;
+constexpr int kAppendVBatch = 16;
 
 __global__ void __launch_bounds__(kAppendVWaves * 64)
 append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
@@ -117,7 +114,7 @@ append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
   const int x = blockIdx.x % 8, y = blockIdx.x / 8;
   const int jt = (y / ttiles) * 8 + x;
   const int tt = y % ttiles;
-  if (jt >= jtiles) return;
+  if (jt >= jtiles) return;                 // uniform over the workgroup, before any barrier
   const int t = tt * 16 + (lane & 15);
   const bool trow = t < n;
   const int j = jt * 16 + (lane & 15);
@@ -127,17 +124,19 @@ append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
   const f16* xrow = v + (size_t)(trow ? t : n - 1) * K + kofs;
   const f16* wrow = wv + (size_t)j * K + kofs;
   floatx4 acc = {};
-  for (int c = 0; c < ksteps; c += 8) {
-    half8 a[8], b[8];
+  for (int c = 0; c < ksteps; c += kAppendVBatch) {
+    half8 a[kAppendVBatch], b[kAppendVBatch];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kAppendVBatch; ++u) {
       const int k0 = kbase + min(c + u, ksteps - 1) * 32;
       a[u] = *reinterpret_cast<const half8*>(xrow + k0);
       b[u] = *reinterpret_cast<const half8*>(wrow + k0);
     }
+    __builtin_amdgcn_sched_barrier(0);      // every load of the batch is in flight before the first MFMA
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (c + u < ksteps) acc = mfma16x16x32(trow ? a[u] : half8{}, b[u], acc);
+    for (int u = 0; u < kAppendVBatch; ++u) {
+      const bool live = trow && c + u < ksteps;   // clamped re-reads contribute nothing
+      acc = mfma16x16x32(live ? a[u] : half8{}, b[u], acc);
     }
   }
   // result layout: lane l, register r holds D[4(l/16) + r][l % 16]
@@ -289,10 +288,21 @@ append_v_valu_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
       const int k = i * 512 + lane * 8;
       wr[i] = (j < RV && k < kn) ? *reinterpret_cast<const half8*>(wv + (size_t)j * K + kc + k) : half8{};
     }
-    __syncthreads();                                // previous pass's readers are done
-    for (int idx = threadIdx.x; idx < cnt * (kn / 8); idx += 512) {
+    // token rows -> LDS: every load of a thread is issued before its first write
+    constexpr int kPer = kAppendGroup * kAppendChunk / 8 / 512;
+    half8 vv[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = threadIdx.x + 512 * i;
       const int r = idx / (kn / 8), c = idx % (kn / 8);
-      *reinterpret_cast<half8*>(&vl[r][c * 8]) = *reinterpret_cast<const half8*>(v + (size_t)(t0 + r) * K + kc + c * 8);
+      vv[i] = idx < cnt * (kn / 8) ? *reinterpret_cast<const half8*>(v + (size_t)(t0 + r) * K + kc + c * 8) : half8{};
+    }
+    __builtin_amdgcn_sched_barrier(0);              // keep the loads ahead of the LDS writes
+    __syncthreads();                                // previous pass's readers are done
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = threadIdx.x + 512 * i;
+      if (idx < cnt * (kn / 8)) *reinterpret_cast<half8*>(&vl[idx / (kn / 8)][(idx % (kn / 8)) * 8]) = vv[i];
     }
     __syncthreads();
 #pragma unroll

@@ -54,6 +54,32 @@ __device__ __forceinline__ float shfl_xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// Dot product of two fp16 rows of n elements (n % 8 == 0, n <= 256) with fp32
+// accumulation.  All 16-byte loads of a 128-element batch are issued before
+// the first multiply (one memory round trip per batch instead of one per
+// load); loads past n are clamped to the last chunk and masked to zero.
+__device__ __forceinline__ float dot_f16(const _Float16* __restrict__ a, const _Float16* __restrict__ b, int n) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  float acc = 0.f;
+  for (int i0 = 0; i0 < n; i0 += 128) {
+    h8 x[16], y[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int i = min(i0 + 8 * j, n - 8);
+      x[j] = *reinterpret_cast<const h8*>(a + i);
+      y[j] = *reinterpret_cast<const h8*>(b + i);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the arithmetic
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float live = i0 + 8 * j < n ? 1.f : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += live * ((float)x[j][e] * (float)y[j][e]);
+    }
+  }
+  return acc;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);            // v_exp_f32; exp2(-inf) = 0
 }

@@ -150,20 +150,50 @@ qproj_plan_valu_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, fl
   const int b = idx / (RK * H);
   const f16* qp = q + ((size_t)b * H + head) * D;
   const f16* bp = bk + ((size_t)(head / (H / KV)) * RK + r) * D;
-  float acc = 0.f;
-  for (int i = 0; i < D; i += 8) {
-    half8 x = *reinterpret_cast<const half8*>(qp + i);
-    half8 y = *reinterpret_cast<const half8*>(bp + i);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)x[e] * (float)y[e];
-  }
-  qt[idx] = acc * scale2;
+  qt[idx] = dot_f16(qp, bp, D) * scale2;
 }
 
 
 // ---------------------------------------------------------------------------
 // 3. merge of a sequence's partials
 // ---------------------------------------------------------------------------
+
+// Online log-sum-exp over the slots c0, c0 + W, ... < s1, U per memory round
+// trip.  Every load of a batch is unconditional (indices past the end re-read
+// the last slot and get weight 0), so all of them are in flight before the
+// first use instead of one (m, l) round trip per slot.
+template <int U, int W>
+__device__ __forceinline__ void merge_slots(const float* __restrict__ ml, const float* __restrict__ zb, size_t zs,
+                                            int H, int c0, int s1, floatx4& a, float& M, float& den) {
+  for (int c = c0; c < s1; c += U * W) {
+    float m[U], l[U];
+    floatx4 z[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sl = min(c + u * W, s1 - 1);
+      m[u] = ml[(size_t)sl * H * 2];
+      l[u] = ml[(size_t)sl * H * 2 + 1];
+      z[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float cm = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      m[u] = c + u * W < s1 ? m[u] : -INFINITY;     // re-read slots weigh nothing
+      cm = fmaxf(cm, m[u]);
+    }
+    const float sc = fast_exp2(M - cm);             // 0 while M is still -inf
+    a *= sc;
+    den *= sc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wgt = fast_exp2(m[u] - cm);
+      a += wgt * z[u];
+      den += wgt * l[u];
+    }
+    M = cm;
+  }
+}
 
 // One 256-thread workgroup merges 1024/W latent dims of one (sequence, head):
 // W slot groups (W = 1 or 4) each take every W-th slot, up to sixteen slots per
@@ -194,41 +224,19 @@ merge_kernel(const float* __restrict__ part_z, const float* __restrict__ part_ml
     if (w == 0 && live) *reinterpret_cast<floatx4*>(zrow + d) = floatx4{};
     return;
   }
-  constexpr int U = 16;
   const float* ml = part_ml + (size_t)h * 2;
   const float* zb = part_z + (size_t)h * RV + (live ? d : 0);
   const size_t zs = (size_t)H * RV;                 // slot stride
   floatx4 a = {};
   float M = -INFINITY, den = 0.f;
-  for (int c = s0 + w; c < s1; c += U * W) {
-    float m[U], l[U];
-    floatx4 z[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int sl = c + u * W;
-      if (sl < s1) {
-        m[u] = ml[(size_t)sl * H * 2];
-        l[u] = ml[(size_t)sl * H * 2 + 1];
-        z[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs);
-      }
-    }
-    float cm = M;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (c + u * W < s1) cm = fmaxf(cm, m[u]);
-    const float sc = fast_exp2(M - cm);             // 0 while M is still -inf
-    a *= sc;
-    den *= sc;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (c + u * W < s1) {
-        const float wgt = fast_exp2(m[u] - cm);
-        a += wgt * z[u];
-        den += wgt * l[u];
-      }
-    }
-    M = cm;
-  }
+  // batch size by slot count (uniform over the workgroup): few re-reads
+  const int n = s1 - s0;
+  if (n <= 4 * W)
+    merge_slots<4, W>(ml, zb, zs, H, s0 + w, s1, a, M, den);
+  else if (n <= 8 * W)
+    merge_slots<8, W>(ml, zb, zs, H, s0 + w, s1, a, M, den);
+  else
+    merge_slots<16, W>(ml, zb, zs, H, s0 + w, s1, a, M, den);
   if constexpr (W == 1) {
     if (live) *reinterpret_cast<floatx4*>(zrow + d) = a * (1.f / den);
   } else {
@@ -271,10 +279,13 @@ constexpr int kUpWaves = 8;
 constexpr int kUpMaxSpan = 128;          // r_v / kUpWaves <= 128 (r_v <= 1024)
 constexpr int kUpPad = 8;
 
+template <int NS>                        // NS = r_v / (16 * kUpWaves) k-steps per wave
 __global__ void __launch_bounds__(kUpWaves * 64)
 upproj_mfma_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
-                   int batch, int H, int KV, int D, int RV) {
-  __shared__ __attribute__((aligned(16))) f16 bt[kUpWaves][32][kUpMaxSpan + kUpPad];
+                   int batch, int H, int KV, int D) {
+  constexpr int RV = NS * 16 * kUpWaves;
+  constexpr int kspan = NS * 16;
+  __shared__ __attribute__((aligned(16))) f16 bt[kUpWaves][32][kspan + kUpPad];
   __shared__ float red[kUpWaves][16][64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -294,42 +305,37 @@ upproj_mfma_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
   const int kofs = (lane >> 5) * 8;
   const size_t ld = (size_t)KV * D;
   const int kvh = h / (H / KV);          // value columns of the group's key/value head
-  const int kspan = RV / kUpWaves;       // multiple of 16
   const int kbase = w * kspan;
   // B_v slice rows kbase.., 32 dims from h*D + nt*32: lane -> (row l/4, 8 dims)
   const f16* bsrc = bv + (size_t)(kbase + (lane >> 2)) * ld + (size_t)kvh * D + nt * 32 + (lane & 3) * 8;
   const float* zrow = zf + ((size_t)(brow ? b : batch - 1) * H + h) * RV + kbase + kofs;
-  half8 braw[kUpMaxSpan / 16];
-  floatx4 za[kUpMaxSpan / 16][2];
+  half8 braw[NS];
+  floatx4 za[NS][2];
 #pragma unroll
-  for (int u = 0; u < kUpMaxSpan / 16; ++u) {
-    if (u * 16 < kspan) {
-      braw[u] = *reinterpret_cast<const half8*>(bsrc + (size_t)u * 16 * ld);
-      za[u][0] = *reinterpret_cast<const floatx4*>(zrow + u * 16);
-      za[u][1] = *reinterpret_cast<const floatx4*>(zrow + u * 16 + 4);
-    }
+  for (int u = 0; u < NS; ++u) {
+    braw[u] = *reinterpret_cast<const half8*>(bsrc + (size_t)u * 16 * ld);
+    za[u][0] = *reinterpret_cast<const floatx4*>(zrow + u * 16);
+    za[u][1] = *reinterpret_cast<const floatx4*>(zrow + u * 16 + 4);
   }
-  f16 (*tw)[kUpMaxSpan + kUpPad] = bt[w];
+  __builtin_amdgcn_sched_barrier(0);     // every load in flight before the first LDS write
+  f16 (*tw)[kspan + kUpPad] = bt[w];
 #pragma unroll
-  for (int u = 0; u < kUpMaxSpan / 16; ++u)
-    if (u * 16 < kspan)
+  for (int u = 0; u < NS; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tw[(lane & 3) * 8 + e][u * 16 + (lane >> 2)] = braw[u][e];
+    for (int e = 0; e < 8; ++e) tw[(lane & 3) * 8 + e][u * 16 + (lane >> 2)] = braw[u][e];
   floatx16 acc = {};
 #pragma unroll
-  for (int u = 0; u < kUpMaxSpan / 16; ++u) {
-    if (u * 16 < kspan) {
-      const half8 bb = *reinterpret_cast<const half8*>(&tw[lane & 31][u * 16 + kofs]);
-      half8 hi, lo;
+  for (int u = 0; u < NS; ++u) {
+    const half8 bb = *reinterpret_cast<const half8*>(&tw[lane & 31][u * 16 + kofs]);
+    half8 hi, lo;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float z = brow ? za[u][e >> 2][e & 3] : 0.f;
-        hi[e] = (f16)z;
-        lo[e] = (f16)(z - (float)hi[e]);
-      }
-      acc = mfma32x32x16(hi, bb, acc);
-      acc = mfma32x32x16(lo, bb, acc);
+    for (int e = 0; e < 8; ++e) {
+      const float z = brow ? za[u][e >> 2][e & 3] : 0.f;
+      hi[e] = (f16)z;
+      lo[e] = (f16)(z - (float)hi[e]);
     }
+    acc = mfma32x32x16(hi, bb, acc);
+    acc = mfma32x32x16(lo, bb, acc);
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) red[w][r][lane] = acc[r];
@@ -482,10 +488,23 @@ upproj_valu_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
     bvr[i] = (nlive && k < RV) ? *reinterpret_cast<const half8*>(bv + (size_t)k * ld + (size_t)kvh * D + n0 + nsub)
                                : half8{};
   }
-  for (int idx = t; idx < rows * (RV / 4); idx += 256) {
-    const int r = idx / (RV / 4), c = idx % (RV / 4);
-    *reinterpret_cast<floatx4*>(&zl[r][c * 4]) =
-        *reinterpret_cast<const floatx4*>(zf + ((size_t)(row0 + r) * H + h) * RV + c * 4);
+  // Z rows -> LDS: every load of a thread is issued before its first LDS write
+  {
+    constexpr int kPer = kSmallBatch * kUpvMaxRV / 4 / 256;
+    floatx4 zv[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = t + 256 * i;
+      const int r = idx / (RV / 4), c = idx % (RV / 4);
+      zv[i] = idx < rows * (RV / 4) ? *reinterpret_cast<const floatx4*>(zf + ((size_t)(row0 + r) * H + h) * RV + c * 4)
+                                    : floatx4{};
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the LDS writes
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = t + 256 * i;
+      if (idx < rows * (RV / 4)) *reinterpret_cast<floatx4*>(&zl[idx / (RV / 4)][(idx % (RV / 4)) * 4]) = zv[i];
+    }
   }
   __syncthreads();
   for (int g = 0; g < rows; g += 4) {
@@ -593,8 +612,18 @@ hipError_t launch_upproj(const Shape& s, int rows, const float* zf, const void* 
   if (rows >= kSmallBatch && s.D % 32 == 0 && s.RV % (16 * kUpWaves) == 0 && s.RV <= kUpWaves * kUpMaxSpan) {
     const int groups = ((rows + 31) / 32) * s.H;
     const int grid = ((groups + 7) / 8) * 8 * (s.D / 32);
-    hipLaunchKernelGGL(upproj_mfma_kernel, dim3(grid), dim3(kUpWaves * 64), 0, st, zf,
-                       static_cast<const f16*>(b_v), static_cast<f16*>(out), rows, s.H, s.KV, s.D, s.RV);
+    const f16* bv = static_cast<const f16*>(b_v);
+    f16* o = static_cast<f16*>(out);
+    switch (s.RV / (16 * kUpWaves)) {
+      case 1: hipLaunchKernelGGL(upproj_mfma_kernel<1>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+      case 2: hipLaunchKernelGGL(upproj_mfma_kernel<2>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+      case 3: hipLaunchKernelGGL(upproj_mfma_kernel<3>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+      case 4: hipLaunchKernelGGL(upproj_mfma_kernel<4>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+      case 5: hipLaunchKernelGGL(upproj_mfma_kernel<5>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+      case 6: hipLaunchKernelGGL(upproj_mfma_kernel<6>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+      case 7: hipLaunchKernelGGL(upproj_mfma_kernel<7>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+      default: hipLaunchKernelGGL(upproj_mfma_kernel<8>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+    }
   } else {
     const int grid = s.H * ((s.D + 31) / 32);
     hipLaunchKernelGGL(upproj_valu_kernel, dim3(grid, (rows + kSmallBatch - 1) / kSmallBatch), dim3(256), 0, st, zf,
