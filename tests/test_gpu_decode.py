@@ -304,6 +304,36 @@ def test_append_then_decode_other_ranks(rk, rv, per_seq):
     check(out, ref, what=f"append+decode r_k={rk} r_v={rv}")
 
 
+@pytest.mark.parametrize("d", [256, 40])
+@pytest.mark.parametrize("batch,per_seq", [(4, 6), (40, 1)])
+def test_head_dims_append_then_decode(d, batch, per_seq):
+    """head_dim at the limit (256) and one that is a multiple of 8 only (40:
+    the projections fall back from MFMA to VALU); 4 sequences take the
+    small-batch decode stages, 40 the MFMA ones."""
+    import torch
+    import rank_compressed_paged_amd as starkv
+    dev = gpu()
+    rng = np.random.default_rng(450 + d + batch)
+    lens = rng.integers(1, 400, size=batch)
+    rk = min(64, d - d % 32)                      # orthonormal B_k rows need r_k <= d
+    case = synth.make_case(450 + d + batch, batch, 32, d, rk, 1024, lens, spare_tokens=per_seq)
+    g = to_dev(case, dev)
+    seqs = np.repeat(np.arange(batch, dtype=np.int32), per_seq)
+    poss = np.concatenate([np.arange(n, n + per_seq, dtype=np.int32) for n in lens])
+    k_new, v_new = synth.make_new_rows(450 + d, len(seqs), 32, d)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    log(f"head_dim {d}: batch {batch}, {per_seq} appended per sequence")
+    starkv.append(t(k_new), t(v_new), g["b_k"], g["b_v"], g["block_tables"], t(seqs), t(poss),
+                  g["k_pool"], g["v_pool"])
+    new_lens = lens + per_seq
+    scale = 1.0 / math.sqrt(d)
+    out = decode_gpu(g, new_lens, scale, dev)
+    kp, vp = oracle.append(k_new, v_new, case["b_k"], case["b_v"], case["block_tables"], seqs, poss,
+                           case["k_pool"], case["v_pool"])
+    ref = oracle.decode(case["q"], case["b_k"], case["b_v"], kp, vp, case["block_tables"], new_lens, scale)
+    check(out, ref, what=f"append+decode d={d} r_k={rk} batch={batch}")
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("layer", [12, 28])
 def test_config6_mixed_rank_layer_full_size_sampled(layer):

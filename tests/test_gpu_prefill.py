@@ -68,6 +68,19 @@ def test_prefill_single_range_direct_write():
     check(out, oracle_prefill(case, 1.0), "prefill single range")
 
 
+@pytest.mark.parametrize("d", [256, 64])
+def test_prefill_head_dims(d):
+    """Other head dims: 300 rows take the general MFMA up-projection instead
+    of the 128-dim many-row one."""
+    dev = gpu()
+    lens, chunks = [500, 130], [200, 100]
+    case = synth.make_prefill_case(720 + d, 32, d, 64, 1024, lens, chunks)
+    scale = 1.0 / math.sqrt(d)
+    log(f"prefill head_dim {d}")
+    out = prefill_gpu(to_dev(case, dev), case, scale, dev)
+    check(out, oracle_prefill(case, scale), f"prefill d={d}")
+
+
 @pytest.mark.parametrize("rk,rv", [(64, 768), (64, 512), (64, 256), (32, 1024), (32, 768), (32, 512), (32, 256)])
 def test_prefill_rank_shapes(rk, rv):
     dev = gpu()
