@@ -104,12 +104,8 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
   const int32_t* __restrict__ prefix = pv.prefix();
   const int32_t* __restrict__ slot_base = pv.slot_base();
 
-  // sequence holding block `start`: last b with prefix[b] <= start
-  int lo = 0, hi = batch;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (prefix[mid] <= start) lo = mid; else hi = mid;
-  }
+  // sequence holding block `start` (from the plan)
+  const int lo = pv.first_seq()[blockIdx.x];
   struct It { int gi, b, lo, hi; };
   It cur{start, lo, prefix[lo], prefix[lo + 1]};
   auto advance = [&](It& it) {
@@ -177,20 +173,30 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
   const int half_ = lane >> 5;       // which 8 tokens of the block
   const bool row_live = h < H;
 
-  // q~ of the range's first QCAP sequences -> LDS before any latent load is in
-  // flight.  The vector-memory counter retires in order, so a q~ load issued
-  // behind the latent prefetch would drain it; only ranges touching more than
-  // QCAP sequences pay that, once per extra sequence.
+  // q~ of the range's first QCAP sequences: loaded ahead of the first latent
+  // prefetch and written to LDS behind it (the vector-memory counter retires
+  // in order, so waiting for q~ then leaves the prefetch in flight).  A q~
+  // load issued behind the latent prefetch would drain it; only ranges
+  // touching more than QCAP sequences pay that, once per extra sequence.
   const int b_first = cur.b;
   auto stage_q = [&](int slot_q, int b) {
     const floatx4* qsrc = reinterpret_cast<const floatx4*>(qt + (size_t)b * H * RK);
     for (int i = threadIdx.x; i < H * RK / 4; i += C::kThreads)
       reinterpret_cast<floatx4*>(q_lds[slot_q])[i] = qsrc[i];
   };
-  for (int sq = 0; sq < QCAP && b_first + sq < batch; ++sq) stage_q(sq, b_first + sq);
-  __syncthreads();
-  const float* qcur = q_lds[0];
+  constexpr int QV = H * RK / 4;                         // float4 words of one sequence's q~
+  constexpr int QPT = (QV + C::kThreads - 1) / C::kThreads;
+  floatx4 q0reg[QCAP][QPT];
+#pragma unroll
+  for (int sq = 0; sq < QCAP; ++sq)
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int b = min(b_first + sq, batch - 1);        // past the batch: re-read, not stored
+      const int i = min((int)threadIdx.x + u * C::kThreads, QV - 1);
+      q0reg[sq][u] = reinterpret_cast<const floatx4*>(qt + (size_t)b * H * RK)[i];
+    }
 
+  const float* qcur = q_lds[0];
   // MFMA path: the wave's A operands (q~ of its group's query heads, rows
   // beyond the group zero) as fp16 high + low parts, held for a segment.
   // x - hi is exact in fp32, so hi + lo carries q~ to about 2^-22 relative.
@@ -235,6 +241,14 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     load_v(vb[u], physu, !more);
     if (more) advance(pf);
   }
+#pragma unroll
+  for (int sq = 0; sq < QCAP; ++sq)
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int i = (int)threadIdx.x + u * C::kThreads;
+      if (b_first + sq < batch && i < QV) reinterpret_cast<floatx4*>(q_lds[sq])[i] = q0reg[sq][u];
+    }
+  __syncthreads();
 
   // register r of lane l holds row (r&3) + 8(r>>2) + 4(l>>5): the r part goes
   // into a uniform base, the lane part into one 32-bit offset
@@ -283,6 +297,8 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
       for (int t = 0; t < C::TPW; ++t) acc[t] = floatx16{};
     }
     const int nvalid = min(kBlock, seq_len - lb * kBlock);
+    const bool more = pf.gi < end;
+    const int pphys = more ? phys_of(pf) : cphys;
 
     // latent-key scores of this block -> LDS
     if constexpr (C::kMfmaScores) {
@@ -302,6 +318,10 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
         }
       }
     } else {
+      // each piece's register is refilled with the next block's piece as soon
+      // as it has been read, so the ring stays full while the dots run
+      const half8* nbase = reinterpret_cast<const half8*>(kpool + (size_t)pphys * C::kBlockKHalves) +
+                           (more ? (w * C::PPW) * 64 : 0) + lane;
 #pragma unroll
       for (int j = 0; j < C::PPW; ++j) {
         const half8 kx = kb[BUF][j];
@@ -315,13 +335,12 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
         s += q1[1] * (float)kx[5];
         s += q1[2] * (float)kx[6];
         s += q1[3] * (float)kx[7];
+        kb[BUF][j] = __builtin_nontemporal_load(nbase + j * 64);
         s = group_sum<C::LPT>(s);
         if (c8 == 0) s_lds[BUF][0][piece_head(j)][piece_tok(j)] = s;
       }
     }
-    const bool more = pf.gi < end;
-    const int pphys = more ? phys_of(pf) : cphys;
-    load_k(kb[BUF], pphys, !more);
+    if constexpr (C::kMfmaScores) load_k(kb[BUF], pphys, !more);
     __syncthreads();
 
     // online softmax in the MFMA A-operand layout: row h, tokens 8*half_..+7

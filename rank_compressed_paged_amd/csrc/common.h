@@ -96,6 +96,8 @@ struct PlanView {
   __device__ int total() const { return p[1]; }
   __device__ const int32_t* prefix() const { return p + 2; }
   __device__ const int32_t* slot_base() const { return p + 3 + batch; }
+  // sequence holding the first block of each attention workgroup's range
+  __device__ const int32_t* first_seq() const { return p + 4 + 2 * batch; }
 };
 
 }  // namespace starkv

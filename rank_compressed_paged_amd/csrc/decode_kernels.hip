@@ -43,13 +43,15 @@ __device__ int block_inclusive_scan(int v, int* sh) {
 
 // Equal split of the batch's blocks over `grid` workgroups.  prefix[b] is the
 // first global block of sequence b; a sequence spanning workgroups g0..g1 owns
-// partial slots slot_base[b] .. slot_base[b] + (g1 - g0).
+// partial slots slot_base[b] .. slot_base[b] + (g1 - g0); first[g] is the
+// (non-empty) sequence holding workgroup g's first block.
 __device__ void build_plan(const int32_t* __restrict__ lens, int batch, int grid,
                            int32_t* __restrict__ plan) {
   __shared__ int sh[kPlanThreads];
   const int tid = threadIdx.x;
   int32_t* prefix = plan + 2;
   int32_t* sbase = plan + 3 + batch;
+  int32_t* first = plan + 4 + 2 * batch;
   int carry = 0;
   for (int base = 0; base < batch; base += kPlanThreads) {
     const int i = base + tid;
@@ -75,6 +77,9 @@ __device__ void build_plan(const int32_t* __restrict__ lens, int batch, int grid
     const int y = block_inclusive_scan(np, sh);
     const int chunk2 = sh[kPlanThreads - 1];
     if (i < batch) sbase[i + 1] = carry2 + y;
+    // ranges starting inside this sequence: g*W in [excl, incl), g < grid
+    if (i < batch && v > 0)
+      for (int g = (excl + W - 1) / W; g * W < incl; ++g) first[g] = i;
     carry1 += chunk1;
     carry2 += chunk2;
     __syncthreads();
@@ -556,7 +561,7 @@ DecodeLayout decode_layout(const Shape& s, int batch, int max_context_len) {
   L.max_slots = L.grid_cap + batch;
   size_t off = 0;
   L.off_plan = off;
-  off = align256(off + sizeof(int32_t) * (size_t)(4 + 2 * batch));
+  off = align256(off + sizeof(int32_t) * (size_t)(4 + 2 * batch + L.grid_cap));
   L.off_qt = off;
   off = align256(off + sizeof(float) * (size_t)batch * s.H * s.RK);
   L.off_ml = off;
