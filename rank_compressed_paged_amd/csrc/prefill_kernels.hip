@@ -159,12 +159,30 @@ template <int RK, int RV>
 struct PfCfg {
   static constexpr int KS = RK / 32;               // 16x16x32 k-steps of a score tile
   static constexpr int TPW = RV / 32 / kPfWaves;   // 32-dim V tiles per wave
+  static constexpr int VB = 3;                     // V blocks in registers (held or in flight)
+  static constexpr int KSTG = 8;                   // K ring stages in LDS
+  static constexpr int CPR = RK / 8;               // 16-byte chunks per token row of a K block
+  static constexpr int KI = kBlock * CPR / 64;     // wave instructions per K block (1 KiB each)
   static_assert(RK % 32 == 0 && KS >= 1 && KS <= 2, "r_k in {32, 64}");
   static_assert(RV % (32 * kPfWaves) == 0 && TPW >= 1 && TPW <= 4, "r_v in {256, 512, 768, 1024}");
 };
 
 template <int N>
 using PfIC = std::integral_constant<int, N>;
+
+// Workgroup barrier for LDS data written with ds_write (waited here) or by
+// direct global-to-LDS loads that the writing wave has already waited for.
+// Unlike __syncthreads() it does not wait for the V ring loads still in
+// flight; the "memory" clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at
+// byte 16*l from lds (wave-uniform), no VGPRs held; counted by the
+// vector-memory counter like any load.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
 
 // max over the 16 lanes of a DPP row (lanes 16g .. 16g+15)
 __device__ __forceinline__ float group_max16(float x) {
@@ -189,9 +207,14 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
   __shared__ float a_lds[3][kPfRows];
   __shared__ __attribute__((aligned(16))) int flag_lds[3][4];
   __shared__ int slot_lds[kPfRows];
+  // K ring of eight stages, one block (16 tokens x r_k of the workgroup's
+  // key head) each, filled by direct global-to-LDS loads of wave 4.  Chunk c
+  // (16 bytes) of token t sits at slot t*CPR + (c ^ swz(t)), so the scorer
+  // waves' fragment reads (16 tokens at one chunk) spread over the banks.
+  __shared__ __attribute__((aligned(16))) f16 k_lds[C::KSTG][kBlock * RK];
+  __shared__ float lrow_lds[kPfRows];      // row sums, for the single-range direct write
   // score A operands of the scorer waves (each lane reads back only its own)
   __shared__ half8 qa_lds[4][C::KS][2][64];
-  __shared__ float lrow_lds[kPfRows];      // row sums, for the single-range direct write
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -266,22 +289,37 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
     // Plain (temporal) loads: unlike decode, every K and V block here is
     // re-read by the other heads' workgroups on this XCD and must stay in L2
     // (non-temporal loads cost 25% at 4 x 512 rows over 8192 positions).
-    const f16* kbase = kpool + ((size_t)kvh * kBlock + (lane & 15)) * RK + (lane >> 4) * 8;
     const f16* vbase = vpool + ((size_t)(w * C::TPW * 32 + c32)) * kBlock + 8 * half_;
-    auto load_k = [&](half8 (&dst)[C::KS], int phys) {
-      const f16* p = kbase + (size_t)phys * HKV * kBlock * RK;
+    // K of a block -> ring stage ks8 (wave 4): LDS slot j*64 + lane takes the
+    // chunk that the swizzle puts there
+    auto swz = [](int t) { return (t ^ (t / C::CPR)) % C::CPR; };
+    auto load_k = [&](int ks8, int phys) __attribute__((always_inline)) {
+      const f16* blk = kpool + ((size_t)phys * HKV + kvh) * kBlock * RK;
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) dst[ks] = *reinterpret_cast<const half8*>(p + ks * 32);
+      for (int j = 0; j < C::KI; ++j) {
+        const int slot = j * 64 + lane;
+        const int t = slot / C::CPR, c = (slot % C::CPR) ^ swz(slot / C::CPR);
+        load_lds16(blk + t * RK + c * 8, &k_lds[ks8][j * 64 * 8]);
+      }
     };
-    auto load_v = [&](half8 (&dst)[C::TPW], int phys) {
+    // V of a block -> registers: the B fragments of the wave's own 128 latent
+    // dims (tile t: latent dim c32 of the tile, tokens 8*half_ .. +7), three
+    // blocks held or in flight.  The scorer waves load nothing else in the
+    // block loop, so their in-order waits for V are never held up by K.
+    half8 vb[C::VB][C::TPW];
+    auto load_v = [&](auto bufc, int phys) __attribute__((always_inline)) {
+      constexpr int BUF = decltype(bufc)::value;
       const f16* p = vbase + (size_t)phys * RV * kBlock;
 #pragma unroll
-      for (int t = 0; t < C::TPW; ++t)
-        dst[t] = *reinterpret_cast<const half8*>(p + t * 32 * kBlock);
+      for (int t = 0; t < C::TPW; ++t) vb[BUF][t] = *reinterpret_cast<const half8*>(p + t * 32 * kBlock);
+    };
+    // wave 4: K of block ib+3 has landed once the V of block ib+1 and the K
+    // and V of the two later blocks are all that is outstanding
+    auto wait_k4 = [&]() {
+      constexpr int n = C::TPW + 2 * (C::KI + C::TPW);
+      __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
     };
 
-    half8 kb[2][C::KS];
-    half8 vb[2][C::TPW];
     floatx16 acc[2][C::TPW];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
@@ -296,20 +334,23 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
       l_part[i] = 0.f;
     }
 
-    // scores of a block held in kb[BUF] (scorer waves)
-    auto score_mfma = [&](auto bufc) -> floatx4 {
-      constexpr int BUF = decltype(bufc)::value;
+    // scores of the block in K ring stage ks8 (scorer waves): B fragment of
+    // k-step ks = token l%16, chunk 4*ks + l/16
+    auto score_mfma = [&](int ks8) __attribute__((always_inline)) -> floatx4 {
+      const int t = lane & 15;
       floatx4 sc{};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        sc = mfma16x16x32(qa_lds[w][ks][0][lane], kb[BUF][ks], sc);
-        sc = mfma16x16x32(qa_lds[w][ks][1][lane], kb[BUF][ks], sc);
+        const int c = 4 * ks + (lane >> 4);
+        const half8 kf = *reinterpret_cast<const half8*>(&k_lds[ks8][(t * C::CPR + (c ^ swz(t))) * 8]);
+        sc = mfma16x16x32(qa_lds[w][ks][0][lane], kf, sc);
+        sc = mfma16x16x32(qa_lds[w][ks][1][lane], kf, sc);
       }
       return sc;
     };
     // causal mask and online softmax of block ib (scorer waves) -> P, rescale
     // factors and flag in LDS buffer PB
-    auto softmax = [&](int PB, const floatx4 sc, int ib) {
+    auto softmax = [&](int PB, const floatx4 sc, int ib) __attribute__((always_inline)) {
       const int tpos = (blk_lo + ib) * kBlock + (lane & 15);
       float s[4];
       bool exceed = false;
@@ -347,7 +388,7 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
     };
 
     // z += P . c_v of block ib (all waves): V in vb[BUF], P in LDS buffer PB
-    auto accumulate = [&](auto bufc, int PB, int ib) {
+    auto accumulate = [&](auto bufc, int PB, int ib) __attribute__((always_inline)) {
       constexpr int BUF = decltype(bufc)::value;
       half8 pa[2];
 #pragma unroll
@@ -377,43 +418,75 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
         for (int t = 0; t < C::TPW; ++t) acc[rt][t] = mfma32x32x16(pa[rt], vb[BUF][t], acc[rt][t]);
     };
 
-    // Prologue: K and V of blocks 0 and 1 in flight; scores of blocks 0 and
-    // 1.  K of block b lives in kb[b & 1], V in vb[b & 1], P in LDS buffer
-    // b % 3.  Loads past the range re-read block 0 (always in range), so every
-    // path issues the same loads and the in-order wait counts stay exact.
+    // K of block b sits in LDS ring stage b % 8, V in vb[b % 3], P in LDS
+    // buffer b % 3.  Scores run two blocks ahead of the z accumulation.  Step
+    // ib: wave 4 loads K of block ib+5, every wave loads its V of block ib+3
+    // into the registers block ib has just left, so both have three steps to
+    // arrive; the scorer waves put the scores of block ib+2 into the MFMA pipe
+    // ahead of block ib's z MFMAs and run its softmax while those drain; wave
+    // 4 waits for K of block ib+3, which the barrier then publishes.  Loads
+    // past the range re-read block 0 (always in range), so every path of a
+    // wave issues the same loads and the in-order wait counts stay exact.
+    // Both roles pass the same number of barriers.
     const int phys0 = table[0];
-    const int phys1 = nblk > 1 ? table[1] : phys0;
-    load_k(kb[0], phys0);
-    load_k(kb[1], phys1);
-    load_v(vb[0], phys0);
-    load_v(vb[1], phys1);
-    if (scorer) softmax(0, score_mfma(PfIC<0>{}), 0);
-    load_k(kb[0], nblk > 2 ? table[2] : phys0);
-    if (scorer && nblk > 1) softmax(1, score_mfma(PfIC<1>{}), 1);
-    load_k(kb[1], nblk > 3 ? table[3] : phys0);
-    __syncthreads();
-
-    // Step ib: scores of block ib+2 go into the MFMA pipe first, then block
-    // ib's z MFMAs; the softmax of block ib+2 runs while those drain.
-    int pb = 0;                              // ib % 3
-    auto step = [&](auto bufc, int ib) {
-      constexpr int BUF = decltype(bufc)::value;
-      floatx4 sc{};
-      if (scorer) sc = score_mfma(bufc);     // block ib+2 (a spare block past the end)
-      accumulate(bufc, pb, ib);
-      load_v(vb[BUF], ib + 2 < nblk ? table[ib + 2] : phys0);
-      const int pb2 = pb == 0 ? 2 : pb - 1;  // (ib + 2) % 3
-      if (scorer && ib + 2 < nblk) softmax(pb2, sc, ib + 2);
-      load_k(kb[BUF], ib + 4 < nblk ? table[ib + 4] : phys0);
-      pb = pb == 2 ? 0 : pb + 1;
-      __syncthreads();
-    };
-    int ib = 0;
-    for (; ib + 1 < nblk; ib += 2) {
-      step(PfIC<0>{}, ib);
-      step(PfIC<1>{}, ib + 1);
+    auto tab = [&](int b) { return b < nblk ? table[b] : phys0; };
+    if (w == 4) {
+      load_k(0, phys0);
+      load_k(1, tab(1));
+      load_k(2, tab(2));
     }
-    if (ib < nblk) step(PfIC<0>{}, ib);
+    load_v(PfIC<0>{}, phys0);
+    if (w == 4) load_k(3, tab(3));
+    load_v(PfIC<1>{}, tab(1));
+    if (w == 4) load_k(4, tab(4));
+    load_v(PfIC<2>{}, tab(2));
+    if (w == 4) {                            // K of blocks 0, 1
+      constexpr int n = 3 * C::KI + 3 * C::TPW;
+      __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+    }
+    barrier_lds();
+    if (scorer) {
+      softmax(0, score_mfma(0), 0);
+      if (nblk > 1) softmax(1, score_mfma(1), 1);
+    }
+    if (w == 4) {                            // K of block 2
+      constexpr int n = 2 * C::KI + 3 * C::TPW;
+      __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+    }
+    barrier_lds();
+    if (scorer) {
+      auto step = [&](auto bufc, int ib) __attribute__((always_inline)) {
+        const floatx4 sc = score_mfma((ib + 2) & 7);   // block ib+2 (a spare block past the end)
+        accumulate(bufc, decltype(bufc)::value, ib);
+        load_v(bufc, tab(ib + 3));
+        if (ib + 2 < nblk) softmax((decltype(bufc)::value + 2) % 3, sc, ib + 2);
+        barrier_lds();
+      };
+      int ib = 0;
+      for (; ib + 2 < nblk; ib += 3) {
+        step(PfIC<0>{}, ib);
+        step(PfIC<1>{}, ib + 1);
+        step(PfIC<2>{}, ib + 2);
+      }
+      if (ib < nblk) step(PfIC<0>{}, ib);
+      if (ib + 1 < nblk) step(PfIC<1>{}, ib + 1);
+    } else {
+      auto step = [&](auto bufc, int ib) __attribute__((always_inline)) {
+        if (w == 4) load_k((ib + 5) & 7, tab(ib + 5));
+        accumulate(bufc, decltype(bufc)::value, ib);
+        load_v(bufc, tab(ib + 3));
+        if (w == 4) wait_k4();               // K of block ib+3
+        barrier_lds();
+      };
+      int ib = 0;
+      for (; ib + 2 < nblk; ib += 3) {
+        step(PfIC<0>{}, ib);
+        step(PfIC<1>{}, ib + 1);
+        step(PfIC<2>{}, ib + 2);
+      }
+      if (ib < nblk) step(PfIC<0>{}, ib);
+      if (ib + 1 < nblk) step(PfIC<1>{}, ib + 1);
+    }
 
     if (zdirect) {
       // Every row's context fits one range: write z / l straight into the
