@@ -120,27 +120,42 @@ prefill_plan_kernel(const int32_t* __restrict__ qs, const int32_t* __restrict__ 
     __syncthreads();
   }
 
-  // 3. partial slots of every query row: one per range its context reaches
-  int slots = 0;
-  for (int base = 0; base < rows; base += 256) {
-    const int r = base + tid;
-    int ns = 0;
-    if (r < rows) {
-      int lo = 0, hi = batch;                 // last b with qs[b] <= r
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (qs[mid] <= r) lo = mid; else hi = mid;
-      }
-      const int n = qs[lo + 1] - qs[lo];
-      const int pos = max(0, lens[lo] - n + (r - qs[lo]));
-      ns = (pos / kBlock + range_blocks) / range_blocks;   // ceil((pos/16 + 1) / RB)
-      row_len[r] = pos + 1;
+  // 3. partial slots of every query row: one per range its context reaches.
+  // Thread tid takes the contiguous rows [r0, r1), finds the sequence of r0
+  // once and walks forward; one block scan of the per-thread counts.
+  const int per = (rows + 255) / 256;
+  const int r0 = min(rows, tid * per), r1 = min(rows, r0 + per);
+  int b0 = 0;
+  if (r0 < r1) {
+    int lo = 0, hi = batch;                   // last b with qs[b] <= r0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (qs[mid] <= r0) lo = mid; else hi = mid;
     }
-    const int x = pf_block_scan(ns, sh);
-    const int chunk = sh[255];
-    if (r < rows) slot_base[r] = slots + x - ns;
-    slots += chunk;
-    __syncthreads();
+    b0 = lo;
+  }
+  // ns(r) for the rows of this thread, in order; f(r, ns, pos) per row
+  auto walk = [&](auto f) {
+    int b = b0;
+    int q0 = qs[b], q1 = qs[b + 1], L = lens[b];
+    for (int r = r0; r < r1; ++r) {
+      while (q1 <= r && b + 1 < batch) {     // next non-empty sequence holding row r
+        ++b;
+        q0 = q1;
+        q1 = qs[b + 1];
+        L = lens[b];
+      }
+      const int pos = max(0, L - (q1 - q0) + (r - q0));
+      f(r, (pos / kBlock + range_blocks) / range_blocks, pos);   // ceil((pos/16 + 1) / RB)
+    }
+  };
+  int cnt = 0;
+  if (r0 < r1) walk([&](int r, int ns, int pos) { cnt += ns; row_len[r] = pos + 1; });
+  const int x = pf_block_scan(cnt, sh);
+  const int slots = sh[255];
+  if (r0 < r1) {
+    int run = x - cnt;
+    walk([&](int r, int ns, int) { slot_base[r] = run; run += ns; });
   }
   if (tid == 0) {
     plan[0] = range_blocks;
@@ -195,7 +210,8 @@ __device__ __forceinline__ float group_max16(float x) {
 
 template <int RK, int RV>
 __global__ void __launch_bounds__(kPfWaves * 64)
-prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f16* __restrict__ vpool,
+prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, const f16* __restrict__ bk, int D,
+                    float scale2, const f16* __restrict__ kpool, const f16* __restrict__ vpool,
                     const int32_t* __restrict__ block_tables, int mb_stride, const int32_t* __restrict__ qs,
                     const int32_t* __restrict__ lens, const int32_t* __restrict__ plan, int rows, int tile_cap,
                     int H, int G, int HKV, float* __restrict__ part_z, float* __restrict__ part_ml,
@@ -215,6 +231,8 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
   __shared__ float lrow_lds[kPfRows];      // row sums, for the single-range direct write
   // score A operands of the scorer waves (each lane reads back only its own)
   __shared__ half8 qa_lds[4][C::KS][2][64];
+  // q~ of a scorer wave's 16 rows, from its MFMA result layout to the A layout
+  __shared__ __attribute__((aligned(16))) float qf_lds[4][16][RK + 4];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -268,6 +286,32 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool,
       const int rr = w * 16 + (lane & 15);
       const bool live = rr < nrows;
       const float* qrow = qt + ((size_t)(live ? row0 + rr : 0) * H + h) * RK + (lane >> 4) * 8;
+      if (qt == nullptr) {
+        // q~ = scale*log2(e) * B_k[g(h)] q of the wave's 16 rows on 16x16x32
+        // MFMA (A = q rows, B = B_k rows, both contiguous along d), then
+        // through LDS from the result layout (lane: latent l%16 of a 16-wide
+        // tile, rows 4*(l/16)+i) to the row layout the score MFMA takes
+        const f16* qa = q + ((size_t)(row0 + min(rr, nrows - 1)) * H + h) * D + (lane >> 4) * 8;
+        const f16* ba = bk + ((size_t)kvh * RK + (lane & 15)) * D + (lane >> 4) * 8;
+        floatx4 c[RK / 16];
+#pragma unroll
+        for (int nt = 0; nt < RK / 16; ++nt) c[nt] = floatx4{};
+        for (int k0 = 0; k0 < D; k0 += 32) {
+          const half8 a8 = *reinterpret_cast<const half8*>(qa + k0);
+#pragma unroll
+          for (int nt = 0; nt < RK / 16; ++nt)
+            c[nt] = mfma16x16x32(a8, *reinterpret_cast<const half8*>(ba + (size_t)nt * 16 * D + k0), c[nt]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < RK / 16; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) qf_lds[w][4 * (lane >> 4) + i][nt * 16 + (lane & 15)] = c[nt][i] * scale2;
+        // other lanes of this wave wrote what this lane reads next
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        qrow = &qf_lds[w][lane & 15][(lane >> 4) * 8];
+      }
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         half8 hi8{}, lo8{};
@@ -596,7 +640,7 @@ PrefillLayout prefill_layout(const Shape& s, int batch, int rows, int max_contex
 }
 
 template <int RK, int RV>
-static hipError_t launch_pf_attn(const PrefillLaunch& a, const float* qt, const int32_t* plan, float* pz,
+static hipError_t launch_pf_attn(const PrefillLaunch& a, const float* qt, float scale2, const int32_t* plan, float* pz,
                                  float* pml, float* zdirect, int device) {
   const auto kernel = prefill_attn_kernel<RK, RV>;
   static std::atomic<int> resident[64];
@@ -614,6 +658,7 @@ static hipError_t launch_pf_attn(const PrefillLaunch& a, const float* qt, const 
   long long grid = units_ub < res ? units_ub : res;
   grid = ((grid + 7) / 8) * 8;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPfWaves * 64), 0, a.stream, qt,
+                     static_cast<const f16*>(a.q), static_cast<const f16*>(a.b_k), s.D, scale2,
                      static_cast<const f16*>(a.k_cache), static_cast<const f16*>(a.v_cache), a.block_tables, s.MB,
                      a.query_start, a.context_lens, plan, a.rows, a.lay.tile_cap, s.H, s.H / s.KV, s.KV, pz, pml,
                      zdirect, kRescaleTau);
@@ -632,15 +677,21 @@ hipError_t prefill_enqueue(const PrefillLaunch& a, int device) {
                      a.rows, a.lay.range_blocks, a.lay.tile_cap, plan);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  err = launch_qproj(s, a.rows, a.q, a.b_k, a.scale * kLog2e, qt, nullptr, 0, nullptr, a.stream);
-  if (err != hipSuccess) return err;
+  // q~: inside the attention kernel when d is a multiple of 32, else its own pass
+  const float scale2 = a.scale * kLog2e;
+  const bool qproj_fused = s.D % 32 == 0;
+  if (!qproj_fused) {
+    err = launch_qproj(s, a.rows, a.q, a.b_k, scale2, qt, nullptr, 0, nullptr, a.stream);
+    if (err != hipSuccess) return err;
+  }
 
   if (a.ev_attn_start && hipEventRecord(a.ev_attn_start, a.stream) != hipSuccess) return hipErrorUnknown;
   err = hipErrorInvalidValue;
   // one context range for every row: the attention kernel writes Z itself
   float* zdirect = a.lay.max_ranges == 1 ? zf : nullptr;
 #define X(rk, rv) \
-  if (s.RK == rk && s.RV == rv) err = launch_pf_attn<rk, rv>(a, qt, plan, pz, pml, zdirect, device);
+  if (s.RK == rk && s.RV == rv)                                                                           \
+    err = launch_pf_attn<rk, rv>(a, qproj_fused ? nullptr : qt, scale2, plan, pz, pml, zdirect, device);
   STARKV_PREFILL_SHAPES(X)
 #undef X
   if (err != hipSuccess) return err;
