@@ -101,6 +101,35 @@ def test_prefill_grouped_heads(kv, rv):
     check(out, oracle_prefill(case, 1.0 / math.sqrt(128)), f"prefill H_kv={kv} r_v={rv}")
 
 
+# (H, H_kv, d, r_k, r_v) drawn by the randomized cases: every built rank pair
+# for 32 heads, grouped layouts, and head dims that take the in-kernel q~
+# projection (d % 32 == 0) or the separate one (d = 40)
+RANDOM_SHAPES = [(32, 32, 128, 64, 1024), (32, 32, 128, 32, 768), (32, 32, 64, 64, 512), (32, 8, 128, 64, 512),
+                 (32, 4, 128, 64, 256), (32, 32, 40, 32, 256), (32, 8, 256, 32, 512)]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefill_random_ragged(seed):
+    """Random batch, context lengths, chunk sizes (empty, single-row, tile
+    multiples and tails), shape and scale, against the oracle."""
+    dev = gpu()
+    rng = np.random.default_rng(7000 + seed)
+    h, kv, d, rk, rv = RANDOM_SHAPES[seed % len(RANDOM_SHAPES)]
+    batch = int(rng.integers(1, 7))
+    lens = rng.integers(1, 1500, size=batch)
+    lens[rng.random(batch) < 0.2] = int(rng.integers(1, 20))
+    chunks = np.array([int(rng.choice([0, 1, 63, 64, 65, int(rng.integers(1, L + 1))])) for L in lens])
+    chunks = np.minimum(chunks, lens)
+    if chunks.sum() == 0:
+        chunks[0] = lens[0]
+    scale = float(rng.choice([1.0 / math.sqrt(d), 1.0, 0.3]))
+    log(f"random prefill seed {seed}: H={h} H_kv={kv} d={d} r_k={rk} r_v={rv} lens={lens.tolist()} "
+        f"chunks={chunks.tolist()} scale={scale:.3f}")
+    case = synth.make_prefill_case(7100 + seed, h, d, rk, rv, lens, chunks, kv_heads=kv)
+    out = prefill_gpu(to_dev(case, dev), case, scale, dev)
+    check(out, oracle_prefill(case, scale), f"random prefill seed {seed}")
+
+
 def test_prefill_single_rows_match_decode():
     """One query per sequence is decode: both kernels agree within tolerance."""
     from helpers import decode_gpu
