@@ -31,14 +31,13 @@ struct SlotOf {
 // K side, MFMA: one wave computes a [32 tokens x 32 latents] tile of one head.
 // The destination slots and all operand loads are issued before the first
 // MFMA, so the launch costs about one memory latency.
-__global__ void __launch_bounds__(64)
-append_k_mfma_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int n, int H, int D, int RK,
-                     SlotOf where, f16* __restrict__ kc) {
-  const int lane = threadIdx.x;
+__device__ __forceinline__ void append_k_mfma_body(int tile, int lane, const f16* __restrict__ k,
+                                                   const f16* __restrict__ wk, int n, int H, int D, int RK,
+                                                   SlotOf where, f16* __restrict__ kc) {
   const int rtiles = RK / 32;
-  const int rt = blockIdx.x % rtiles;
-  const int h = (blockIdx.x / rtiles) % H;
-  const int tt = blockIdx.x / (rtiles * H);
+  const int rt = tile % rtiles;
+  const int h = (tile / rtiles) % H;
+  const int tt = tile / (rtiles * H);
   const int t = tt * 32 + (lane & 31);
   const bool trow = t < n;
   const int r = rt * 32 + (lane & 31);
@@ -74,10 +73,9 @@ append_k_mfma_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int 
 }
 
 // K side, VALU: one thread per (token, head, latent).
-__global__ void __launch_bounds__(256)
-append_k_valu_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int n, int H, int D, int RK,
-                     SlotOf where, f16* __restrict__ kc) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void append_k_valu_body(int idx, const f16* __restrict__ k, const f16* __restrict__ wk,
+                                                   int n, int H, int D, int RK, SlotOf where,
+                                                   f16* __restrict__ kc) {
   if (idx >= n * H * RK) return;
   const int r = idx % RK;
   const int h = (idx / RK) % H;
@@ -101,9 +99,8 @@ append_k_valu_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int 
 constexpr int kAppendVWaves = 8;
 constexpr int kAppendVBatch = 16;
 
-__global__ void __launch_bounds__(kAppendVWaves * 64)
-append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
-                     SlotOf where, f16* __restrict__ vc) {
+__device__ __forceinline__ void append_v_mfma_body(int bid, const f16* __restrict__ v, const f16* __restrict__ wv,
+                                                   int n, int K, int RV, SlotOf where, f16* __restrict__ vc) {
   __shared__ float red[kAppendVWaves][4][64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -111,7 +108,7 @@ append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
   // latent tile share its w_v rows, so their ids are equal mod 8
   const int jtiles = RV / 16;
   const int ttiles = (n + 15) / 16;
-  const int x = blockIdx.x % 8, y = blockIdx.x / 8;
+  const int x = bid % 8, y = bid / 8;
   const int jt = (y / ttiles) * 8 + x;
   const int tt = y % ttiles;
   if (jt >= jtiles) return;                 // uniform over the workgroup, before any barrier
@@ -172,9 +169,8 @@ constexpr int kAppendRowsSpan = 128;
 constexpr int kAppendRowsAhead = 4;
 constexpr int kAppendRowsPad = 8;        // halves of LDS row padding
 
-__global__ void __launch_bounds__(512)
-append_v_rows_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
-                     SlotOf where, f16* __restrict__ vc) {
+__device__ __forceinline__ void append_v_rows_body(int bid, const f16* __restrict__ v, const f16* __restrict__ wv,
+                                                   int n, int K, int RV, SlotOf where, f16* __restrict__ vc) {
   constexpr int Row = kAppendRowsSpan + kAppendRowsPad;
   constexpr int kA = kAppendRowsTok * kAppendRowsSpan / 8 / 512;   // 16-byte v pieces per thread per span
   constexpr int kB = kAppendRowsLat * kAppendRowsSpan / 8 / 512;   // 16-byte w_v pieces per thread per span
@@ -184,7 +180,7 @@ append_v_rows_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int ttiles = (n + kAppendRowsTok - 1) / kAppendRowsTok;
-  const int x = blockIdx.x % 8, y = blockIdx.x / 8;
+  const int x = bid % 8, y = bid / 8;
   const int tt = y % ttiles;
   const int jt = (y / ttiles) * 8 + x;
   if (jt * kAppendRowsLat >= RV) return;   // whole workgroup: no barrier skipped unevenly
@@ -271,13 +267,13 @@ append_v_rows_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
 constexpr int kAppendGroup = 4;
 constexpr int kAppendChunk = 4096;                  // contraction elements per pass
 
-__global__ void __launch_bounds__(512)
-append_v_valu_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
-                     SlotOf where, f16* __restrict__ vc) {
+__device__ __forceinline__ void append_v_valu_body(int bx, int by, const f16* __restrict__ v,
+                                                   const f16* __restrict__ wv, int n, int K, int RV, SlotOf where,
+                                                   f16* __restrict__ vc) {
   __shared__ __attribute__((aligned(16))) f16 vl[kAppendGroup][kAppendChunk];
   const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * 8 + (threadIdx.x >> 6);
-  const int t0 = blockIdx.y * kAppendGroup;
+  const int j = bx * 8 + (threadIdx.x >> 6);
+  const int t0 = by * kAppendGroup;
   const int cnt = min(kAppendGroup, n - t0);
   float acc[kAppendGroup] = {};
   for (int kc = 0; kc < K; kc += kAppendChunk) {
@@ -334,6 +330,55 @@ append_v_valu_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
   }
 }
 
+// Kernels of the two sides (each a thin wrapper around its body).
+__global__ void __launch_bounds__(64)
+append_k_mfma_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int n, int H, int D, int RK,
+                     SlotOf where, f16* __restrict__ kc) {
+  append_k_mfma_body(blockIdx.x, threadIdx.x, k, wk, n, H, D, RK, where, kc);
+}
+
+__global__ void __launch_bounds__(256)
+append_k_valu_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int n, int H, int D, int RK,
+                     SlotOf where, f16* __restrict__ kc) {
+  append_k_valu_body(blockIdx.x * 256 + threadIdx.x, k, wk, n, H, D, RK, where, kc);
+}
+
+__global__ void __launch_bounds__(kAppendVWaves * 64)
+append_v_mfma_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
+                     SlotOf where, f16* __restrict__ vc) {
+  append_v_mfma_body(blockIdx.x, v, wv, n, K, RV, where, vc);
+}
+
+__global__ void __launch_bounds__(512)
+append_v_rows_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
+                     SlotOf where, f16* __restrict__ vc) {
+  append_v_rows_body(blockIdx.x, v, wv, n, K, RV, where, vc);
+}
+
+__global__ void __launch_bounds__(512)
+append_v_valu_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
+                     SlotOf where, f16* __restrict__ vc) {
+  append_v_valu_body(blockIdx.x, blockIdx.y, v, wv, n, K, RV, where, vc);
+}
+
+// Small appends (fewer than 16 tokens, both sides on VALU): one launch of
+// 512-thread workgroups, the first nv running the V side and the rest the K
+// side (512 outputs each).  Both sides are latency-bound chains of a few
+// memory round trips, so running them side by side saves one of them.  (With
+// MFMA-sized appends the V side fills every CU by itself and the K side would
+// only start after it.)
+__global__ void __launch_bounds__(512)
+append_kv_valu_kernel(const f16* __restrict__ k, const f16* __restrict__ v, const f16* __restrict__ wk,
+                      const f16* __restrict__ wv, int n, int KV, int D, int RK, int RV, SlotOf where,
+                      f16* __restrict__ kc, f16* __restrict__ vc, int nv, int vgx) {
+  const int bid = blockIdx.x;
+  if (bid < nv) {                            // whole workgroup: the V side's barriers see every wave
+    append_v_valu_body(bid % vgx, bid / vgx, v, wv, n, KV * D, RV, where, vc);
+    return;
+  }
+  append_k_valu_body((bid - nv) * 512 + (int)threadIdx.x, k, wk, n, KV, D, RK, where, kc);
+}
+
 hipError_t append_enqueue(const AppendLaunch& a) {
   const Shape& s = a.s;
   const SlotOf where{a.block_tables, a.token_seq, a.token_pos, s.MB};
@@ -345,7 +390,19 @@ hipError_t append_enqueue(const AppendLaunch& a) {
   f16* vc = static_cast<f16*>(a.v_cache);
   // new rows, w_k and the K pool are per key/value head
   const int K = s.KV * s.D;
-  if (a.n >= 16 && s.RK % 32 == 0 && s.D % 16 == 0) {
+  const bool kmfma = a.n >= 16 && s.RK % 32 == 0 && s.D % 16 == 0;
+  const bool vrows = a.n >= 256 && s.RV % kAppendRowsLat == 0 && K % kAppendRowsSpan == 0;
+  const bool vmfma = !vrows && a.n >= 16 && s.RV % 16 == 0 && K % (32 * kAppendVWaves) == 0;
+  if (!kmfma && !vrows && !vmfma) {
+    const int vgx = (s.RV + 7) / 8;
+    const long long nv = (long long)vgx * ((a.n + kAppendGroup - 1) / kAppendGroup);
+    const long long grid = nv + ((long long)a.n * s.KV * s.RK + 511) / 512;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(append_kv_valu_kernel, dim3((unsigned)grid), dim3(512), 0, a.stream, k, v, wk, wv, a.n, s.KV,
+                       s.D, s.RK, s.RV, where, kc, vc, (int)nv, vgx);
+    return hipGetLastError();
+  }
+  if (kmfma) {
     const int grid = ((a.n + 31) / 32) * s.KV * (s.RK / 32);
     hipLaunchKernelGGL(append_k_mfma_kernel, dim3(grid), dim3(64), 0, a.stream, k, wk, a.n, s.KV, s.D, s.RK,
                        where, kc);
@@ -356,11 +413,11 @@ hipError_t append_enqueue(const AppendLaunch& a) {
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (a.n >= 256 && s.RV % kAppendRowsLat == 0 && K % kAppendRowsSpan == 0) {
+  if (vrows) {
     const int ttiles = (a.n + kAppendRowsTok - 1) / kAppendRowsTok;
     const int grid = ttiles * ((s.RV / kAppendRowsLat + 7) / 8) * 8;
     hipLaunchKernelGGL(append_v_rows_kernel, dim3(grid), dim3(512), 0, a.stream, v, wv, a.n, K, s.RV, where, vc);
-  } else if (a.n >= 16 && s.RV % 16 == 0 && K % (32 * kAppendVWaves) == 0) {
+  } else if (vmfma) {
     const int grid = ((s.RV / 16 + 7) / 8) * 8 * ((a.n + 15) / 16);
     hipLaunchKernelGGL(append_v_mfma_kernel, dim3(grid), dim3(kAppendVWaves * 64), 0, a.stream, v, wv, a.n, K,
                        s.RV, where, vc);
