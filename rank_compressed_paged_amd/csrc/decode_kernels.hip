@@ -547,6 +547,137 @@ upproj_valu_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
 
 // ---------------------------------------------------------------------------
 // host side
+// Few (sequence, head) pairs with d = 128 (long sequences at small batch): the
+// merge and the up-projection of one (sequence, head) in one 512-thread
+// workgroup, so Z never goes to memory and one launch with its memory round
+// trips is saved.
+//   1. The head's B_v column block is fetched first (thread t: output dims
+//      8*(t%16) .. +7, latent rows (t/16)*r_v/32 .. +r_v/32-1), so it is in
+//      flight during the merge.
+//   2. Merge as in merge_kernel<4>: four slot groups take every fourth slot,
+//      eight slots per round trip, base-2 log-sum-exp online; the groups
+//      combine through LDS into the normalised z (LDS).
+//   3. out[b, h, :] = z . B_v block: per-thread partial sums over its latent
+//      rows, reduced over the 32 row groups through LDS.
+constexpr int kMuGroups = 4;
+constexpr int kMuSlots = 8;
+constexpr int kMuD = 128;
+
+__global__ void __launch_bounds__(512)
+merge_upproj_small_kernel(const float* __restrict__ part_z, const float* __restrict__ part_ml,
+                          const int32_t* __restrict__ plan, const int32_t* __restrict__ lens,
+                          const f16* __restrict__ bv, f16* __restrict__ out, int batch, int H, int KV, int RV) {
+  __shared__ __attribute__((aligned(16))) float zl[kUpvMaxRV];
+  __shared__ __attribute__((aligned(16))) float ca[kMuGroups][kUpvMaxRV];
+  __shared__ float cm_s[kMuGroups], cl_s[kMuGroups];
+  __shared__ float red[32][kMuD + 1];
+  const int t = threadIdx.x;
+  const int h = blockIdx.x % H, b = blockIdx.x / H;
+  const int kvh = h / (H / KV);
+  const size_t ld = (size_t)KV * kMuD;
+
+  // 1. B_v rows of this thread (clamped re-reads past r_v/32 rows are unused)
+  const int n8 = (t % 16) * 8, kq = t / 16;
+  const int kpt = RV / 32;                           // r_v is a multiple of 32, at most 1024
+  half8 br[kUpvMaxRV / 32];
+#pragma unroll
+  for (int i = 0; i < kUpvMaxRV / 32; ++i)
+    br[i] = *reinterpret_cast<const half8*>(bv + (size_t)(kq * kpt + min(i, kpt - 1)) * ld + (size_t)kvh * kMuD + n8);
+
+  // 2. merge: lane li of slot group g holds latent dims 8*li .. +7
+  const int g = t / 128, li = t % 128;
+  const int d0 = li * 8;
+  const PlanView pv{plan, batch};
+  const int s0 = pv.slot_base()[b];
+  const int s1 = pv.slot_base()[b + 1];
+  const bool empty = lens[b] == 0 || s1 <= s0;       // uniform over the workgroup
+  floatx4 a0 = {}, a1 = {};
+  float M = -INFINITY, den = 0.f;
+  if (!empty) {
+    const float* ml = part_ml + (size_t)h * 2;
+    const float* zb = part_z + (size_t)h * RV + (d0 < RV ? d0 : 0);
+    const size_t zs = (size_t)H * RV;                // slot stride
+    for (int c = s0 + g; c < s1; c += kMuSlots * kMuGroups) {
+      float m[kMuSlots], l[kMuSlots];
+      floatx4 z0[kMuSlots], z1[kMuSlots];
+#pragma unroll
+      for (int u = 0; u < kMuSlots; ++u) {
+        const int sl = min(c + u * kMuGroups, s1 - 1);
+        m[u] = ml[(size_t)sl * H * 2];
+        l[u] = ml[(size_t)sl * H * 2 + 1];
+        z0[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs);
+        z1[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs + 4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      float cm = M;
+#pragma unroll
+      for (int u = 0; u < kMuSlots; ++u) {
+        m[u] = c + u * kMuGroups < s1 ? m[u] : -INFINITY;   // re-read slots weigh nothing
+        cm = fmaxf(cm, m[u]);
+      }
+      const float sc = fast_exp2(M - cm);                   // 0 while M is still -inf
+      a0 *= sc;
+      a1 *= sc;
+      den *= sc;
+#pragma unroll
+      for (int u = 0; u < kMuSlots; ++u) {
+        const float wgt = fast_exp2(m[u] - cm);
+        a0 += wgt * z0[u];
+        a1 += wgt * z1[u];
+        den += wgt * l[u];
+      }
+      M = cm;
+    }
+  }
+  *reinterpret_cast<floatx4*>(&ca[g][d0]) = a0;
+  *reinterpret_cast<floatx4*>(&ca[g][d0 + 4]) = a1;
+  if (li == 0) {
+    cm_s[g] = M;
+    cl_s[g] = den;
+  }
+  __syncthreads();
+  if (g == 0) {
+    float top = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kMuGroups; ++q) top = fmaxf(top, cm_s[q]);
+    floatx4 s0v = {}, s1v = {};
+    float dsum = 0.f;
+#pragma unroll
+    for (int q = 0; q < kMuGroups; ++q) {
+      if (cm_s[q] != -INFINITY) {                   // groups without slots hold nothing
+        const float wgt = fast_exp2(cm_s[q] - top);
+        s0v += wgt * *reinterpret_cast<const floatx4*>(&ca[q][d0]);
+        s1v += wgt * *reinterpret_cast<const floatx4*>(&ca[q][d0 + 4]);
+        dsum += wgt * cl_s[q];
+      }
+    }
+    const float inv = dsum > 0.f ? 1.f / dsum : 0.f;   // empty sequence: zero row
+    *reinterpret_cast<floatx4*>(&zl[d0]) = s0v * inv;
+    *reinterpret_cast<floatx4*>(&zl[d0 + 4]) = s1v * inv;
+  }
+  __syncthreads();
+
+  // 3. up-projection
+  float acc[8] = {};
+#pragma unroll
+  for (int i = 0; i < kUpvMaxRV / 32; ++i) {
+    if (i < kpt) {
+      const float z = zl[kq * kpt + i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += z * (float)br[i][e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[kq][n8 + e] = acc[e];
+  __syncthreads();
+  if (t < kMuD) {
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) sum += red[q][t];
+    out[((size_t)b * H + h) * kMuD + t] = (f16)sum;
+  }
+}
+
 // ---------------------------------------------------------------------------
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -658,7 +789,13 @@ hipError_t decode_enqueue(const DecodeLaunch& a) {
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
-  // 3. merge, 4. up-projection
+  // 3. merge, 4. up-projection (one launch for few (sequence, head) pairs at d = 128)
+  if ((long long)a.batch * s.H < 512 && s.D == kMuD && s.RV <= kUpvMaxRV) {
+    hipLaunchKernelGGL(merge_upproj_small_kernel, dim3(a.batch * s.H), dim3(512), 0, a.stream, pz, pml, plan,
+                       a.context_lens, static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H,
+                       s.KV, s.RV);
+    return hipGetLastError();
+  }
   err = launch_merge(s, a.batch, pz, pml, plan, a.context_lens, zf, a.stream);
   if (err != hipSuccess) return err;
   return launch_upproj(s, a.batch, zf, a.b_v, a.out, a.stream);
