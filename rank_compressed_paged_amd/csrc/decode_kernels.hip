@@ -9,6 +9,8 @@
 //                   each (range, sequence) pair leaves (max, sum, z) partials.
 //   3. merge        log-sum-exp merge of a sequence's partials -> Z [B][H][r_v].
 //   4. upproj       out[b,h] = Z[b,h] . B_v[:, h*d:(h+1)*d]  (MFMA at batch >= 16).
+// With few (sequence, head) pairs at d = 128, launches 3 and 4 are one launch
+// (merge_upproj_small) that keeps Z in LDS.
 //
 // Method: Proxima README text on wpnews ("Show HN: Proxima ..."), opening
 // description of STAR-KV (head-wise K latents, one joint V latent, compressed

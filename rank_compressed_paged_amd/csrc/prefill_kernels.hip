@@ -2,16 +2,19 @@
 //
 // A prefill call attends a chunk of new tokens per sequence (already appended
 // to the latent cache) to every cached position up to and including its own.
-// Five launches on the caller's stream:
+// Launches on the caller's stream:
 //   1. prefill_plan   one workgroup: 64-row query tiles of every chunk, the
 //                     context ranges of each tile, and the partial-state slots
 //                     of each query row;
-//   2. qproj          q~ = scale*log2(e) * B_k[g(h)] q for every query row
-//                     (shared with decode);
-//   3. prefill_attn   per (tile, context range, query head): scores on MFMA,
-//                     causal online softmax, z += P . c_v on MFMA;
-//   4. merge          log-sum-exp merge of each row's range partials (shared);
-//   5. upproj         out = Z . B_v column block (shared).
+//   (qproj            q~ = scale*log2(e) * B_k[g(h)] q for every query row,
+//                     shared with decode; only when d is not a multiple of 32 -
+//                     otherwise the attention kernel computes q~ itself)
+//   2. prefill_attn   per (tile, context range, query head): q~ of the tile,
+//                     scores on MFMA, causal online softmax, z += P . c_v on
+//                     MFMA;
+//   3. merge          log-sum-exp merge of each row's range partials (shared;
+//                     skipped when every row fits one range);
+//   4. upproj         out = Z . B_v column block (shared).
 //
 // Method: Proxima README text on wpnews ("Show HN: Proxima ..."), opening
 // description of STAR-KV (head-wise K latents, one joint V latent, compressed
@@ -28,15 +31,19 @@
 //
 // Per 16-token block:
 //   waves 0-3   S[16 rows x 16 tokens] = q~ . c_k^T on 16x16x32 MFMA (q~ as
-//               fp16 high + low parts, B fragment = one 16-byte load of the
-//               token-major K block), causal mask, online softmax with lazy
-//               rescale; P (fp16) and the rows' rescale factors go to LDS;
+//               fp16 high + low parts, B fragment = one 16-byte LDS read of the
+//               block's K in an LDS ring), causal mask, online softmax with
+//               lazy rescale; P (fp16) and the rows' rescale factors go to LDS;
 //   all waves   z[64 rows x own 128 dims] += P . c_v on 32x32x16 MFMA (B
-//               fragment = one 16-byte load of the dim-major V block).
+//               fragment = one 16-byte load of the dim-major V block, three
+//               blocks held in registers).
 // Scores run two blocks ahead of the accumulation (three P buffers in LDS):
 // the score MFMAs of block i+2 enter each SIMD's MFMA pipe before block i's z
 // MFMAs, and their softmax runs while those drain; one barrier per block.
-// K and V use plain loads: every block is re-read by the other heads'
+// K blocks reach LDS through direct global-to-LDS loads issued by wave 4
+// (an 8-stage ring, rows swizzled so the fragment reads do not conflict);
+// V blocks are loaded into registers three blocks ahead of their MFMAs.  Both
+// use ordinary cached loads: every block is re-read by the other heads'
 // workgroups on the same XCD and should stay in its L2.
 
 #include <math.h>
