@@ -176,6 +176,23 @@ def test_ranges_spanning_many_sequences():
     check(got[live], ref[live], what="many short sequences")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_single_long_sequence_every_range(d):
+    """One sequence of 40,000 tokens (2,500 blocks): every workgroup range lies
+    inside it, so each (sequence, head) row merges ~250 partials.  d = 128
+    takes the fused small merge + up-projection, d = 64 the separate merge
+    (four slot groups) and VALU up-projection."""
+    dev = gpu()
+    lens = np.array([40000])
+    case = synth.make_case(470 + d, 1, 32, d, 64, 1024, lens)
+    scale = 1.0 / math.sqrt(d)
+    log(f"single sequence of {lens[0]} tokens, d={d}")
+    out = decode_gpu(to_dev(case, dev), lens, scale, dev)
+    ref = oracle.decode(case["q"], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
+                        case["block_tables"], lens, scale)
+    check(out, ref, what=f"single long sequence d={d}")
+
+
 # ------------------------------------------------------------- full sizes
 @pytest.fixture(scope="module")
 def config3():
