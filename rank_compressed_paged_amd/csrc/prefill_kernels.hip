@@ -40,11 +40,12 @@
 // Scores run two blocks ahead of the accumulation (three P buffers in LDS):
 // the score MFMAs of block i+2 enter each SIMD's MFMA pipe before block i's z
 // MFMAs, and their softmax runs while those drain; one barrier per block.
-// K blocks reach LDS through direct global-to-LDS loads issued by wave 4
-// (an 8-stage ring, rows swizzled so the fragment reads do not conflict);
-// V blocks are loaded into registers three blocks ahead of their MFMAs.  Both
-// use ordinary cached loads: every block is re-read by the other heads'
-// workgroups on the same XCD and should stay in its L2.
+// K blocks reach a four-stage LDS ring through the four non-scorer waves (a
+// quarter of each block per wave, loaded three steps ahead and stored to LDS
+// with rows swizzled so the fragment reads do not conflict); V blocks are
+// loaded into registers three blocks ahead of their MFMAs.  Both use ordinary
+// cached loads: every block is re-read by the other heads' workgroups on the
+// same XCD and should stay in its L2.
 
 #include <math.h>
 
@@ -182,9 +183,12 @@ struct PfCfg {
   static constexpr int KS = RK / 32;               // 16x16x32 k-steps of a score tile
   static constexpr int TPW = RV / 32 / kPfWaves;   // 32-dim V tiles per wave
   static constexpr int VB = 3;                     // V blocks in registers (held or in flight)
-  static constexpr int KSTG = 8;                   // K ring stages in LDS
+  static constexpr int KSTG = 4;                   // K ring stages in LDS
   static constexpr int CPR = RK / 8;               // 16-byte chunks per token row of a K block
-  static constexpr int KI = kBlock * CPR / 64;     // wave instructions per K block (1 KiB each)
+  // K of a block is loaded by the four non-scorer waves, one piece per lane:
+  // 2*16*RK bytes / 256 lanes = RK/8 bytes, 16 pieces per token row
+  using KPiece = std::conditional_t<RK == 64, uint2, uint32_t>;
+  static constexpr int PPC = 16 / (int)sizeof(KPiece);   // pieces per 16-byte chunk
   static_assert(RK % 32 == 0 && KS >= 1 && KS <= 2, "r_k in {32, 64}");
   static_assert(RV % (32 * kPfWaves) == 0 && TPW >= 1 && TPW <= 4, "r_v in {256, 512, 768, 1024}");
 };
@@ -192,18 +196,15 @@ struct PfCfg {
 template <int N>
 using PfIC = std::integral_constant<int, N>;
 
-// Workgroup barrier for LDS data written with ds_write (waited here) or by
-// direct global-to-LDS loads that the writing wave has already waited for.
-// Unlike __syncthreads() it does not wait for the V ring loads still in
+// Workgroup barrier for LDS data written with ds_write (waited here).
+// Unlike __syncthreads() it does not wait for the K and V loads still in
 // flight; the "memory" clobber keeps the compiler from moving LDS accesses
-// across it.
+// across it.  The scorer and loader loops use differently spelled copies so
+// that the compiler cannot merge their identical loop tails into shared
+// blocks, whose merged wait bookkeeping would over-wait in both loops.
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at
-// byte 16*l from lds (wave-uniform), no VGPRs held; counted by the
-// vector-memory counter like any load.
-__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+__device__ __forceinline__ void barrier_lds_b() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier ; loader" ::: "memory");
 }
 
 // max over the 16 lanes of a DPP row (lanes 16g .. 16g+15)
@@ -230,9 +231,9 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
   __shared__ float a_lds[3][kPfRows];
   __shared__ __attribute__((aligned(16))) int flag_lds[3][4];
   __shared__ int slot_lds[kPfRows];
-  // K ring of eight stages, one block (16 tokens x r_k of the workgroup's
-  // key head) each, filled by direct global-to-LDS loads of wave 4.  Chunk c
-  // (16 bytes) of token t sits at slot t*CPR + (c ^ swz(t)), so the scorer
+  // K ring of four stages, one block (16 tokens x r_k of the workgroup's
+  // key head) each, written by the four non-scorer waves.  Chunk c (16
+  // bytes) of token t sits at slot t*CPR + (c ^ swz(t)), so the scorer
   // waves' fragment reads (16 tokens at one chunk) spread over the banks.
   __shared__ __attribute__((aligned(16))) f16 k_lds[C::KSTG][kBlock * RK];
   __shared__ float lrow_lds[kPfRows];      // row sums, for the single-range direct write
@@ -341,34 +342,31 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
     // re-read by the other heads' workgroups on this XCD and must stay in L2
     // (non-temporal loads cost 25% at 4 x 512 rows over 8192 positions).
     const f16* vbase = vpool + ((size_t)(w * C::TPW * 32 + c32)) * kBlock + 8 * half_;
-    // K of a block -> ring stage ks8 (wave 4): LDS slot j*64 + lane takes the
-    // chunk that the swizzle puts there
+    // K of a block, loaded by the non-scorer waves (wave w-4 takes pieces
+    // 64*(w-4) .. +63, 512 or 256 contiguous bytes): piece g = token g/16,
+    // piece g%16 of its row; stored to its swizzled place in a ring stage
+    // two steps after its load.  Plain loads like V, so a wave's in-order
+    // waits count one kind of load.
+    using KP = typename C::KPiece;
+    const int kg = (w - 4) * 64 + lane;
+    const int kt = kg / 16, kc = (kg % 16) / C::PPC;
     auto swz = [](int t) { return (t ^ (t / C::CPR)) % C::CPR; };
-    auto load_k = [&](int ks8, int phys) __attribute__((always_inline)) {
-      const f16* blk = kpool + ((size_t)phys * HKV + kvh) * kBlock * RK;
-#pragma unroll
-      for (int j = 0; j < C::KI; ++j) {
-        const int slot = j * 64 + lane;
-        const int t = slot / C::CPR, c = (slot % C::CPR) ^ swz(slot / C::CPR);
-        load_lds16(blk + t * RK + c * 8, &k_lds[ks8][j * 64 * 8]);
-      }
+    const int k_dst = (kt * C::CPR + (kc ^ swz(kt))) * 8 + (kg % C::PPC) * (int)(sizeof(KP) / 2);
+    auto load_k = [&](int phys) __attribute__((always_inline)) -> KP {
+      return reinterpret_cast<const KP*>(kpool + ((size_t)phys * HKV + kvh) * kBlock * RK)[kg];
+    };
+    auto store_k = [&](int stage, KP v) __attribute__((always_inline)) {
+      *reinterpret_cast<KP*>(&k_lds[stage][k_dst]) = v;
     };
     // V of a block -> registers: the B fragments of the wave's own 128 latent
     // dims (tile t: latent dim c32 of the tile, tokens 8*half_ .. +7), three
-    // blocks held or in flight.  The scorer waves load nothing else in the
-    // block loop, so their in-order waits for V are never held up by K.
+    // blocks held or in flight.
     half8 vb[C::VB][C::TPW];
     auto load_v = [&](auto bufc, int phys) __attribute__((always_inline)) {
       constexpr int BUF = decltype(bufc)::value;
       const f16* p = vbase + (size_t)phys * RV * kBlock;
 #pragma unroll
       for (int t = 0; t < C::TPW; ++t) vb[BUF][t] = *reinterpret_cast<const half8*>(p + t * 32 * kBlock);
-    };
-    // wave 4: K of block ib+3 has landed once the V of block ib+1 and the K
-    // and V of the two later blocks are all that is outstanding
-    auto wait_k4 = [&]() {
-      constexpr int n = C::TPW + 2 * (C::KI + C::TPW);
-      __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
     };
 
     floatx16 acc[2][C::TPW];
@@ -385,15 +383,15 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
       l_part[i] = 0.f;
     }
 
-    // scores of the block in K ring stage ks8 (scorer waves): B fragment of
+    // scores of the block in K ring stage ks4 (scorer waves): B fragment of
     // k-step ks = token l%16, chunk 4*ks + l/16
-    auto score_mfma = [&](int ks8) __attribute__((always_inline)) -> floatx4 {
+    auto score_mfma = [&](int ks4) __attribute__((always_inline)) -> floatx4 {
       const int t = lane & 15;
       floatx4 sc{};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const int c = 4 * ks + (lane >> 4);
-        const half8 kf = *reinterpret_cast<const half8*>(&k_lds[ks8][(t * C::CPR + (c ^ swz(t))) * 8]);
+        const half8 kf = *reinterpret_cast<const half8*>(&k_lds[ks4][(t * C::CPR + (c ^ swz(t))) * 8]);
         sc = mfma16x16x32(qa_lds[w][ks][0][lane], kf, sc);
         sc = mfma16x16x32(qa_lds[w][ks][1][lane], kf, sc);
       }
@@ -469,45 +467,29 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
         for (int t = 0; t < C::TPW; ++t) acc[rt][t] = mfma32x32x16(pa[rt], vb[BUF][t], acc[rt][t]);
     };
 
-    // K of block b sits in LDS ring stage b % 8, V in vb[b % 3], P in LDS
+    // K of block b sits in LDS ring stage b % 4, V in vb[b % 3], P in LDS
     // buffer b % 3.  Scores run two blocks ahead of the z accumulation.  Step
-    // ib: wave 4 loads K of block ib+5, every wave loads its V of block ib+3
-    // into the registers block ib has just left, so both have three steps to
-    // arrive; the scorer waves put the scores of block ib+2 into the MFMA pipe
-    // ahead of block ib's z MFMAs and run its softmax while those drain; wave
-    // 4 waits for K of block ib+3, which the barrier then publishes.  Loads
-    // past the range re-read block 0 (always in range), so every path of a
-    // wave issues the same loads and the in-order wait counts stay exact.
-    // Both roles pass the same number of barriers.
+    // ib: every wave loads its V of block ib+3 into the registers block ib has
+    // just left; the non-scorer waves load their pieces of K of block ib+5
+    // and store those of block ib+3 (loaded two steps before) to the ring, so
+    // both streams have three steps to arrive.  The scorer waves put the
+    // scores of block ib+2 into the MFMA pipe ahead of block ib's z MFMAs and
+    // run its softmax while those drain.  Loads past the range re-read block
+    // 0 (always in range), so every path of a wave issues the same loads and
+    // the in-order wait counts stay exact.  Both roles pass the same number of
+    // barriers: two in the prologue, one per step.
     const int phys0 = table[0];
     auto tab = [&](int b) { return b < nblk ? table[b] : phys0; };
-    if (w == 4) {
-      load_k(0, phys0);
-      load_k(1, tab(1));
-      load_k(2, tab(2));
-    }
-    load_v(PfIC<0>{}, phys0);
-    if (w == 4) load_k(3, tab(3));
-    load_v(PfIC<1>{}, tab(1));
-    if (w == 4) load_k(4, tab(4));
-    load_v(PfIC<2>{}, tab(2));
-    if (w == 4) {                            // K of blocks 0, 1
-      constexpr int n = 3 * C::KI + 3 * C::TPW;
-      __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-    }
-    barrier_lds();
     if (scorer) {
+      load_v(PfIC<0>{}, phys0);
+      load_v(PfIC<1>{}, tab(1));
+      load_v(PfIC<2>{}, tab(2));
+      barrier_lds();                         // K of blocks 0, 1 stored
       softmax(0, score_mfma(0), 0);
       if (nblk > 1) softmax(1, score_mfma(1), 1);
-    }
-    if (w == 4) {                            // K of block 2
-      constexpr int n = 2 * C::KI + 3 * C::TPW;
-      __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-    }
-    barrier_lds();
-    if (scorer) {
+      barrier_lds();                         // K of block 2 stored
       auto step = [&](auto bufc, int ib) __attribute__((always_inline)) {
-        const floatx4 sc = score_mfma((ib + 2) & 7);   // block ib+2 (a spare block past the end)
+        const floatx4 sc = score_mfma((ib + 2) & 3);   // block ib+2 (a spare block past the end)
         accumulate(bufc, decltype(bufc)::value, ib);
         load_v(bufc, tab(ib + 3));
         if (ib + 2 < nblk) softmax((decltype(bufc)::value + 2) % 3, sc, ib + 2);
@@ -522,12 +504,30 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
       if (ib < nblk) step(PfIC<0>{}, ib);
       if (ib + 1 < nblk) step(PfIC<1>{}, ib + 1);
     } else {
+      // K of block b in flight in kr[b % 3] (blocks 3, 4 on entry).  The
+      // loads are issued in the loop's own order (K of block b+3 ahead of V of
+      // block b+1), so the compiler's wait counts at the loop entry match
+      // those of its back edge.
+      KP kr[3];
+      const KP k0 = load_k(phys0), k1 = load_k(tab(1));
+      kr[2] = load_k(tab(2));
+      load_v(PfIC<0>{}, phys0);
+      kr[0] = load_k(tab(3));
+      load_v(PfIC<1>{}, tab(1));
+      kr[1] = load_k(tab(4));
+      load_v(PfIC<2>{}, tab(2));
+      store_k(0, k0);
+      store_k(1, k1);
+      barrier_lds_b();
+      store_k(2, kr[2]);
+      barrier_lds_b();
       auto step = [&](auto bufc, int ib) __attribute__((always_inline)) {
-        if (w == 4) load_k((ib + 5) & 7, tab(ib + 5));
-        accumulate(bufc, decltype(bufc)::value, ib);
+        constexpr int BUF = decltype(bufc)::value;
+        kr[(BUF + 2) % 3] = load_k(tab(ib + 5));
+        accumulate(bufc, BUF, ib);
         load_v(bufc, tab(ib + 3));
-        if (w == 4) wait_k4();               // K of block ib+3
-        barrier_lds();
+        store_k((ib + 3) & 3, kr[BUF]);      // K of block ib+3
+        barrier_lds_b();
       };
       int ib = 0;
       for (; ib + 2 < nblk; ib += 3) {
