@@ -196,6 +196,8 @@ struct PfCfg {
 template <int N>
 using PfIC = std::integral_constant<int, N>;
 
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+
 // Workgroup barrier for LDS data written with ds_write (waited here).
 // Unlike __syncthreads() it does not wait for the K and V loads still in
 // flight; the "memory" clobber keeps the compiler from moving LDS accesses
@@ -205,15 +207,6 @@ using PfIC = std::integral_constant<int, N>;
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void barrier_lds_b() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier ; loader" ::: "memory");
-}
-
-// max over the 16 lanes of a DPP row (lanes 16g .. 16g+15)
-__device__ __forceinline__ float group_max16(float x) {
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)));
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)));
-  return x;
 }
 
 template <int RK, int RV>
@@ -374,66 +367,68 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int t = 0; t < C::TPW; ++t) acc[rt][t] = floatx16{};
-    // running max of each of the lane's 4 rows, and the lane's share of the
-    // row sums (one token per lane; reduced over the 16 lanes at the end)
-    float m_run[4], l_part[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m_run[i] = -INFINITY;
-      l_part[i] = 0.f;
-    }
+    // Scores are taken transposed (S^T = K q~^T), so lane l of a scorer wave
+    // holds row w*16 + l%16 and tokens 4*(l/16) .. +3 of a block: the four
+    // lanes l, l^16, l^32, l^48 share a row.  Running max of the lane's row
+    // (equal in those four lanes) and the lane's share of its row sum
+    // (added over the four lanes at the end).
+    const int srow = w * 16 + (lane & 15);
+    const int slast = srow < nrows ? pos0 + srow : -1;      // last position the row sees
+    float m_run = -INFINITY, l_part = 0.f;
 
-    // scores of the block in K ring stage ks4 (scorer waves): B fragment of
-    // k-step ks = token l%16, chunk 4*ks + l/16
+    // scores of the block in K ring stage ks4 (scorer waves): A fragment of
+    // k-step ks = token l%16, chunk 4*ks + l/16; B = q~ of row l%16.  The hi
+    // and lo parts of q~ accumulate in two independent chains.
     auto score_mfma = [&](int ks4) __attribute__((always_inline)) -> floatx4 {
       const int t = lane & 15;
-      floatx4 sc{};
+      floatx4 sh{}, sl{};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const int c = 4 * ks + (lane >> 4);
         const half8 kf = *reinterpret_cast<const half8*>(&k_lds[ks4][(t * C::CPR + (c ^ swz(t))) * 8]);
-        sc = mfma16x16x32(qa_lds[w][ks][0][lane], kf, sc);
-        sc = mfma16x16x32(qa_lds[w][ks][1][lane], kf, sc);
+        sh = mfma16x16x32(kf, qa_lds[w][ks][0][lane], sh);
+        sl = mfma16x16x32(kf, qa_lds[w][ks][1][lane], sl);
       }
-      return sc;
+      return sh + sl;
     };
     // causal mask and online softmax of block ib (scorer waves) -> P, rescale
     // factors and flag in LDS buffer PB
     auto softmax = [&](int PB, const floatx4 sc, int ib) __attribute__((always_inline)) {
-      const int tpos = (blk_lo + ib) * kBlock + (lane & 15);
+      const int tpos = (blk_lo + ib) * kBlock + 4 * (lane >> 4);   // position of register 0's token
       float s[4];
       bool exceed = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rrow = w * 16 + 4 * (lane >> 4) + i;      // register i: row 4*(l/16)+i, token l%16
-        const bool valid = rrow < nrows && tpos <= pos0 + rrow;
-        s[i] = valid ? sc[i] : -INFINITY;
-        exceed |= s[i] > m_run[i] + tau;
+        s[i] = tpos + i <= slast ? sc[i] : -INFINITY;
+        exceed |= s[i] > m_run + tau;
       }
       // Lazy rescale: while no score beats its row's running max by more than
       // tau, P = exp2(s - m) <= 2^tau needs no row reduction at all.
       const bool rescale = __any(exceed);
       if (rescale) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rrow = w * 16 + 4 * (lane >> 4) + i;
-          const float bm = group_max16(s[i]);
-          const bool need = bm > m_run[i] + tau;
-          const float m_new = need ? bm : m_run[i];
-          const float alpha = need ? fast_exp2(m_run[i] - m_new) : 1.f;
-          l_part[i] *= alpha;
-          m_run[i] = m_new;
-          if ((lane & 15) == 0) a_lds[PB][rrow] = alpha;
-        }
+        float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const bool need = bm > m_run + tau;
+        const float m_new = need ? bm : m_run;
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+        l_part *= alpha;
+        m_run = m_new;
+        if (lane < 16) a_lds[PB][srow] = alpha;
       }
+      half4 p4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rrow = w * 16 + 4 * (lane >> 4) + i;
-        const f16 p16 = s[i] != -INFINITY ? (f16)fast_exp2(s[i] - m_run[i]) : (f16)0.f;
-        l_part[i] += (float)p16;
-        p_lds[PB][rrow][lane & 15] = p16;
+        p4[i] = s[i] != -INFINITY ? (f16)fast_exp2(s[i] - m_run) : (f16)0.f;
+        l_part += (float)p4[i];
       }
+      *reinterpret_cast<half4*>(&p_lds[PB][srow][4 * (lane >> 4)]) = p4;
       if (lane == 0) flag_lds[PB][w] = rescale ? 1 : 0;
+    };
+    // the row sum of the lane's row (over its four lanes)
+    auto row_sum = [&]() {
+      const float x = l_part + __shfl_xor(l_part, 16);
+      return x + __shfl_xor(x, 32);
     };
 
     // z += P . c_v of block ib (all waves): V in vb[BUF], P in LDS buffer PB
@@ -478,8 +473,12 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
     // 0 (always in range), so every path of a wave issues the same loads and
     // the in-order wait counts stay exact.  Both roles pass the same number of
     // barriers: two in the prologue, one per step.
+    // Block table entries are read one step before the loads that use them
+    // (pv: V of block ib+3, pk: K of block ib+5), so no step waits for a
+    // scalar load.
     const int phys0 = table[0];
     auto tab = [&](int b) { return b < nblk ? table[b] : phys0; };
+    int pv = tab(3);
     if (scorer) {
       load_v(PfIC<0>{}, phys0);
       load_v(PfIC<1>{}, tab(1));
@@ -489,9 +488,11 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
       if (nblk > 1) softmax(1, score_mfma(1), 1);
       barrier_lds();                         // K of block 2 stored
       auto step = [&](auto bufc, int ib) __attribute__((always_inline)) {
+        const int pv_now = pv;
+        pv = tab(ib + 4);
         const floatx4 sc = score_mfma((ib + 2) & 3);   // block ib+2 (a spare block past the end)
         accumulate(bufc, decltype(bufc)::value, ib);
-        load_v(bufc, tab(ib + 3));
+        load_v(bufc, pv_now);
         if (ib + 2 < nblk) softmax((decltype(bufc)::value + 2) % 3, sc, ib + 2);
         barrier_lds();
       };
@@ -521,11 +522,15 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
       barrier_lds_b();
       store_k(2, kr[2]);
       barrier_lds_b();
+      int pk = tab(5);
       auto step = [&](auto bufc, int ib) __attribute__((always_inline)) {
         constexpr int BUF = decltype(bufc)::value;
-        kr[(BUF + 2) % 3] = load_k(tab(ib + 5));
+        const int pv_now = pv, pk_now = pk;
+        pv = tab(ib + 4);
+        pk = tab(ib + 6);
+        kr[(BUF + 2) % 3] = load_k(pk_now);
         accumulate(bufc, BUF, ib);
-        load_v(bufc, tab(ib + 3));
+        load_v(bufc, pv_now);
         store_k((ib + 3) & 3, kr[BUF]);      // K of block ib+3
         barrier_lds_b();
       };
@@ -543,11 +548,8 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
       // Every row's context fits one range: write z / l straight into the
       // merged buffer (no partial state, no merge pass).
       if (scorer) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float l_row = group_sum<16>(l_part[i]);
-          if ((lane & 15) == 0) lrow_lds[w * 16 + 4 * (lane >> 4) + i] = l_row;
-        }
+        const float l_row = row_sum();
+        if (lane < 16) lrow_lds[srow] = l_row;
       }
       __syncthreads();
 #pragma unroll
@@ -568,15 +570,11 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
 
     // partial state of every row whose context reaches this range
     if (scorer) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float l_row = group_sum<16>(l_part[i]);
-        const int rrow = w * 16 + 4 * (lane >> 4) + i;
-        const int sl = slot_lds[rrow];
-        if ((lane & 15) == 0 && sl >= 0) {
-          part_ml[((size_t)sl * H + h) * 2 + 0] = m_run[i];
-          part_ml[((size_t)sl * H + h) * 2 + 1] = l_row;
-        }
+      const float l_row = row_sum();
+      const int sl = slot_lds[srow];
+      if (lane < 16 && sl >= 0) {
+        part_ml[((size_t)sl * H + h) * 2 + 0] = m_run;
+        part_ml[((size_t)sl * H + h) * 2 + 1] = l_row;
       }
     }
 #pragma unroll
