@@ -197,6 +197,7 @@ template <int N>
 using PfIC = std::integral_constant<int, N>;
 
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 
 // Workgroup barrier for LDS data written with ds_write (waited here).
 // Unlike __syncthreads() it does not wait for the K and V loads still in
@@ -395,35 +396,49 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
     // factors and flag in LDS buffer PB
     auto softmax = [&](int PB, const floatx4 sc, int ib) __attribute__((always_inline)) {
       const int tpos = (blk_lo + ib) * kBlock + 4 * (lane >> 4);   // position of register 0's token
-      float s[4];
-      bool exceed = false;
+      // The causal mask only bites on the blocks that reach the wave's own
+      // rows (and on a short last tile); every other block is seen whole by
+      // all 16 rows (uniform over the wave).
+      const bool whole = (blk_lo + ib + 1) * kBlock - 1 <= pos0 + w * 16 && w * 16 + 16 <= nrows;
+      auto body = [&](auto maskc) __attribute__((always_inline)) {
+        constexpr bool masked = decltype(maskc)::value;
+        float s[4];
+        bool exceed = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[i] = tpos + i <= slast ? sc[i] : -INFINITY;
-        exceed |= s[i] > m_run + tau;
-      }
-      // Lazy rescale: while no score beats its row's running max by more than
-      // tau, P = exp2(s - m) <= 2^tau needs no row reduction at all.
-      const bool rescale = __any(exceed);
-      if (rescale) {
-        float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const bool need = bm > m_run + tau;
-        const float m_new = need ? bm : m_run;
-        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-        l_part *= alpha;
-        m_run = m_new;
-        if (lane < 16) a_lds[PB][srow] = alpha;
-      }
-      half4 p4;
+        for (int i = 0; i < 4; ++i) {
+          s[i] = !masked || tpos + i <= slast ? sc[i] : -INFINITY;
+          exceed |= s[i] > m_run + tau;
+        }
+        // Lazy rescale: while no score beats its row's running max by more
+        // than tau, P = exp2(s - m) <= 2^tau needs no row reduction at all.
+        const bool rescale = __any(exceed);
+        if (rescale) {
+          float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+          bm = fmaxf(bm, __shfl_xor(bm, 16));
+          bm = fmaxf(bm, __shfl_xor(bm, 32));
+          const bool need = bm > m_run + tau;
+          const float m_new = need ? bm : m_run;
+          const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+          l_part *= alpha;
+          m_run = m_new;
+          if (lane < 16) a_lds[PB][srow] = alpha;
+        }
+        // (unmasked, every score is finite, and so is m_run after the first
+        // block: a finite score beats the initial -inf by more than tau)
+        half4 p4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p4[i] = s[i] != -INFINITY ? (f16)fast_exp2(s[i] - m_run) : (f16)0.f;
-        l_part += (float)p4[i];
-      }
-      *reinterpret_cast<half4*>(&p_lds[PB][srow][4 * (lane >> 4)]) = p4;
-      if (lane == 0) flag_lds[PB][w] = rescale ? 1 : 0;
+        for (int i = 0; i < 4; ++i)
+          p4[i] = !masked || s[i] != -INFINITY ? (f16)fast_exp2(s[i] - m_run) : (f16)0.f;
+        // row sum of the rounded P, as the MFMA sees it
+        l_part = __builtin_amdgcn_fdot2(half2{p4[0], p4[1]}, half2{1, 1}, l_part, false);
+        l_part = __builtin_amdgcn_fdot2(half2{p4[2], p4[3]}, half2{1, 1}, l_part, false);
+        *reinterpret_cast<half4*>(&p_lds[PB][srow][4 * (lane >> 4)]) = p4;
+        if (lane == 0) flag_lds[PB][w] = rescale ? 1 : 0;
+      };
+      if (whole)
+        body(std::false_type{});
+      else
+        body(std::true_type{});
     };
     // the row sum of the lane's row (over its four lanes)
     auto row_sum = [&]() {
@@ -491,9 +506,9 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
         const int pv_now = pv;
         pv = tab(ib + 4);
         const floatx4 sc = score_mfma((ib + 2) & 3);   // block ib+2 (a spare block past the end)
+        if (ib + 2 < nblk) softmax((decltype(bufc)::value + 2) % 3, sc, ib + 2);
         accumulate(bufc, decltype(bufc)::value, ib);
         load_v(bufc, pv_now);
-        if (ib + 2 < nblk) softmax((decltype(bufc)::value + 2) % 3, sc, ib + 2);
         barrier_lds();
       };
       int ib = 0;
