@@ -231,8 +231,6 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
   // waves' fragment reads (16 tokens at one chunk) spread over the banks.
   __shared__ __attribute__((aligned(16))) f16 k_lds[C::KSTG][kBlock * RK];
   __shared__ float lrow_lds[kPfRows];      // row sums, for the single-range direct write
-  // score A operands of the scorer waves (each lane reads back only its own)
-  __shared__ half8 qa_lds[4][C::KS][2][64];
   // q~ of a scorer wave's 16 rows, from its MFMA result layout to the A layout
   __shared__ __attribute__((aligned(16))) float qf_lds[4][16][RK + 4];
 
@@ -284,6 +282,9 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
     // score operands: lane l of scorer wave w owns tile row w*16 + l%16 and
     // latent dims 8*(l/16) .. +7 of every 32-dim k-step; q~ as fp16 high +
     // low parts (x - hi is exact in fp32, so hi + lo keeps ~22 bits)
+    // q~ of the lane's row (score B operands of the scorer waves) as fp16 high
+    // and low parts, held in registers for the whole unit
+    half8 qh[C::KS], ql[C::KS];
     if (scorer) {
       const int rr = w * 16 + (lane & 15);
       const bool live = rr < nrows;
@@ -327,8 +328,8 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
             lo8[e] = (f16)(v - (float)hi8[e]);
           }
         }
-        qa_lds[w][ks][0][lane] = hi8;
-        qa_lds[w][ks][1][lane] = lo8;
+        qh[ks] = hi8;
+        ql[ks] = lo8;
       }
     }
 
@@ -387,8 +388,8 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
       for (int ks = 0; ks < C::KS; ++ks) {
         const int c = 4 * ks + (lane >> 4);
         const half8 kf = *reinterpret_cast<const half8*>(&k_lds[ks4][(t * C::CPR + (c ^ swz(t))) * 8]);
-        sh = mfma16x16x32(kf, qa_lds[w][ks][0][lane], sh);
-        sl = mfma16x16x32(kf, qa_lds[w][ks][1][lane], sl);
+        sh = mfma16x16x32(kf, qh[ks], sh);
+        sl = mfma16x16x32(kf, ql[ks], sl);
       }
       return sh + sl;
     };
