@@ -96,11 +96,11 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const PlanView pv{plan, batch};
-  const RangeSplit split = pv.split();
+  const int W = pv.W();
   const int total = pv.total();
-  const int start = split.start(blockIdx.x);
+  const int start = blockIdx.x * W;
   if (start >= total) return;
-  const int end = min(split.stop(blockIdx.x), total);
+  const int end = min(start + W, total);
   const int32_t* __restrict__ prefix = pv.prefix();
   const int32_t* __restrict__ slot_base = pv.slot_base();
 
@@ -280,7 +280,7 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     const int cphys = phys_of(cur);
     if (seg_first) {
       seq_len = context_lens[cur.b];
-      slot = slot_base[cur.b] + ((int)blockIdx.x - split.owner(cur.lo));
+      slot = slot_base[cur.b] + ((int)blockIdx.x - cur.lo / W);
       if (cur.b - b_first < QCAP) {
         qcur = q_lds[cur.b - b_first];
       } else {

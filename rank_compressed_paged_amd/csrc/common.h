@@ -89,32 +89,15 @@ __device__ __forceinline__ float fast_exp2(float x) {
 //   [0] W  blocks per attention workgroup   [1] total blocks in the batch
 //   [2 .. 2+B]        prefix[b]: first global block of sequence b (prefix[B] = total)
 //   [3+B .. 3+2B]     slot_base[b]: first partial-state slot of sequence b
-// Block ranges of the attention workgroups.  Workgroups run in pairs over 2W
-// blocks each: 2p (dispatched to an even XCD) takes the first W + d, 2p+1 (an
-// odd XCD) the rest.  On the MI355X parts measured, workgroups on odd XCDs
-// stream the latents about 6 % slower than those on even ones, consistently
-// across runs and whatever data they read; d moves a share of the work to the
-// faster ones.
-struct RangeSplit {
-  int W, d;
-  __device__ int start(int g) const { return (g >> 1) * 2 * W + ((g & 1) ? W + d : 0); }
-  __device__ int stop(int g) const { return (g >> 1) * 2 * W + ((g & 1) ? 2 * W : W + d); }
-  // workgroup whose range holds block x
-  __device__ int owner(int x) const {
-    const int pr = x / (2 * W);
-    return 2 * pr + (x - pr * 2 * W >= W + d ? 1 : 0);
-  }
-};
-
 struct PlanView {
   const int32_t* p;
   int batch;
-  __device__ RangeSplit split() const { return RangeSplit{p[0], p[2]}; }
+  __device__ int W() const { return p[0]; }
   __device__ int total() const { return p[1]; }
-  __device__ const int32_t* prefix() const { return p + 3; }
-  __device__ const int32_t* slot_base() const { return p + 4 + batch; }
+  __device__ const int32_t* prefix() const { return p + 2; }
+  __device__ const int32_t* slot_base() const { return p + 3 + batch; }
   // sequence holding the first block of each attention workgroup's range
-  __device__ const int32_t* first_seq() const { return p + 5 + 2 * batch; }
+  __device__ const int32_t* first_seq() const { return p + 4 + 2 * batch; }
 };
 
 }  // namespace starkv

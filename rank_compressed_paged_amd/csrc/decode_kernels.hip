@@ -29,8 +29,6 @@ namespace starkv {
 // ---------------------------------------------------------------------------
 
 constexpr int kPlanThreads = 256;
-// the even workgroup of a pair takes W + W / kEvenSurplus blocks (RangeSplit)
-constexpr int kEvenSurplus = 25;
 
 __device__ int block_inclusive_scan(int v, int* sh) {
   const int tid = threadIdx.x;
@@ -45,8 +43,7 @@ __device__ int block_inclusive_scan(int v, int* sh) {
   return sh[tid];
 }
 
-// Split of the batch's blocks over `grid` workgroups (RangeSplit: pairs of
-// workgroups over 2W blocks, the even one taking W + d).  prefix[b] is the
+// Equal split of the batch's blocks over `grid` workgroups.  prefix[b] is the
 // first global block of sequence b; a sequence spanning workgroups g0..g1 owns
 // partial slots slot_base[b] .. slot_base[b] + (g1 - g0); first[g] is the
 // (non-empty) sequence holding workgroup g's first block.
@@ -54,9 +51,9 @@ __device__ void build_plan(const int32_t* __restrict__ lens, int batch, int grid
                            int32_t* __restrict__ plan) {
   __shared__ int sh[kPlanThreads];
   const int tid = threadIdx.x;
-  int32_t* prefix = plan + 3;
-  int32_t* sbase = plan + 4 + batch;
-  int32_t* first = plan + 5 + 2 * batch;
+  int32_t* prefix = plan + 2;
+  int32_t* sbase = plan + 3 + batch;
+  int32_t* first = plan + 4 + 2 * batch;
   int carry = 0;
   for (int base = 0; base < batch; base += kPlanThreads) {
     const int i = base + tid;
@@ -69,7 +66,6 @@ __device__ void build_plan(const int32_t* __restrict__ lens, int batch, int grid
   }
   const int total = carry;
   const int W = max(1, (total + grid - 1) / grid);
-  const RangeSplit split{W, W / kEvenSurplus};
   int carry1 = 0, carry2 = 0;
   for (int base = 0; base < batch; base += kPlanThreads) {
     const int i = base + tid;
@@ -79,22 +75,20 @@ __device__ void build_plan(const int32_t* __restrict__ lens, int batch, int grid
     __syncthreads();
     const int incl = carry1 + x;
     const int excl = incl - v;
-    const int np = (v > 0) ? (split.owner(incl - 1) - split.owner(excl) + 1) : 0;
+    const int np = (v > 0) ? ((incl - 1) / W - excl / W + 1) : 0;
     const int y = block_inclusive_scan(np, sh);
     const int chunk2 = sh[kPlanThreads - 1];
     if (i < batch) sbase[i + 1] = carry2 + y;
-    // ranges starting inside this sequence: start(g) in [excl, incl)
+    // ranges starting inside this sequence: g*W in [excl, incl), g < grid
     if (i < batch && v > 0)
-      for (int g = split.owner(excl); g < grid && split.start(g) < incl; ++g)
-        if (split.start(g) >= excl) first[g] = i;
+      for (int g = (excl + W - 1) / W; g * W < incl; ++g) first[g] = i;
     carry1 += chunk1;
     carry2 += chunk2;
     __syncthreads();
   }
   if (tid == 0) {
-    plan[0] = split.W;
+    plan[0] = W;
     plan[1] = total;
-    plan[2] = split.d;
     prefix[0] = 0;
     sbase[0] = 0;
   }
@@ -700,7 +694,7 @@ DecodeLayout decode_layout(const Shape& s, int batch, int max_context_len) {
   L.max_slots = L.grid_cap + batch;
   size_t off = 0;
   L.off_plan = off;
-  off = align256(off + sizeof(int32_t) * (size_t)(5 + 2 * batch + L.grid_cap));
+  off = align256(off + sizeof(int32_t) * (size_t)(4 + 2 * batch + L.grid_cap));
   L.off_qt = off;
   off = align256(off + sizeof(float) * (size_t)batch * s.H * s.RK);
   L.off_ml = off;

@@ -66,7 +66,7 @@ hipError_t decode_enqueue(const DecodeLaunch& a);
 // decode plan for plan_grid attention workgroups.
 hipError_t launch_qproj(const Shape& s, int rows, const void* q, const void* b_k, float scale2, float* qt,
                         const int32_t* plan_lens, int plan_grid, int32_t* plan, hipStream_t st);
-// Log-sum-exp merge of each row's partial slots (slot_base at plan + 4 + rows;
+// Log-sum-exp merge of each row's partial slots (slot_base at plan + 3 + rows;
 // rows with lens[row] == 0 give zeros).
 hipError_t launch_merge(const Shape& s, int rows, const float* pz, const float* pml, const int32_t* plan,
                         const int32_t* lens, float* zf, hipStream_t st);
@@ -110,9 +110,8 @@ struct PrefillPlan {
   int32_t* p;
   int rows;
   int tile_cap;
-  // slot_base sits where the decode plan keeps it (read by the shared merge)
-  static size_t ints(int rows, int tile_cap) { return 4 + (size_t)rows + (rows + 1) + rows + 3 * (size_t)tile_cap + 1; }
-  __host__ __device__ int32_t* slot_base_w() const { return p + 4 + rows; }
+  static size_t ints(int rows, int tile_cap) { return 3 + (size_t)rows + (rows + 1) + rows + 3 * (size_t)tile_cap + 1; }
+  __host__ __device__ int32_t* slot_base_w() const { return p + 3 + rows; }
   __host__ __device__ int32_t* row_len_w() const { return slot_base_w() + rows + 1; }
   __host__ __device__ int32_t* tile_seq_w() const { return row_len_w() + rows; }
   __host__ __device__ int32_t* tile_j_w() const { return tile_seq_w() + tile_cap; }
