@@ -280,10 +280,9 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
     }
 
     // score operands: lane l of scorer wave w owns tile row w*16 + l%16 and
-    // latent dims 8*(l/16) .. +7 of every 32-dim k-step; q~ as fp16 high +
-    // low parts (x - hi is exact in fp32, so hi + lo keeps ~22 bits)
-    // q~ of the lane's row (score B operands of the scorer waves) as fp16 high
-    // and low parts, held in registers for the whole unit
+    // latent dims 8*(l/16) .. +7 of every 32-dim k-step of q~, as fp16 high
+    // and low parts (x - hi is exact in fp32, so hi + lo keeps ~22 bits),
+    // held in registers for the whole unit
     half8 qh[C::KS], ql[C::KS];
     if (scorer) {
       const int rr = w * 16 + (lane & 15);
@@ -483,12 +482,13 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
     // ib: every wave loads its V of block ib+3 into the registers block ib has
     // just left; the non-scorer waves load their pieces of K of block ib+5
     // and store those of block ib+3 (loaded two steps before) to the ring, so
-    // both streams have three steps to arrive.  The scorer waves put the
-    // scores of block ib+2 into the MFMA pipe ahead of block ib's z MFMAs and
-    // run its softmax while those drain.  Loads past the range re-read block
-    // 0 (always in range), so every path of a wave issues the same loads and
-    // the in-order wait counts stay exact.  Both roles pass the same number of
-    // barriers: two in the prologue, one per step.
+    // both streams have three steps to arrive.  The scorer waves take the
+    // scores of block ib+2 and run its softmax before their z MFMAs of block
+    // ib, while the non-scorer wave on the same SIMD keeps the MFMA pipe busy.
+    // Loads past the range re-read block 0 (always in range), so every path
+    // of a wave issues the same loads and the in-order wait counts stay exact.
+    // Both roles pass the same number of barriers: two in the prologue, one
+    // per step.
     // Block table entries are read one step before the loads that use them
     // (pv: V of block ib+3, pk: K of block ib+5), so no step waits for a
     // scalar load.
