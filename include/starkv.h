@@ -197,6 +197,27 @@ starkv_status starkv_prefill(const starkv_dims* dims, int32_t batch, int32_t num
                              const int32_t* context_lens, float scale, void* workspace,
                              size_t workspace_bytes, void* out, void* stream);
 
+/*
+ * starkv_check_block_tables - debug check of the device-side contract that
+ * starkv_decode and starkv_prefill rely on but cannot verify synchronously
+ * (block tables as in the PagedAttention page's block-level management item):
+ * for every sequence b, 0 <= context_lens[b] <= 16*max_blocks_per_seq, and the
+ * ceil(context_lens[b]/16) table entries a call reads lie in [0, num_blocks).
+ * Enqueued on `stream`; writes the number of violations to *error_count
+ * (device int32): one per sequence with a bad length, one per bad entry among
+ * those read.  0 means the tables are safe to decode over.  Entries past the
+ * read ones are not checked.
+ *
+ *   block_tables  [batch][max_blocks_per_seq] int32, device.
+ *   context_lens  [batch] int32, device.
+ *   error_count   one int32, device, 4-byte aligned (overwritten).
+ *
+ * Allocates nothing and does not synchronise: read the count after the stream
+ * has reached it.  INVALID_ARG on bad dims, batch < 1 or a null pointer.
+ */
+starkv_status starkv_check_block_tables(const starkv_dims* dims, int32_t batch, const int32_t* block_tables,
+                                        const int32_t* context_lens, int32_t* error_count, void* stream);
+
 /* Static, human-readable name of a status code (host-only). */
 const char* starkv_status_string(starkv_status status);
 

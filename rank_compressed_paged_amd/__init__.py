@@ -14,7 +14,7 @@ import os
 __all__ = [
     "Dims", "StarkvError", "load_library", "library_path", "status_string",
     "decode_workspace_size", "decode", "append", "prefill_workspace_size", "prefill", "profile_begin",
-    "profile_end", "stream_read_probe",
+    "profile_end", "stream_read_probe", "check_block_tables",
     "BLOCK_SIZE",
 ]
 
@@ -86,6 +86,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.starkv_profile_end.restype = ctypes.c_int
     lib.starkv_stream_read_probe.argtypes = [vp, sz, vp, i32, i32, vp]
     lib.starkv_stream_read_probe.restype = ctypes.c_int
+    lib.starkv_check_block_tables.argtypes = [dp, i32, vp, vp, vp, vp]
+    lib.starkv_check_block_tables.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -265,6 +267,26 @@ def append(k, v, w_k, w_v, block_tables, token_seq, token_pos, k_cache, v_cache,
         raise ValueError("down-projection shapes do not match the caches")
     code = lib.starkv_append(ctypes.byref(dims), n, *[ctypes.c_void_p(p) for p in ptrs], _stream(stream))
     _check(code, "starkv_append")
+
+
+def check_block_tables(block_tables, context_lens, dims: Dims, *, out=None, stream=None):
+    """Count block-table violations a decode over these tables would hit
+    (lengths outside [0, 16*MB], read entries outside [0, num_blocks)).
+
+    Returns a device int32 tensor [1] (read it after the stream gets there)."""
+    import torch
+    bt = _need(block_tables, "block_tables", torch.int32, 2)
+    cl = _need(context_lens, "context_lens", torch.int32, 1)
+    batch = block_tables.shape[0]
+    if context_lens.shape[0] != batch or block_tables.shape[1] != dims.max_blocks_per_seq:
+        raise ValueError("block_tables / context_lens do not match the dims")
+    if out is None:
+        out = torch.empty(1, dtype=torch.int32, device=block_tables.device)
+    op = _need(out, "out", torch.int32, 1)
+    _check(load_library().starkv_check_block_tables(ctypes.byref(dims), batch, ctypes.c_void_p(bt),
+                                                     ctypes.c_void_p(cl), ctypes.c_void_p(op), _stream(stream)),
+           "starkv_check_block_tables")
+    return out
 
 
 def stream_read_probe(buf, sink, grid: int, block: int, stream=None):

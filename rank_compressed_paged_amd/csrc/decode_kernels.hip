@@ -19,6 +19,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -767,6 +769,49 @@ hipError_t launch_upproj(const Shape& s, int rows, const float* zf, const void* 
     hipLaunchKernelGGL(upproj_valu_kernel, dim3(grid, (rows + kSmallBatch - 1) / kSmallBatch), dim3(256), 0, st, zf,
                        static_cast<const f16*>(b_v), static_cast<f16*>(out), rows, s.H, s.KV, s.D, s.RV);
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// debug check of the block tables
+// ---------------------------------------------------------------------------
+
+__global__ void table_check_zero_kernel(int32_t* __restrict__ count) {
+  if (threadIdx.x == 0) *count = 0;
+}
+
+// Grid-stride over every table entry; a workgroup adds its violations once.
+__global__ void __launch_bounds__(256)
+table_check_kernel(const int32_t* __restrict__ bt, const int32_t* __restrict__ lens, int batch, int mb, int nb,
+                   int32_t* __restrict__ count) {
+  __shared__ int bad_wg;
+  if (threadIdx.x == 0) bad_wg = 0;
+  __syncthreads();
+  int bad = 0;
+  const long long n = (long long)batch * mb;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const int b = (int)(i / mb), j = (int)(i % mb);
+    const int len = lens[b];
+    const bool len_ok = len >= 0 && (long long)len <= (long long)kBlock * mb;
+    if (j == 0 && !len_ok) ++bad;
+    const int read = len_ok ? (len + kBlock - 1) / kBlock : 0;
+    if (j < read) {
+      const int p = bt[i];
+      if (p < 0 || p >= nb) ++bad;
+    }
+  }
+  if (bad) atomicAdd(&bad_wg, bad);
+  __syncthreads();
+  if (threadIdx.x == 0 && bad_wg) atomicAdd(count, bad_wg);
+}
+
+hipError_t table_check_enqueue(const int32_t* block_tables, const int32_t* context_lens, int batch, int mb, int nb,
+                               int32_t* count, hipStream_t st) {
+  hipLaunchKernelGGL(table_check_zero_kernel, dim3(1), dim3(64), 0, st, count);
+  const long long n = (long long)batch * mb;
+  const int grid = (int)std::min<long long>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(table_check_kernel, dim3(grid), dim3(256), 0, st, block_tables, context_lens, batch, mb, nb,
+                     count);
   return hipGetLastError();
 }
 

@@ -60,6 +60,10 @@ struct DecodeLaunch {
 int attn_resident_grid(int H, int KV, int RK, int RV, int device);
 
 hipError_t decode_enqueue(const DecodeLaunch& a);
+// Count of block-table violations (entries read outside [0, nb), bad lengths)
+// into *count, on the stream.
+hipError_t table_check_enqueue(const int32_t* block_tables, const int32_t* context_lens, int batch, int mb, int nb,
+                               int32_t* count, hipStream_t st);
 
 // Stages shared by decode and prefill (decode_kernels.hip); `rows` = query rows.
 // q~ projection; with plan_lens non-null its last workgroup also builds the

@@ -111,6 +111,20 @@ size_t starkv_decode_workspace_size(const starkv_dims* dims, int32_t batch, int3
   return decode_layout(shape_of(dims), batch, max_context_len).bytes;
 }
 
+starkv_status starkv_check_block_tables(const starkv_dims* dims, int32_t batch, const int32_t* block_tables,
+                                        const int32_t* context_lens, int32_t* error_count, void* stream) {
+  const starkv_status ds = check_dims(dims);
+  if (ds != STARKV_OK) return ds;
+  if (batch < 1 || batch > (1 << 20) || !block_tables || !context_lens || !error_count)
+    return STARKV_ERR_INVALID_ARG;
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(error_count, 4))
+    return STARKV_ERR_INVALID_ARG;
+  return table_check_enqueue(block_tables, context_lens, batch, dims->max_blocks_per_seq, dims->num_blocks,
+                             error_count, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? STARKV_OK
+             : STARKV_ERR_HIP;
+}
+
 starkv_status starkv_decode(const starkv_dims* dims, int32_t batch, int32_t max_context_len, const void* q,
                             const void* b_k, const void* b_v, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, const int32_t* context_lens, float scale,

@@ -177,3 +177,16 @@ def test_prefill_workspace_size(lib):
     assert f(ctypes.byref(d), 0, 512, 8192) == 0
     assert f(ctypes.byref(d), 4, 0, 8192) == 0
     assert f(ctypes.byref(d), 4, 512, 512 * 16 + 1) == 0
+
+
+def test_check_block_tables_rejects_before_touching_the_device(lib):
+    d = main_dims()
+    ok_ptr = ctypes.c_void_p(256)
+    f = lib.starkv_check_block_tables
+    assert f(None, 4, ok_ptr, ok_ptr, ok_ptr, None) == INVALID
+    assert f(ctypes.byref(d), 0, ok_ptr, ok_ptr, ok_ptr, None) == INVALID
+    assert f(ctypes.byref(d), 4, None, ok_ptr, ok_ptr, None) == INVALID
+    assert f(ctypes.byref(d), 4, ok_ptr, None, ok_ptr, None) == INVALID
+    assert f(ctypes.byref(d), 4, ok_ptr, ok_ptr, None, None) == INVALID
+    assert f(ctypes.byref(d), 4, ok_ptr, ok_ptr, ctypes.c_void_p(258), None) == INVALID   # misaligned count
+    assert f(ctypes.byref(main_dims(block_size=32)), 4, ok_ptr, ok_ptr, ok_ptr, None) == UNSUPPORTED

@@ -193,6 +193,35 @@ def test_single_long_sequence_every_range(d):
     check(out, ref, what=f"single long sequence d={d}")
 
 
+def test_check_block_tables_counts_planted_violations():
+    """The debug table check finds nothing in valid tables, and exactly the
+    planted violations otherwise: read entries outside [0, NB), a length past
+    16*MB; entries past a sequence's read blocks (and an empty sequence's) are
+    not read and not counted."""
+    import torch
+    import rank_compressed_paged_amd as starkv
+    dev = gpu()
+    lens = np.array([300, 47, 0, 129, 16], np.int32)
+    case = small_main_case(481, lens)
+    g = to_dev(case, dev)
+    dims = starkv.dims_of(g["k_pool"], g["v_pool"], g["block_tables"], 128, heads=32)
+    clean = starkv.check_block_tables(g["block_tables"], g["context_lens"], dims)
+    torch.cuda.synchronize()
+    assert int(clean.item()) == 0
+    bt = case["block_tables"].copy()
+    L = lens.copy()
+    nb, mb = case["num_blocks"], bt.shape[1]
+    bt[0, 5] = -1                 # read: 300 tokens use blocks 0..18
+    bt[3, 8] = nb                 # read: 129 tokens use blocks 0..8
+    bt[1, 3] = nb + 7             # not read: 47 tokens use blocks 0..2
+    bt[2, 0] = -5                 # not read: empty sequence
+    L[4] = 16 * mb + 1            # length past the table row
+    got = starkv.check_block_tables(torch.from_numpy(bt).to(dev), torch.from_numpy(L).to(dev), dims)
+    torch.cuda.synchronize()
+    log(f"table check: {int(got.item())} violations (3 planted)")
+    assert int(got.item()) == 3
+
+
 # ------------------------------------------------------------- full sizes
 @pytest.fixture(scope="module")
 def config3():
