@@ -362,7 +362,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph timing of the headline step")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr, flush=True)
+        print("bench.py: measures one GPU (the library has no multi-GPU path); --gpus must be 1", file=sys.stderr, flush=True)
         sys.exit(2)
     if args.calib_copy:
         calib_copy()
