@@ -181,7 +181,7 @@ def graph_replay_ms(step, steps: int, out, flush=None) -> float:
 
 
 def config_report(cfg_id: int, steps: int, warmup: int, graph: bool = False):
-    """Timing of one of the five parity workloads (a separate JSON line).
+    """Timing of one of the decode workloads 1-7 (a separate JSON line).
 
     A step appends one token per sequence, then decodes; for the 32-layer stack
     a step runs that for every layer (tokens/s = batch / summed layer time).
