@@ -197,6 +197,18 @@ def test_prefill_workspace_reuse_deterministic():
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
+def test_prefill_long_context_many_ranges():
+    """A 70-row chunk (a full tile and a 6-row tail) at the end of a
+    40,000-token context: the plan cuts the context into ~10 ranges, so each row
+    merges that many partial states."""
+    dev = gpu()
+    lens, chunks = [40000], [70]
+    case = synth.make_prefill_case(790, 32, 128, 64, 1024, lens, chunks)
+    log("prefill 70 rows at context 40000")
+    out = prefill_gpu(to_dev(case, dev), case, 1.0 / math.sqrt(128), dev)
+    check(out, oracle_prefill(case, 1.0 / math.sqrt(128)), "long context, many ranges")
+
+
 @pytest.mark.slow
 def test_prefill_chunks_full_size_sampled():
     """Chunked prefill at serving size: 4 sequences, 512-token chunks at
