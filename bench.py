@@ -243,6 +243,7 @@ def config_report(cfg_id: int, steps: int, warmup: int, graph: bool = False):
     starkv.profile_begin()
     total_ms = 0.0
     tokens = 0
+    step_ms = []
     for s in range(warmup, warmup + steps):
         if flush is not None:
             flush.fill_(s & 0xFF)
@@ -252,7 +253,8 @@ def config_report(cfg_id: int, steps: int, warmup: int, graph: bool = False):
         tokens += step(s)
         e1.record()
         e1.synchronize()
-        total_ms += e0.elapsed_time(e1)
+        step_ms.append(e0.elapsed_time(e1))
+        total_ms += step_ms[-1]
     attn_ms, launches = starkv.profile_end()
     latent = tokens * sum(layer_bytes)
     line = {
@@ -260,6 +262,7 @@ def config_report(cfg_id: int, steps: int, warmup: int, graph: bool = False):
         "heads": cfg.heads, "kv_heads": cfg.kv,
         "mean_latent_elems_per_token_layer": sum(layer_bytes) / 2 / cfg.layers,
         "steps": steps, "warmup": warmup, "ms_per_step": total_ms / steps,
+        "step_ms_p10_median_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
         "decode_tokens_per_s": cfg.batch * steps / (total_ms / 1e3),
         "attn_kernel_us_per_launch": attn_ms / launches * 1e3,
         "latent_gb_per_step": latent / steps / 1e9,
