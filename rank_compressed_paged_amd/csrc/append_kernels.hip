@@ -76,7 +76,7 @@ __device__ __forceinline__ void append_k_mfma_body(int tile, int lane, const f16
 __device__ __forceinline__ void append_k_valu_body(int idx, const f16* __restrict__ k, const f16* __restrict__ wk,
                                                    int n, int H, int D, int RK, SlotOf where,
                                                    f16* __restrict__ kc) {
-  if (idx >= n * H * RK) return;
+  if ((long long)idx >= (long long)n * H * RK) return;
   const int r = idx % RK;
   const int h = (idx / RK) % H;
   const int t = idx / (RK * H);
@@ -120,6 +120,17 @@ __device__ __forceinline__ void append_v_mfma_body(int bid, const f16* __restric
   const int kbase = w * ksteps * 32;
   const f16* xrow = v + (size_t)(trow ? t : n - 1) * K + kofs;
   const f16* wrow = wv + (size_t)j * K + kofs;
+  // destination of the value this lane stores (waves 0-3, see the end): its
+  // sequence and position are read before the operands and its table entry
+  // right behind them, so the slot lookup overlaps the contraction instead of
+  // adding two dependent round trips after it
+  const int ti = tt * 16 + 4 * (lane >> 4) + w;
+  const bool storer = w < 4 && ti < n;
+  int dseq = 0, dpos = 0, dphys = 0;
+  if (storer) {
+    dseq = where.seq[ti];
+    dpos = where.pos[ti];
+  }
   floatx4 acc = {};
   for (int c = 0; c < ksteps; c += kAppendVBatch) {
     half8 a[kAppendVBatch], b[kAppendVBatch];
@@ -130,6 +141,8 @@ __device__ __forceinline__ void append_v_mfma_body(int bid, const f16* __restric
       b[u] = *reinterpret_cast<const half8*>(wrow + k0);
     }
     __builtin_amdgcn_sched_barrier(0);      // every load of the batch is in flight before the first MFMA
+    if (c == 0 && storer) dphys = where.bt[(size_t)dseq * where.mb + dpos / kBlock];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < kAppendVBatch; ++u) {
       const bool live = trow && c + u < ksteps;   // clamped re-reads contribute nothing
@@ -140,17 +153,11 @@ __device__ __forceinline__ void append_v_mfma_body(int bid, const f16* __restric
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[w][r][lane] = acc[r];
   __syncthreads();
-  if (w < 4) {                         // wave w finishes register w
-    const int r = w;
+  if (storer) {                        // wave w finishes register w
     float sum = 0.f;
 #pragma unroll
-    for (int q = 0; q < kAppendVWaves; ++q) sum += red[q][r][lane];
-    const int ti = tt * 16 + 4 * (lane >> 4) + r;
-    if (ti < n) {
-      int phys, slot;
-      where(ti, phys, slot);
-      vc[((size_t)phys * RV + j) * kBlock + slot] = (f16)sum;
-    }
+    for (int q = 0; q < kAppendVWaves; ++q) sum += red[q][w][lane];
+    vc[((size_t)dphys * RV + j) * kBlock + dpos % kBlock] = (f16)sum;
   }
 }
 
@@ -361,6 +368,25 @@ append_v_valu_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
   append_v_valu_body(blockIdx.x, blockIdx.y, v, wv, n, K, RV, where, vc);
 }
 
+// Small MFMA appends (from 16 tokens up to what fills the compute units;
+// 48 at 32 heads, r_v 1024 on 256 units): one launch of 512-thread
+// workgroups, the first nv running the V side's [16 x 16] tiles and the rest
+// eight K-side [32 x 32] tiles each (one per wave).  The K side then runs
+// beside the V side instead of adding its own launch and memory round trip.
+__global__ void __launch_bounds__(kAppendVWaves * 64)
+append_kv_mfma_kernel(const f16* __restrict__ k, const f16* __restrict__ v, const f16* __restrict__ wk,
+                      const f16* __restrict__ wv, int n, int KV, int D, int RK, int RV, SlotOf where,
+                      f16* __restrict__ kc, f16* __restrict__ vc, int nv, int ktiles) {
+  const int bid = blockIdx.x;
+  if (bid < nv) {                            // whole workgroup: the V side's barrier sees every wave
+    append_v_mfma_body(bid, v, wv, n, KV * D, RV, where, vc);
+    return;
+  }
+  const int tile = (bid - nv) * kAppendVWaves + ((int)threadIdx.x >> 6);
+  if (tile >= ktiles) return;                // the K side has no barrier
+  append_k_mfma_body(tile, threadIdx.x & 63, k, wk, n, KV, D, RK, where, kc);
+}
+
 // Small appends (fewer than 16 tokens, both sides on VALU): one launch of
 // 512-thread workgroups, the first nv running the V side and the rest the K
 // side (512 outputs each).  Both sides are latency-bound chains of a few
@@ -397,34 +423,47 @@ hipError_t append_enqueue(const AppendLaunch& a) {
     const int vgx = (s.RV + 7) / 8;
     const long long nv = (long long)vgx * ((a.n + kAppendGroup - 1) / kAppendGroup);
     const long long grid = nv + ((long long)a.n * s.KV * s.RK + 511) / 512;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (grid * 512 > (1LL << 31)) return hipErrorInvalidValue;    // thread indices stay in int
     hipLaunchKernelGGL(append_kv_valu_kernel, dim3((unsigned)grid), dim3(512), 0, a.stream, k, v, wk, wv, a.n, s.KV,
                        s.D, s.RK, s.RV, where, kc, vc, (int)nv, vgx);
     return hipGetLastError();
   }
-  if (kmfma) {
-    const int grid = ((a.n + 31) / 32) * s.KV * (s.RK / 32);
-    hipLaunchKernelGGL(append_k_mfma_kernel, dim3(grid), dim3(64), 0, a.stream, k, wk, a.n, s.KV, s.D, s.RK,
-                       where, kc);
-  } else {
-    const int grid = (a.n * s.KV * s.RK + 255) / 256;
-    hipLaunchKernelGGL(append_k_valu_kernel, dim3(grid), dim3(256), 0, a.stream, k, wk, a.n, s.KV, s.D, s.RK,
-                       where, kc);
+  // grid sizes in 64-bit: no launch below exceeds 2^31 threads, so thread
+  // and tile indices inside the kernels stay in int
+  const long long n = a.n;
+  const long long nv = ((s.RV / 16 + 7) / 8) * 8LL * ((n + 15) / 16);
+  const long long ktiles = ((n + 31) / 32) * s.KV * (s.RK / 32);
+  const long long grid_kv = nv + (ktiles + kAppendVWaves - 1) / kAppendVWaves;
+  const long long kgrid = kmfma ? ktiles : (n * s.KV * s.RK + 255) / 256;   // 64 / 256 threads
+  const long long vtiles = (n + kAppendRowsTok - 1) / kAppendRowsTok * ((s.RV / kAppendRowsLat + 7) / 8) * 8;
+  const long long vgrid = vrows ? vtiles : nv;          // the VALU V side has a 2-D grid of (r_v/8, n/4)
+  if (kgrid * (kmfma ? 64 : 256) > (1LL << 31) || ((vrows || vmfma) && vgrid * 512 > (1LL << 31)))
+    return hipErrorInvalidValue;
+  // One launch for both sides only while every workgroup gets a compute unit
+  // of its own: a V-side workgroup leaves too few registers on its unit for a
+  // second one, so K-side workgroups beyond that would wait for the V side.
+  if (kmfma && vmfma && grid_kv <= a.cus) {
+    hipLaunchKernelGGL(append_kv_mfma_kernel, dim3((unsigned)grid_kv), dim3(kAppendVWaves * 64), 0, a.stream, k, v,
+                       wk, wv, a.n, s.KV, s.D, s.RK, s.RV, where, kc, vc, (int)nv, (int)ktiles);
+    return hipGetLastError();
   }
+  if (kmfma)
+    hipLaunchKernelGGL(append_k_mfma_kernel, dim3((unsigned)kgrid), dim3(64), 0, a.stream, k, wk, a.n, s.KV, s.D,
+                       s.RK, where, kc);
+  else
+    hipLaunchKernelGGL(append_k_valu_kernel, dim3((unsigned)kgrid), dim3(256), 0, a.stream, k, wk, a.n, s.KV, s.D,
+                       s.RK, where, kc);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (vrows) {
-    const int ttiles = (a.n + kAppendRowsTok - 1) / kAppendRowsTok;
-    const int grid = ttiles * ((s.RV / kAppendRowsLat + 7) / 8) * 8;
-    hipLaunchKernelGGL(append_v_rows_kernel, dim3(grid), dim3(512), 0, a.stream, v, wv, a.n, K, s.RV, where, vc);
-  } else if (vmfma) {
-    const int grid = ((s.RV / 16 + 7) / 8) * 8 * ((a.n + 15) / 16);
-    hipLaunchKernelGGL(append_v_mfma_kernel, dim3(grid), dim3(kAppendVWaves * 64), 0, a.stream, v, wv, a.n, K,
-                       s.RV, where, vc);
-  } else {
-    const dim3 grid((s.RV + 7) / 8, (a.n + kAppendGroup - 1) / kAppendGroup);
-    hipLaunchKernelGGL(append_v_valu_kernel, grid, dim3(512), 0, a.stream, v, wv, a.n, K, s.RV, where, vc);
-  }
+  if (vrows)
+    hipLaunchKernelGGL(append_v_rows_kernel, dim3((unsigned)vgrid), dim3(512), 0, a.stream, v, wv, a.n, K, s.RV,
+                       where, vc);
+  else if (vmfma)
+    hipLaunchKernelGGL(append_v_mfma_kernel, dim3((unsigned)vgrid), dim3(kAppendVWaves * 64), 0, a.stream, v, wv,
+                       a.n, K, s.RV, where, vc);
+  else
+    hipLaunchKernelGGL(append_v_valu_kernel, dim3((s.RV + 7) / 8, (unsigned)((n + kAppendGroup - 1) / kAppendGroup)),
+                       dim3(512), 0, a.stream, v, wv, a.n, K, s.RV, where, vc);
   return hipGetLastError();
 }
 

@@ -93,6 +93,7 @@ struct AppendLaunch {
   void* k_cache;
   void* v_cache;
   hipStream_t stream;
+  int cus;               // compute units of the device (0 if unknown)
 };
 
 hipError_t append_enqueue(const AppendLaunch& a);

@@ -62,6 +62,19 @@ int resident_grid(int H, int KV, int RK, int RV, int device) {
   return v;
 }
 
+// Compute units per device, filled on first use.
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus(int device) {
+  if (device < 0 || device >= kMaxDevices) return 0;
+  int v = g_cus[device].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || v < 1) return 0;
+    g_cus[device].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 // measurement hooks
 std::mutex g_prof_mu;
 bool g_prof_on = false;
@@ -236,9 +249,12 @@ starkv_status starkv_append(const starkv_dims* dims, int32_t n_tokens, const voi
       !aligned(block_tables, 4) || !aligned(token_seq, 4) || !aligned(token_pos, 4) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16))
     return STARKV_ERR_INVALID_ARG;
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return STARKV_ERR_HIP;
   AppendLaunch a{};
   a.s = shape_of(dims);
   a.n = n_tokens;
+  a.cus = device_cus(device);
   a.k = k;
   a.v = v;
   a.w_k = w_k;
