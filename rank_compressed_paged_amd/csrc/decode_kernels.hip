@@ -365,7 +365,8 @@ upproj_mfma_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
 // all its row tiles, which run on one XCD.  Wave w owns output tile
 // (rows 32*(w&1), dims 32*(w>>1)).  The contraction runs in spans of 128
 // latent dims; per span both operands are staged in LDS with every load of a
-// thread issued before its first LDS write (one memory round trip per span):
+// thread issued before its first LDS write, and the next span's loads are in
+// flight while this span's MFMAs run:
 //   Z   [64 rows x 128] fp32, coalesced (a wave instruction reads 512 B of
 //       each of two rows); A fragments are split into fp16 hi + lo on the way
 //       to the MFMA;
@@ -404,9 +405,11 @@ upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
   const f16* bsrc = bv + (size_t)(2 * kp) * ld + (size_t)kvh * D + sn;
   constexpr int kZPieces = kUpRowsTile * kUpRowsSpan / 4 / 512;   // 16-byte Z pieces per thread
   floatx16 acc = {};
-  for (int k0 = 0; k0 < RV; k0 += kUpRowsSpan) {
-    half8 braw[2][kNPer / 8];
-    floatx4 zv[kZPieces];
+  half8 braw[2][kNPer / 8];
+  floatx4 zv[kZPieces];
+  // Z is read exactly once: non-temporal loads keep it from evicting the
+  // B_v slices that the head's other row tiles re-read from L2
+  auto load_span = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -416,9 +419,13 @@ upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
     for (int i = 0; i < kZPieces; ++i) {
       const int f = i * 512 + threadIdx.x;
       const int r = f / (kUpRowsSpan / 4), c4 = (f % (kUpRowsSpan / 4)) * 4;
-      zv[i] = row0 + r < rows ? *reinterpret_cast<const floatx4*>(zf + ((size_t)(row0 + r) * H + h) * RV + k0 + c4)
+      zv[i] = row0 + r < rows ? __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(
+                                    zf + ((size_t)(row0 + r) * H + h) * RV + k0 + c4))
                               : floatx4{};
     }
+  };
+  load_span(0);
+  for (int k0 = 0; k0 < RV; k0 += kUpRowsSpan) {
     __syncthreads();                      // previous span's readers are done
 #pragma unroll
     for (int i = 0; i < kZPieces; ++i) {
@@ -439,6 +446,7 @@ upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
       }
     }
     __syncthreads();
+    if (k0 + kUpRowsSpan < RV) load_span(k0 + kUpRowsSpan);   // in flight during this span's MFMAs
     const float* za = &zl[rt * 32 + (lane & 31)][(lane >> 5) * 8];
     const uint32_t* brow = &bt[nt * 32 + (lane & 31)][(lane >> 5) * 4];
 #pragma unroll

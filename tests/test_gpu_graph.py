@@ -55,9 +55,10 @@ def replay_and_compare(step, tensors, what):
 
 
 @pytest.mark.parametrize("h,kv,rk,rv,batch", [(32, 32, 64, 1024, 6), (32, 32, 64, 1024, 40),
-                                              (32, 8, 64, 512, 6), (4, 4, 16, 64, 3)])
+                                              (32, 32, 64, 1024, 64), (32, 8, 64, 512, 6), (4, 4, 16, 64, 3)])
 def test_graph_append_decode(h, kv, rk, rv, batch):
-    """Small batches take the VALU projections, 40 sequences the MFMA ones."""
+    """Small batches take the VALU projections; 40 sequences the MFMA ones in
+    one launch, 64 in two."""
     import torch
     import rank_compressed_paged_amd as starkv
     dev = gpu()
