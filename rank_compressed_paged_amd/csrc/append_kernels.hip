@@ -29,8 +29,10 @@ struct SlotOf {
 };
 
 // K side, MFMA: one wave computes a [32 tokens x 32 latents] tile of one head.
-// The destination slots and all operand loads are issued before the first
-// MFMA, so the launch costs about one memory latency.
+// Lane l looks up the slot of token l % 32 (its sequence and position ahead of
+// the operand loads, its table entry right behind them) and the stores fetch
+// each row's slot from that lane by a shuffle: three loads per lane instead of
+// three per result register, all in flight with the operands.
 __device__ __forceinline__ void append_k_mfma_body(int tile, int lane, const f16* __restrict__ k,
                                                    const f16* __restrict__ wk, int n, int H, int D, int RK,
                                                    SlotOf where, f16* __restrict__ kc) {
@@ -42,14 +44,9 @@ __device__ __forceinline__ void append_k_mfma_body(int tile, int lane, const f16
   const bool trow = t < n;
   const int r = rt * 32 + (lane & 31);
   const int kofs = (lane >> 5) * 8;
-  size_t dst[16];
-#pragma unroll
-  for (int reg = 0; reg < 16; ++reg) {
-    const int ti = min(tt * 32 + mfma_row(reg, lane), n - 1);
-    int phys, slot;
-    where(ti, phys, slot);
-    dst[reg] = (((size_t)phys * H + h) * kBlock + slot) * RK + r;
-  }
+  const int tl = min(tt * 32 + (lane & 31), n - 1);
+  const int lseq = where.seq[tl], lpos = where.pos[tl];
+  int lphys = 0;
   const f16* xrow = k + ((size_t)(trow ? t : n - 1) * H + h) * D + kofs;
   const f16* wrow = wk + ((size_t)h * RK + r) * D + kofs;
   const int ksteps = D / 16;
@@ -62,10 +59,22 @@ __device__ __forceinline__ void append_k_mfma_body(int tile, int lane, const f16
       a[u] = *reinterpret_cast<const half8*>(xrow + k0);
       b[u] = *reinterpret_cast<const half8*>(wrow + k0);
     }
+    __builtin_amdgcn_sched_barrier(0);      // the table entry is read behind the operands
+    if (c == 0) lphys = where.bt[(size_t)lseq * where.mb + lpos / kBlock];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (c + u < ksteps) acc = mfma32x32x16(trow ? a[u] : half8{}, b[u], acc);
     }
+  }
+  // every shuffle is issued before the first store (the stores are guarded)
+  size_t dst[16];
+#pragma unroll
+  for (int reg = 0; reg < 16; ++reg) {
+    const int src = mfma_row(reg, lane);    // token row of this register, looked up by lane src
+    const int phys = __shfl(lphys, src, 64);
+    const int slot = __shfl(lpos, src, 64) % kBlock;
+    dst[reg] = (((size_t)phys * H + h) * kBlock + slot) * RK + r;
   }
 #pragma unroll
   for (int reg = 0; reg < 16; ++reg)
