@@ -248,11 +248,16 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
   const long long units = (long long)((items + 7) & ~7) * H;
 
   for (long long u = blockIdx.x; u < units; u += gridDim.x) {
-    // XCD-aware order: the H heads of an item share u % 8, hence one XCD
+    // XCD-aware order: the H heads of an item share u % 8, hence one XCD.
+    // Items run in groups of eight, one per XCD, and every other group is
+    // reversed: items are in tile order, and a causal prompt's later tiles
+    // see more context, so a fixed order would hand one XCD the longest item
+    // of every group.
     const int x = (int)(u % 8);
     const long long sidx = u / 8;
     const int h = (int)(sidx % H);
-    const int item = (int)(sidx / H) * 8 + x;
+    const int grp = (int)(sidx / H);
+    const int item = grp * 8 + ((grp & 1) ? 7 - x : x);
     if (item >= items) continue;
     int lo = 0, hi = tiles;                  // last tile with tile_items[t] <= item
     while (hi - lo > 1) {
