@@ -85,7 +85,10 @@ typedef struct {
  * latent r).  With orthonormal-row up-projections B, w = B gives the
  * least-squares latents, so callers may pass b_k / b_v of starkv_decode.
  *
- *   n_tokens     number of rows; 0 is a no-op returning STARKV_OK.
+ *   n_tokens     number of rows, at most 2^24 (else STARKV_ERR_INVALID_ARG);
+ *                0 is a no-op returning STARKV_OK.  A call too large for one
+ *                launch grid (over 2^31 threads, reachable only for very large
+ *                n_tokens) enqueues nothing and returns STARKV_ERR_HIP.
  *   k, v         [n_tokens][H_kv][d] fp16, 16-byte aligned.
  *   block_tables [B][max_blocks_per_seq] int32.  The target block of every
  *                token must already be assigned (allocation is the caller's).
