@@ -71,13 +71,13 @@ def test_append_golden_bits(golden_dir):
     assert not kb.any() and not vb.any()
 
 
-@pytest.mark.parametrize("n_per_seq", [2, 12, 20, 120])
+@pytest.mark.parametrize("n_per_seq", [2, 4, 12, 20, 120])
 @pytest.mark.parametrize("shape", ["main", "tiny"])
 def test_append_selection_projection_bit_exact(shape, n_per_seq):
     """w = [I | 0]: every latent is a copied input value, so the pool image is exact.
-    Main shape: n = 8 takes the VALU kernels, n = 48 the MFMA kernels of both
-    sides in one launch, n = 76 the same kernels in two launches and n = 288
-    the many-token V kernel."""
+    Main shape: n = 8 takes the VALU kernels, n = 16 (the smallest MFMA
+    append) and n = 48 the MFMA kernels of both sides in one launch, n = 76
+    the same kernels in two launches and n = 288 the many-token V kernel."""
     dev = gpu()
     if shape == "main":
         H, d, rk, rv = 32, 128, 64, 1024
