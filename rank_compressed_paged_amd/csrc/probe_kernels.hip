@@ -1,5 +1,5 @@
 // HBM stream-read ceiling probe: the plain sequential read rate one MI355X
-// sustains, against which the latent scan is judged alongside the 8 TB/s peak.
+// sustains; the latent scan is compared with it as well as with the 8 TB/s peak.
 // Every lane reads 16-byte words in a grid-stride loop with U loads in
 // flight; the values are folded so the loads cannot be removed.
 
