@@ -56,7 +56,7 @@ typedef enum {
 typedef struct {
   int32_t num_heads;          /* H query heads                          */
   int32_t head_dim;           /* d, multiple of 8, <= 256               */
-  int32_t rank_k;             /* r_k per head, multiple of 8            */
+  int32_t rank_k;             /* r_k per head, multiple of 8, <= 256    */
   int32_t rank_v;             /* r_v joint over heads, multiple of 32, <= 1024 */
   int32_t block_size;         /* tokens per paged block; must be 16     */
   int32_t num_blocks;         /* physical blocks in each pool           */
@@ -133,7 +133,8 @@ size_t starkv_decode_workspace_size(const starkv_dims* dims, int32_t batch,
  *                    16*max_blocks_per_seq.
  *   q                [B][H][d] fp16, 16-byte aligned.
  *   b_k              [H_kv][r_k][d] fp16, 16-byte aligned.
- *   b_v              [r_v][H_kv*d] fp16, 2-byte aligned.
+ *   b_v              [r_v][H_kv*d] fp16, 16-byte aligned (rows are read as
+ *                    16-byte vectors).
  *   k_cache, v_cache pools (layout above), 16-byte aligned.  Entries of a
  *                    table row at index >= ceil(len/16), and slots >= len%16 of
  *                    the last block, are never read.

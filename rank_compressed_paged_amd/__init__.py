@@ -129,6 +129,36 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
+def _torch_stream(stream, device):
+    """The torch Stream object of `stream` (None = the current stream)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _scratch(nbytes, device, stream):
+    """Workspace for one call on `stream`.  It is allocated from the caching
+    allocator's pool of that stream, so once the call returns and the tensor
+    is dropped the memory is reused only by work ordered after the call's
+    kernels on the same stream."""
+    import torch
+    s = _torch_stream(stream, device)
+    with torch.cuda.stream(s):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _own_out(out, device, stream):
+    """A tensor the library writes on a stream other than the current one must
+    not be recycled by the allocator before that stream gets there."""
+    import torch
+    s = _torch_stream(stream, device)
+    if s != torch.cuda.current_stream(device):
+        out.record_stream(s)
+
+
 def dims_of(k_cache, v_cache, block_tables, head_dim, heads=None):
     """Dims from the cache shapes; `heads` = query heads (default: the cache's key/value heads)."""
     nb, kv_heads, bs, rank_k = k_cache.shape
@@ -176,11 +206,12 @@ def decode(q, b_k, b_v, k_cache, v_cache, block_tables, context_lens, scale, *,
     if need == 0:
         _check(1, "starkv_decode_workspace_size")
     if workspace is None:
-        workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need + 256, q.device, stream)
     ws_ptr = _need(workspace, "workspace", torch.uint8, 1)
     pad = (-ws_ptr) % 256
     if out is None:
         out = torch.empty_like(q)
+        _own_out(out, q.device, stream)
     optr = _need(out, "out", torch.float16, 3)
     code = lib.starkv_decode(ctypes.byref(dims), batch, int(max_context_len), *ptrs[:5], ptrs[5], ptrs[6],
                              float(scale), ctypes.c_void_p(ws_ptr + pad), workspace.numel() - pad,
@@ -225,13 +256,14 @@ def prefill(q, b_k, b_v, k_cache, v_cache, block_tables, query_start, context_le
         raise ValueError("projection shapes do not match the caches")
     if out is None:
         out = torch.empty_like(q)
+        _own_out(out, q.device, stream)
     if rows == 0:
         return out
     need = lib.starkv_prefill_workspace_size(ctypes.byref(dims), batch, rows, int(max_context_len))
     if need == 0:
         _check(1, "starkv_prefill_workspace_size")
     if workspace is None:
-        workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need + 256, q.device, stream)
     ws_ptr = _need(workspace, "workspace", torch.uint8, 1)
     pad = (-ws_ptr) % 256
     optr = _need(out, "out", torch.float16, 3)

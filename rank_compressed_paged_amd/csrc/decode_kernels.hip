@@ -152,11 +152,11 @@ qproj_plan_valu_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, fl
     build_plan(lens, batch, grid, plan);
     return;
   }
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= batch * H * RK) return;
-  const int r = idx % RK;
-  const int head = (idx / RK) % H;
-  const int b = idx / (RK * H);
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)batch * H * RK) return;
+  const int r = (int)(idx % RK);
+  const int head = (int)((idx / RK) % H);
+  const int b = (int)(idx / ((long long)RK * H));
   const f16* qp = q + ((size_t)b * H + head) * D;
   const f16* bp = bk + ((size_t)(head / (H / KV)) * RK + r) * D;
   qt[idx] = dot_f16(qp, bp, D) * scale2;
@@ -694,12 +694,13 @@ merge_upproj_small_kernel(const float* __restrict__ part_z, const float* __restr
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-DecodeLayout decode_layout(const Shape& s, int batch, int max_context_len) {
+DecodeLayout decode_layout(const Shape& s, int batch, int max_context_len, int grid) {
   DecodeLayout L{};
   const long long blocks_ub = (long long)batch * ((max_context_len + kBlock - 1) / kBlock);
   long long cap = (blocks_ub + kMinBlocksPerWG - 1) / kMinBlocksPerWG;
   if (cap < 1) cap = 1;
   if (cap > kMaxGrid) cap = kMaxGrid;
+  if (grid > 0 && grid < cap) cap = grid;      // carved for a known launch grid
   L.grid_cap = (int)cap;
   L.max_slots = L.grid_cap + batch;
   size_t off = 0;
@@ -728,8 +729,10 @@ hipError_t launch_qproj(const Shape& s, int rows, const void* q, const void* b_k
                        static_cast<const f16*>(b_k), qt, rows, s.H, s.KV, s.D, s.RK, scale2, plan_lens, plan_grid,
                        plan);
   } else {
-    const int nq = (rows * s.H * s.RK + 255) / 256;
-    hipLaunchKernelGGL(qproj_plan_valu_kernel, dim3(nq + extra), dim3(256), 0, st, static_cast<const f16*>(q),
+    // one thread per (row, head, latent): the grid size is counted in 64 bits
+    const long long nq = ((long long)rows * s.H * s.RK + 255) / 256;
+    if (nq + extra > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(qproj_plan_valu_kernel, dim3((unsigned)(nq + extra)), dim3(256), 0, st, static_cast<const f16*>(q),
                        static_cast<const f16*>(b_k), qt, rows, s.H, s.KV, s.D, s.RK, scale2, plan_lens, plan_grid,
                        plan);
   }

@@ -28,7 +28,9 @@ struct DecodeLayout {
   size_t off_plan, off_qt, off_ml, off_z, off_zf, bytes;
 };
 
-DecodeLayout decode_layout(const Shape& s, int batch, int max_context_len);
+// grid > 0: carve only for that many attention workgroups (else for the cap,
+// which needs no device query).
+DecodeLayout decode_layout(const Shape& s, int batch, int max_context_len, int grid = 0);
 
 // Returns true if a latent attention kernel is built for (H, H_kv, r_k, r_v).
 bool attn_shape_supported(int H, int KV, int RK, int RV);

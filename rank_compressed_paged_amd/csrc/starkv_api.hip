@@ -24,7 +24,7 @@ starkv_status check_dims(const starkv_dims* d) {
   if (d->num_kv_heads < 0 || (d->num_kv_heads > 0 && d->num_heads % d->num_kv_heads != 0))
     return STARKV_ERR_INVALID_ARG;
   if (d->block_size != kBlock) return STARKV_ERR_UNSUPPORTED;
-  if (d->head_dim % 8 != 0 || d->head_dim > 256 || d->rank_k % 8 != 0 || d->rank_v % 32 != 0 ||
+  if (d->head_dim % 8 != 0 || d->head_dim > 256 || d->rank_k % 8 != 0 || d->rank_k > 256 || d->rank_v % 32 != 0 ||
       d->rank_v > 1024)
     return STARKV_ERR_UNSUPPORTED;
   // 64-bit products stay far from overflow; 32-bit indices inside kernels need:
@@ -104,6 +104,60 @@ bool prefill_args_ok(const starkv_dims* d, int32_t batch, int32_t num_queries, i
   return (long long)num_queries * ((max_context_len + kBlock - 1) / kBlock) < (1LL << 40);
 }
 
+// Body of starkv_decode.  `tight`: carve the workspace for the launch grid
+// actually used, instead of for the grid cap that
+// starkv_decode_workspace_size assumes.  The grid, and so every partial split
+// and every result bit, is the same.
+starkv_status decode_call(const starkv_dims* dims, int32_t batch, int32_t max_context_len, const void* q,
+                          const void* b_k, const void* b_v, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, float scale, void* workspace,
+                          size_t workspace_bytes, bool tight, void* out, void* stream) {
+  const starkv_status ds = check_dims(dims);
+  if (ds != STARKV_OK) return ds;
+  if (!decode_args_ok(dims, batch, max_context_len)) return STARKV_ERR_INVALID_ARG;
+  if (!q || !b_k || !b_v || !k_cache || !v_cache || !block_tables || !context_lens || !workspace || !out)
+    return STARKV_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(b_k, 16) || !aligned(b_v, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      !aligned(workspace, 256) || !aligned(out, 2))
+    return STARKV_ERR_INVALID_ARG;
+  if (!(scale == scale)) return STARKV_ERR_INVALID_ARG;  // NaN scale
+  const Shape s = shape_of(dims);
+  if (!attn_shape_supported(s.H, s.KV, s.RK, s.RV)) return STARKV_ERR_UNSUPPORTED;
+  DecodeLayout lay = decode_layout(s, batch, max_context_len);
+  if (!tight && workspace_bytes < lay.bytes) return STARKV_ERR_WORKSPACE;   // host-only check
+
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return STARKV_ERR_HIP;
+  int grid = resident_grid(s.H, s.KV, s.RK, s.RV, device);
+  if (grid > lay.grid_cap) grid = lay.grid_cap;
+  if (grid < 1) grid = 1;
+  if (tight) {
+    lay = decode_layout(s, batch, max_context_len, grid);
+    if (workspace_bytes < lay.bytes) return STARKV_ERR_WORKSPACE;
+  }
+
+  DecodeLaunch a{};
+  a.s = s;
+  a.batch = batch;
+  a.grid = grid;
+  a.q = q;
+  a.b_k = b_k;
+  a.b_v = b_v;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.scale = scale;
+  a.ws = static_cast<char*>(workspace);
+  a.lay = lay;
+  a.out = out;
+  a.stream = static_cast<hipStream_t>(stream);
+
+  profile_events(a.ev_attn_start, a.ev_attn_stop);
+  return decode_enqueue(a) == hipSuccess ? STARKV_OK : STARKV_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -142,46 +196,8 @@ starkv_status starkv_decode(const starkv_dims* dims, int32_t batch, int32_t max_
                             const void* b_k, const void* b_v, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, const int32_t* context_lens, float scale,
                             void* workspace, size_t workspace_bytes, void* out, void* stream) {
-  const starkv_status ds = check_dims(dims);
-  if (ds != STARKV_OK) return ds;
-  if (!decode_args_ok(dims, batch, max_context_len)) return STARKV_ERR_INVALID_ARG;
-  if (!q || !b_k || !b_v || !k_cache || !v_cache || !block_tables || !context_lens || !workspace || !out)
-    return STARKV_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(b_k, 16) || !aligned(b_v, 2) || !aligned(k_cache, 16) ||
-      !aligned(v_cache, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
-      !aligned(workspace, 256) || !aligned(out, 2))
-    return STARKV_ERR_INVALID_ARG;
-  if (!(scale == scale)) return STARKV_ERR_INVALID_ARG;  // NaN scale
-  const Shape s = shape_of(dims);
-  if (!attn_shape_supported(s.H, s.KV, s.RK, s.RV)) return STARKV_ERR_UNSUPPORTED;
-  const DecodeLayout lay = decode_layout(s, batch, max_context_len);
-  if (workspace_bytes < lay.bytes) return STARKV_ERR_WORKSPACE;
-
-  int device = 0;
-  if (hipGetDevice(&device) != hipSuccess) return STARKV_ERR_HIP;
-  int grid = resident_grid(s.H, s.KV, s.RK, s.RV, device);
-  if (grid > lay.grid_cap) grid = lay.grid_cap;
-  if (grid < 1) grid = 1;
-
-  DecodeLaunch a{};
-  a.s = s;
-  a.batch = batch;
-  a.grid = grid;
-  a.q = q;
-  a.b_k = b_k;
-  a.b_v = b_v;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.scale = scale;
-  a.ws = static_cast<char*>(workspace);
-  a.lay = lay;
-  a.out = out;
-  a.stream = static_cast<hipStream_t>(stream);
-
-  profile_events(a.ev_attn_start, a.ev_attn_stop);
-  return decode_enqueue(a) == hipSuccess ? STARKV_OK : STARKV_ERR_HIP;
+  return decode_call(dims, batch, max_context_len, q, b_k, b_v, k_cache, v_cache, block_tables, context_lens, scale,
+                     workspace, workspace_bytes, false, out, stream);
 }
 
 size_t starkv_prefill_workspace_size(const starkv_dims* dims, int32_t batch, int32_t num_queries,
@@ -202,7 +218,7 @@ starkv_status starkv_prefill(const starkv_dims* dims, int32_t batch, int32_t num
   if (!q || !b_k || !b_v || !k_cache || !v_cache || !block_tables || !query_start || !context_lens || !workspace ||
       !out)
     return STARKV_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(b_k, 16) || !aligned(b_v, 2) || !aligned(k_cache, 16) ||
+  if (!aligned(q, 16) || !aligned(b_k, 16) || !aligned(b_v, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(block_tables, 4) || !aligned(query_start, 4) ||
       !aligned(context_lens, 4) || !aligned(workspace, 256) || !aligned(out, 2))
     return STARKV_ERR_INVALID_ARG;

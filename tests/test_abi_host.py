@@ -190,3 +190,19 @@ def test_check_block_tables_rejects_before_touching_the_device(lib):
     assert f(ctypes.byref(d), 4, ok_ptr, ok_ptr, None, None) == INVALID
     assert f(ctypes.byref(d), 4, ok_ptr, ok_ptr, ctypes.c_void_p(258), None) == INVALID   # misaligned count
     assert f(ctypes.byref(main_dims(block_size=32)), 4, ok_ptr, ok_ptr, ok_ptr, None) == UNSUPPORTED
+
+
+def test_b_v_must_be_16_byte_aligned(lib):
+    """Every up-projection path reads B_v rows as 16-byte vectors."""
+    d = main_dims()
+    p = ctypes.c_void_p(0x1000)
+    bad = ctypes.c_void_p(0x1002)
+    args = [p, p, bad, p, p, p, p]                     # q, b_k, b_v, k_cache, v_cache, tables, lens
+    assert lib.starkv_decode(ctypes.byref(d), 4, 64, *args, 0.1, p, 1 << 30, p, None) == INVALID
+    pargs = [p, p, bad, p, p, p, p, p]                 # q, b_k, b_v, pools, tables, query_start, lens
+    assert lib.starkv_prefill(ctypes.byref(d), 2, 8, 64, *pargs, 0.1, p, 1 << 30, p, None) == INVALID
+
+
+def test_rank_k_bounded(lib):
+    assert call_decode(lib, main_dims(rank_k=264, head_dim=256)) == UNSUPPORTED
+    assert ws_size(lib, main_dims(rank_k=264, head_dim=256), 4, 64) == 0
