@@ -154,6 +154,34 @@ starkv_status starkv_decode(const starkv_dims* dims, int32_t batch, int32_t max_
                             void* out, void* stream);
 
 /*
+ * starkv_decode_noalloc - starkv_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same operation, arguments and results (bit for
+ * bit: the same kernels, launch grid and partial splits), with no workspace
+ * argument.  Its scratch is a fixed device array inside the library,
+ * STARKV_NOALLOC_SCRATCH_BYTES per GPU, held from the library's first use of
+ * that GPU until the process ends; its address is looked up once per device
+ * on the first call made with that device current.  No hipMalloc, hipFree or
+ * other allocating call is made.
+ *
+ *   A call whose workspace (carved for its actual launch grid) would exceed
+ *   the scratch returns STARKV_ERR_WORKSPACE and enqueues nothing.  At 32
+ *   heads and r_v = 1024 that is about (256 + 2*batch) * 128 KiB on a
+ *   256-CU GPU, so batches up to about 120 fit; use starkv_decode with a
+ *   caller workspace beyond that.
+ *   Nothing in the scratch needs to start at zero; every call overwrites what
+ *   it reads.  All calls on one GPU share that GPU's scratch: two calls whose
+ *   kernels may overlap (different streams, or threads without ordering)
+ *   race and corrupt each other's results.  Order them on one stream.
+ */
+#define STARKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+starkv_status starkv_decode_noalloc(const starkv_dims* dims, int32_t batch, int32_t max_context_len,
+                                    const void* q, const void* b_k, const void* b_v,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    float scale, void* out, void* stream);
+
+/*
  * starkv_prefill_workspace_size - bytes of device scratch starkv_prefill needs
  * for this (dims, batch, num_queries, max_context_len).  Host-only; returns 0
  * if the arguments are invalid.

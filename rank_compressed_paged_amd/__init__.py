@@ -13,7 +13,7 @@ import os
 
 __all__ = [
     "Dims", "StarkvError", "load_library", "library_path", "status_string",
-    "decode_workspace_size", "decode", "append", "prefill_workspace_size", "prefill", "profile_begin",
+    "decode_workspace_size", "decode", "decode_noalloc", "append", "prefill_workspace_size", "prefill", "profile_begin",
     "profile_end", "stream_read_probe", "check_block_tables",
     "BLOCK_SIZE",
 ]
@@ -74,6 +74,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.starkv_decode_workspace_size.restype = sz
     lib.starkv_decode.argtypes = [dp, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, vp, sz, vp, vp]
     lib.starkv_decode.restype = ctypes.c_int
+    lib.starkv_decode_noalloc.argtypes = [dp, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp]
+    lib.starkv_decode_noalloc.restype = ctypes.c_int
     lib.starkv_prefill_workspace_size.argtypes = [dp, i32, i32, i32]
     lib.starkv_prefill_workspace_size.restype = sz
     lib.starkv_prefill.argtypes = [dp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, sz, vp, vp]
@@ -217,6 +219,35 @@ def decode(q, b_k, b_v, k_cache, v_cache, block_tables, context_lens, scale, *,
                              float(scale), ctypes.c_void_p(ws_ptr + pad), workspace.numel() - pad,
                              ctypes.c_void_p(optr), _stream(stream))
     _check(code, "starkv_decode")
+    return out
+
+
+def decode_noalloc(q, b_k, b_v, k_cache, v_cache, block_tables, context_lens, scale, out, *,
+                   max_context_len=None, stream=None):
+    """decode() through starkv_decode_noalloc: no workspace, the library's own
+    fixed per-GPU scratch instead (calls on one GPU must not overlap).  `out`
+    [B, H, d] fp16 is required, so nothing is allocated here either."""
+    import torch
+    lib = load_library()
+    batch, heads, d = q.shape
+    dims = dims_of(k_cache, v_cache, block_tables, d, heads=heads)
+    if max_context_len is None:
+        max_context_len = BLOCK_SIZE * block_tables.shape[1]
+    ptrs = [
+        _need(q, "q", torch.float16, 3), _need(b_k, "b_k", torch.float16, 3),
+        _need(b_v, "b_v", torch.float16, 2), _need(k_cache, "k_cache", torch.float16, 4),
+        _need(v_cache, "v_cache", torch.float16, 3), _need(block_tables, "block_tables", torch.int32, 2),
+        _need(context_lens, "context_lens", torch.int32, 1),
+    ]
+    if block_tables.shape[0] != batch or context_lens.shape[0] != batch:
+        raise ValueError("block_tables / context_lens rows must match q's batch")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    optr = _need(out, "out", torch.float16, 3)
+    code = lib.starkv_decode_noalloc(ctypes.byref(dims), batch, int(max_context_len),
+                                     *[ctypes.c_void_p(p) for p in ptrs], float(scale), ctypes.c_void_p(optr),
+                                     _stream(stream))
+    _check(code, "starkv_decode_noalloc")
     return out
 
 

@@ -104,10 +104,10 @@ bool prefill_args_ok(const starkv_dims* d, int32_t batch, int32_t num_queries, i
   return (long long)num_queries * ((max_context_len + kBlock - 1) / kBlock) < (1LL << 40);
 }
 
-// Body of starkv_decode.  `tight`: carve the workspace for the launch grid
-// actually used, instead of for the grid cap that
-// starkv_decode_workspace_size assumes.  The grid, and so every partial split
-// and every result bit, is the same.
+// Shared body of starkv_decode and starkv_decode_noalloc.  `tight`: carve the
+// workspace for the launch grid actually used (the no-allocation scratch),
+// instead of for the grid cap that starkv_decode_workspace_size assumes.  The
+// grid, and so every partial split and every result bit, is the same.
 starkv_status decode_call(const starkv_dims* dims, int32_t batch, int32_t max_context_len, const void* q,
                           const void* b_k, const void* b_v, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, const int32_t* context_lens, float scale, void* workspace,
@@ -160,6 +160,34 @@ starkv_status decode_call(const starkv_dims* dims, int32_t batch, int32_t max_co
 
 }  // namespace
 
+// Device scratch of starkv_decode_noalloc: one copy per GPU, alive until the
+// process ends.  Host code never uses this name as an address (on the host it
+// is only a stand-in): the device address comes from hipGetSymbolAddress,
+// once per device, and is kept in g_scratch.
+constexpr size_t kScratchBytes = (size_t)STARKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// Device address of this device's scratch (set up on the first call on it,
+// with the device current).
+starkv_status scratch_of(int device, void** ptr) {
+  if (device < 0 || device >= kMaxDevices) return STARKV_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[device]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return STARKV_ERR_HIP;
+    g_scratch[device] = p;
+  }
+  *ptr = g_scratch[device];
+  return STARKV_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* starkv_status_string(starkv_status status) {
@@ -198,6 +226,19 @@ starkv_status starkv_decode(const starkv_dims* dims, int32_t batch, int32_t max_
                             void* workspace, size_t workspace_bytes, void* out, void* stream) {
   return decode_call(dims, batch, max_context_len, q, b_k, b_v, k_cache, v_cache, block_tables, context_lens, scale,
                      workspace, workspace_bytes, false, out, stream);
+}
+
+starkv_status starkv_decode_noalloc(const starkv_dims* dims, int32_t batch, int32_t max_context_len, const void* q,
+                                    const void* b_k, const void* b_v, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                    void* out, void* stream) {
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return STARKV_ERR_HIP;
+  void* ws = nullptr;
+  const starkv_status st = scratch_of(device, &ws);
+  if (st != STARKV_OK) return st;
+  return decode_call(dims, batch, max_context_len, q, b_k, b_v, k_cache, v_cache, block_tables, context_lens, scale,
+                     ws, kScratchBytes, true, out, stream);
 }
 
 size_t starkv_prefill_workspace_size(const starkv_dims* dims, int32_t batch, int32_t num_queries,
