@@ -34,8 +34,10 @@ weights applied to c_v before B_v) as re-association of the same products,
 the method's output is exactly ordinary single-query softmax attention over
 the reconstructed keys and values.  So the oracle reconstructs K and V in
 fp64 and runs textbook attention.  Prefill (a chunk of new tokens per
-sequence) is the same attention with a causal mask.  Every pin of this file
-lives in tests/test_oracle.py.
+sequence) is the same attention with a causal mask.  The uncompressed paged
+decode that the pages benchmark against is the same attention over stored
+full-width keys and values.  Every pin of this file lives in
+tests/test_oracle.py.
 """
 
 from __future__ import annotations
@@ -86,6 +88,43 @@ def decode(q, b_k, b_v, k_pool, v_pool, block_tables, context_lens, scale, block
             scores = float(scale) * (keys @ q[b, h])       # [L]
             w = np.exp(scores - scores.max())
             out[b, h] = (w @ values[:, kv * d:(kv + 1) * d]) / w.sum()
+    return out
+
+
+def decode_uncompressed(q, k_pool, v_pool, block_tables, context_lens, scale, block_size=16):
+    """Single-token attention over a plain (uncompressed) paged fp16 KV cache.
+
+    This is the baseline the pages compare their decode kernel with (Proxima
+    landing page, "Decode kernel" table; Proxima README, kernel bench table:
+    the same paged decode over full-width keys and values).  Layout, with
+    H_kv key/value heads and head_dim d:
+      k_pool[p, g, slot, :]  key of key/value head g      [NB, H_kv, 16, d]
+      v_pool[p, g, slot, :]  value of key/value head g    [NB, H_kv, 16, d]
+    Position t of sequence b lives in block block_tables[b, t // 16], slot
+    t % 16; query head h reads key/value head h // (H / H_kv).
+    out[b, h] = softmax(scale * K_g q[b, h]) . V_g over the context_lens[b]
+    positions; a sequence of length 0 yields a zero row.  Returns fp64 [B, H, d].
+    """
+    q = np.asarray(q).astype(F64)
+    kp = np.asarray(k_pool)
+    vp = np.asarray(v_pool)
+    nb, nh, d = q.shape
+    group = nh // kp.shape[1]
+    out = np.zeros((nb, nh, d), F64)
+    for b in range(nb):
+        length = int(context_lens[b])
+        if length == 0:
+            continue
+        t = np.arange(length)
+        phys = np.asarray(block_tables[b])[t // block_size]
+        slot = t % block_size
+        keys = kp[phys, :, slot, :].astype(F64)            # [L, H_kv, d]
+        values = vp[phys, :, slot, :].astype(F64)          # [L, H_kv, d]
+        for h in range(nh):
+            g = h // group
+            scores = float(scale) * (keys[:, g, :] @ q[b, h])
+            w = np.exp(scores - scores.max())
+            out[b, h] = (w @ values[:, g, :]) / w.sum()
     return out
 
 

@@ -273,6 +273,41 @@ def make_case(seed: int, batch: int, heads: int, head_dim: int, rank_k: int, ran
                 heads=heads, kv_heads=kvh, head_dim=head_dim, rank_k=rank_k, rank_v=rank_v)
 
 
+def make_uncompressed_case(seed: int, batch: int, heads: int, head_dim: int, context_lens, *,
+                           kv_heads: int | None = None, key: tuple = (), sentinel: bool = True,
+                           spare_tokens: int = 0):
+    """Inputs of the plain (uncompressed) paged decode that the latent path is
+    compared with: the same block tables as make_case() draws for the same
+    seed, lengths and key, and full-width fp16 keys and values
+      k_pool, v_pool [num_blocks, H_kv, 16, d]  ~ N(0, 1)
+    with q ~ N(0, 1)/sqrt(d).  Unused slots hold the NaN sentinel."""
+    kvh = heads if kv_heads is None else kv_heads
+    context_lens = np.asarray(context_lens, np.int32)
+    assert len(context_lens) == batch
+    need = (context_lens.astype(np.int64) + spare_tokens + BLOCK_SIZE - 1) // BLOCK_SIZE
+    bt, nb = make_block_tables(seed, need, key=key)
+    q = normal_f16(seed, (4, *key), (batch, heads, head_dim), scale=1.0 / math.sqrt(head_dim))
+    k_pool = normal_f16(seed, (11, *key), (nb, kvh, BLOCK_SIZE, head_dim))
+    v_pool = normal_f16(seed, (12, *key), (nb, kvh, BLOCK_SIZE, head_dim))
+    if sentinel:
+        touched = np.zeros(nb, bool)
+        kb = k_pool.view(np.uint16)
+        vb = v_pool.view(np.uint16)
+        for b, length in enumerate(context_lens):
+            full, rem = divmod(int(length), BLOCK_SIZE)
+            touched[bt[b, :full]] = True
+            if rem:
+                p = int(bt[b, full])
+                touched[p] = True
+                kb[p, :, rem:, :] = FP16_NAN_BITS
+                vb[p, :, rem:, :] = FP16_NAN_BITS
+        idle = np.nonzero(~touched)[0]
+        kb[idle] = FP16_NAN_BITS
+        vb[idle] = FP16_NAN_BITS
+    return dict(q=q, k_pool=k_pool, v_pool=v_pool, block_tables=bt, context_lens=context_lens, num_blocks=nb,
+                heads=heads, kv_heads=kvh, head_dim=head_dim)
+
+
 def make_prefill_case(seed: int, heads: int, head_dim: int, rank_k: int, rank_v: int, context_lens, chunks, *,
                       kv_heads: int | None = None, key: tuple = (), sentinel: bool = True, spare_tokens: int = 0):
     """A prefill call's inputs: the decode case's cache plus one chunk per sequence.

@@ -516,3 +516,116 @@ def test_prefill_first_token_sees_only_itself_and_empty_chunks_skip():
     d = case["head_dim"]
     for h in range(case["heads"]):
         np.testing.assert_allclose(got[0, h], v_row[h * d:(h + 1) * d], rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------- uncompressed paged decode pins
+def scatter_dense(k_list, v_list, tables, nb, fill=np.nan):
+    """Place per-sequence keys/values [L, H_kv, d] into [NB, H_kv, 16, d] pools
+    by walking each table with a counter."""
+    heads, d = k_list[0].shape[1:]
+    kp = np.full((nb, heads, BS, d), fill, F64)
+    vp = np.full((nb, heads, BS, d), fill, F64)
+    for b, (k, v) in enumerate(zip(k_list, v_list)):
+        for t, (p, j) in enumerate(walk_slots(tables[b], len(k))):
+            kp[p, :, j, :] = k[t]
+            vp[p, :, j, :] = v[t]
+    return kp, vp
+
+
+def dense_case(seed, lens, heads=3, kv_heads=None, d=4):
+    rng = np.random.default_rng(seed)
+    kvh = heads if kv_heads is None else kv_heads
+    bt, nb = random_tables(rng, lens, spare=2)
+    ks = [rng.standard_normal((max(n, 1), kvh, d))[:n] for n in lens]
+    vs = [rng.standard_normal((max(n, 1), kvh, d))[:n] for n in lens]
+    kp, vp = scatter_dense([k if len(k) else np.zeros((0, kvh, d)) for k in ks],
+                           [v if len(v) else np.zeros((0, kvh, d)) for v in vs], bt, nb)
+    q = rng.standard_normal((len(lens), heads, d))
+    return dict(q=q, ks=ks, vs=vs, kp=kp, vp=vp, bt=bt, lens=np.array(lens), nb=nb)
+
+
+@pytest.mark.parametrize("kv_heads", [None, 1])
+def test_uncompressed_equals_sdpa(kv_heads):
+    """Against torch SDPA in fp64 on the contiguous keys and values."""
+    c = dense_case(31, [40, 23, 1], heads=4, kv_heads=kv_heads, d=8)
+    scale = 0.41
+    got = oracle.decode_uncompressed(c["q"], c["kp"], c["vp"], c["bt"], c["lens"], scale)
+    heads = c["q"].shape[1]
+    kvh = c["kp"].shape[1]
+    for b in range(len(c["lens"])):
+        for h in range(heads):
+            g = h * kvh // heads
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(c["q"][b, h][None, None, None, :]),
+                torch.from_numpy(np.ascontiguousarray(c["ks"][b][:, g])[None, None]),
+                torch.from_numpy(np.ascontiguousarray(c["vs"][b][:, g])[None, None]), scale=scale)
+            np.testing.assert_allclose(got[b, h], ref.numpy()[0, 0, 0], rtol=1e-12, atol=1e-13)
+
+
+def test_uncompressed_bruteforce_with_grouped_heads():
+    c = dense_case(32, [19, 0, 33], heads=4, kv_heads=2, d=3)
+    scale = 1.7
+    got = oracle.decode_uncompressed(c["q"], c["kp"], c["vp"], c["bt"], c["lens"], scale)
+    for b, n in enumerate(c["lens"]):
+        slots = walk_slots(c["bt"][b], n)
+        for h in range(4):
+            g = h // 2
+            if not slots:
+                assert not got[b, h].any()
+                continue
+            sc = [scale * math.fsum(float(c["kp"][p, g, j, i]) * float(c["q"][b, h, i]) for i in range(3))
+                  for p, j in slots]
+            top = max(sc)
+            w = [math.exp(s - top) for s in sc]
+            tot = math.fsum(w)
+            for i in range(3):
+                ref = math.fsum(w[t] * float(c["vp"][p, g, j, i]) for t, (p, j) in enumerate(slots)) / tot
+                assert abs(got[b, h, i] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_uncompressed_equals_latent_oracle_on_reconstructed_cache():
+    """Filling the plain pools with K = C_k B_k and V = (C_v B_v) head slices
+    (fp64, no rounding) gives the latent decode's result: the two oracle
+    functions agree on what attention over the same keys and values is."""
+    case = small_case(seed=33, heads=2, head_dim=4, rank_k=3, rank_v=6, lens=(37, 0, 16, 1))
+    bt, lens = case["block_tables"], case["context_lens"]
+    bk = case["b_k"].astype(F64)
+    bv = case["b_v"].astype(F64)
+    H, d = 2, 4
+    ks, vs = [], []
+    for b, n in enumerate(lens):
+        slots = walk_slots(bt[b], n)
+        ck = np.array([case["k_pool"][p, :, j, :] for p, j in slots], F64).reshape(n, H, 3)
+        cv = np.array([case["v_pool"][p, :, j] for p, j in slots], F64).reshape(n, 6)
+        ks.append(np.einsum("thr,hrd->thd", ck, bk))
+        vs.append((cv @ bv).reshape(n, H, d))
+    kp, vp = scatter_dense(ks, vs, bt, case["num_blocks"])
+    for scale in (0.5, 3.0):
+        a = oracle.decode_uncompressed(case["q"], kp, vp, bt, lens, scale)
+        b = run_oracle(case, scale)
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+def test_uncompressed_closed_forms_and_invariances():
+    c = dense_case(34, [21, 1, 0, 50], heads=2, d=5)
+    args = (c["kp"], c["vp"], c["bt"], c["lens"])
+    base = oracle.decode_uncompressed(c["q"], *args, 0.8)
+    # zero-length row is zero; one token returns its value row
+    assert not base[2].any()
+    np.testing.assert_allclose(base[1], c["vs"][1][0], rtol=1e-15)
+    # q = 0: mean of the value rows
+    mean = oracle.decode_uncompressed(np.zeros_like(c["q"]), *args, 0.8)
+    for b in (0, 3):
+        np.testing.assert_allclose(mean[b], c["vs"][b].mean(axis=0), rtol=1e-12)
+    # moving physical blocks (and rewriting the tables) changes nothing
+    perm = np.random.default_rng(5).permutation(c["nb"])
+    kp2 = np.empty_like(c["kp"])
+    vp2 = np.empty_like(c["vp"])
+    kp2[perm] = c["kp"]
+    vp2[perm] = c["vp"]
+    bt2 = c["bt"].copy()
+    bt2[bt2 >= 0] = perm[bt2[bt2 >= 0]]
+    moved = oracle.decode_uncompressed(c["q"], kp2, vp2, bt2, c["lens"], 0.8)
+    assert np.array_equal(moved, base)
+    # NaN in unread slots never matters (pools were filled with NaN outside the sequences)
+    assert np.isnan(c["kp"]).any() and np.isfinite(base).all()

@@ -66,3 +66,17 @@ def test_config_shapes():
     case = synth.make_config_case(c[1])
     assert case["k_pool"].shape == (16, 4, 16, 16) and case["v_pool"].shape == (16, 64, 16)
     assert sorted(case["block_tables"][0].tolist()) == list(range(16))
+
+
+def test_uncompressed_case_shares_the_latent_case_tables():
+    lens = np.array([300, 0, 47, 1000], np.int32)
+    a = synth.make_case(77, 4, 4, 64, 16, 64, lens)
+    b = synth.make_uncompressed_case(77, 4, 4, 64, lens)
+    assert np.array_equal(a["block_tables"], b["block_tables"])
+    assert np.array_equal(a["q"], b["q"])
+    assert b["k_pool"].shape == (a["num_blocks"], 4, 16, 64) == b["v_pool"].shape
+    # unused slots poisoned, used ones finite
+    t = np.arange(300)
+    p, j = a["block_tables"][0, t // 16], t % 16
+    assert np.isfinite(b["k_pool"][p, :, j, :]).all() and np.isfinite(b["v_pool"][p, :, j, :]).all()
+    assert np.isnan(b["k_pool"][a["block_tables"][0, 300 // 16], :, 300 % 16:, :]).all()
