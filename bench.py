@@ -18,6 +18,8 @@ Prints one JSON line.  Options:
   --config N               time decode workload N (1-7) instead; own JSON line
   --graph                  with --config: also time HIP-graph replays of the step
   --prefill N              time prefill workload N (1-3) instead; own JSON line
+  --grid                   time the pages' seq x batch grid: latent decode vs the
+                           uncompressed paged decode baseline; own JSON line
   --calib-copy             run only a plain device copy of known size (for
                            scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
 """
@@ -282,6 +284,104 @@ def config_report(cfg_id: int, steps: int, warmup: int, graph: bool = False):
 
 PEAK_MFMA_F16_TFLOPS = 2500.0
 
+# The pages' kernel comparison (Proxima landing page, "Decode kernel" table;
+# Proxima README, kernel bench table): latent decode speed over FlashAttention-2
+# on an NVIDIA L4, 32-head MHA, head size 128, rank 64, fp16.  Context only.
+PAGES_L4_SPEEDUP = {1024: (0.36, 1.23, 1.40), 2048: (0.57, 1.33, 1.43), 4096: (0.84, 1.40, 1.43),
+                    8192: (0.87, 1.44, 1.46)}
+
+
+def speedup_grid(reps: int, warmup: int):
+    """The pages' speedup grid on this GPU: for seq in {1024..8192} and batch
+    in {1, 16, 64}, one starkv_decode call (query projection, latent
+    attention, merge, up-projection; 32 heads, d 128, r_k 64, r_v 1024)
+    against one starkv_uncompressed_decode call (plain paged fp16 K/V, same
+    block tables and lengths).  Each call is timed alone between HIP events
+    (median of `reps`), after a 1 GiB cache flush when the data it reads
+    would otherwise stay in the 256 MB last-level cache.  Both attention
+    kernels' HBM roofline fractions are reported (algorithmic bytes: 6,144 B
+    per latent token, H*d*2*2 = 16,384 B per uncompressed token)."""
+    import torch
+
+    import rank_compressed_paged_amd as starkv
+    from rank_compressed_paged_amd import synth
+
+    dev = torch.device("cuda:0")
+    H, D, RK, RV = 32, 128, 64, 1024
+    seqs, batches = (1024, 2048, 4096, 8192), (1, 16, 64)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    rows = []
+
+    def timed(call, cold):
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        starkv.profile_begin()
+        ts = []
+        for i in range(reps):
+            if cold:
+                flush.fill_(i & 0xFF)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        attn_ms, n = starkv.profile_end()
+        return float(np.median(ts)), attn_ms / n
+
+    for batch in batches:
+        seed = 20261203 + 500 + batch
+        full = np.full(batch, max(seqs), np.int32)
+        lat = synth.make_case(seed, batch, H, D, RK, RV, full, sentinel=False)
+        pla = synth.make_uncompressed_case(seed, batch, H, D, full, sentinel=False)
+        gl = {k: torch.from_numpy(v).to(dev) for k, v in lat.items() if isinstance(v, np.ndarray)}
+        gp = {k: torch.from_numpy(v).to(dev) for k, v in pla.items() if isinstance(v, np.ndarray)}
+        del lat, pla
+        for seq in seqs:
+            lens = torch.full((batch,), seq, dtype=torch.int32, device=dev)
+            dims = starkv.dims_of(gl["k_pool"], gl["v_pool"], gl["block_tables"], D, heads=H)
+            ws = torch.empty(starkv.decode_workspace_size(dims, batch, seq) + 256, dtype=torch.uint8, device=dev)
+            out_l = torch.empty_like(gl["q"])
+            out_p = torch.empty_like(gp["q"])
+            wsp = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+
+            def call_latent():
+                starkv.decode(gl["q"], gl["b_k"], gl["b_v"], gl["k_pool"], gl["v_pool"], gl["block_tables"], lens,
+                              scale, max_context_len=seq, workspace=ws, out=out_l)
+
+            def call_plain():
+                starkv.uncompressed_decode(gp["q"], gp["k_pool"], gp["v_pool"], gp["block_tables"], lens, scale,
+                                           max_context_len=seq, workspace=wsp, out=out_p)
+
+            tokens = batch * seq
+            plain_bytes = tokens * H * D * 2 * 2
+            latent_bytes = tokens * (H * RK + RV) * 2
+            cold = plain_bytes < (1 << 30)
+            lat_ms, lat_attn = timed(call_latent, cold)
+            pla_ms, pla_attn = timed(call_plain, cold)
+            rows.append({
+                "seq": seq, "batch": batch,
+                "latent_ms": lat_ms, "uncompressed_ms": pla_ms, "speedup": pla_ms / lat_ms,
+                "latent_attn_kernel_us": lat_attn * 1e3, "uncompressed_attn_kernel_us": pla_attn * 1e3,
+                "attn_kernel_speedup": pla_attn / lat_attn,
+                "latent_attn_frac_of_8tbps": latent_bytes / (lat_attn / 1e3) / 1e9 / PEAK_HBM_GBPS,
+                "uncompressed_attn_frac_of_8tbps": plain_bytes / (pla_attn / 1e3) / 1e9 / PEAK_HBM_GBPS,
+                "cache_flushed": cold,
+                "pages_l4_vs_fa2": PAGES_L4_SPEEDUP[seq][batches.index(batch)],
+            })
+            print(f"# seq {seq} batch {batch}: latent {lat_ms * 1e3:.1f} us, uncompressed {pla_ms * 1e3:.1f} us, "
+                  f"speedup {pla_ms / lat_ms:.2f}", file=sys.stderr, flush=True)
+        del gl, gp
+        torch.cuda.empty_cache()
+    print(json.dumps({
+        "metric": "decode call speedup of the latent path over an uncompressed paged fp16 decode (>1 = latent faster)",
+        "workload": "32 heads, head_dim 128, r_k 64, r_v 1024, block size 16; seq x batch grid of the pages' kernel "
+                    "comparison; speedup = uncompressed call time / latent call time",
+        "reps": reps, "warmup": warmup, "grid": rows}), flush=True)
+
 
 def prefill_report(cfg_id: int, steps: int, warmup: int):
     """Time prefill workload N: a step appends every sequence's chunk (its K/V
@@ -360,6 +460,8 @@ def main():
                     help="time workload 1-7 instead (prints its own JSON line)")
     ap.add_argument("--prefill", type=int, default=0,
                     help="time prefill workload 1-3 instead (prints its own JSON line)")
+    ap.add_argument("--grid", action="store_true",
+                    help="time the seq x batch speedup grid over the uncompressed paged decode instead")
     ap.add_argument("--graph", action="store_true",
                     help="with --config: also time the step captured in a HIP graph")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph timing of the headline step")
@@ -375,6 +477,9 @@ def main():
         return
     if args.prefill:
         prefill_report(args.prefill, args.steps, args.warmup)
+        return
+    if args.grid:
+        speedup_grid(args.steps, args.warmup)
         return
 
     import torch

@@ -230,6 +230,34 @@ starkv_status starkv_prefill(const starkv_dims* dims, int32_t batch, int32_t num
                              size_t workspace_bytes, void* out, void* stream);
 
 /*
+ * starkv_uncompressed_decode - the baseline, not the method: single-query
+ * attention over a plain paged fp16 KV cache holding full-width keys and
+ * values, as the pages' decode kernel is measured against (Proxima landing
+ * page, "Decode kernel" table; Proxima README, kernel bench table: the latent
+ * kernel's speed relative to an uncompressed paged decode at several batch
+ * sizes and sequence lengths).  Same block tables and lengths as
+ * starkv_decode; the pools hold the keys and values themselves:
+ *
+ *   k_cache, v_cache  [num_blocks][H_kv][16][d] fp16, 16-byte aligned
+ *   out[b,h,:] = softmax(scale * K_g q[b,h]) . V_g   (g = h / (H/H_kv))
+ *
+ * dims: num_heads, head_dim, num_kv_heads, block_size, num_blocks and
+ * max_blocks_per_seq as for starkv_decode; rank_k and rank_v are not used.
+ * Built for head_dim in {64, 128} and H/H_kv in {1, 2, 4, 8}; other shapes ->
+ * STARKV_ERR_UNSUPPORTED.  q [B][H][d] fp16 16-byte aligned, out [B][H][d]
+ * fp16; context_lens[b] == 0 gives a zero row.  workspace: device scratch of
+ * at least starkv_uncompressed_decode_workspace_size() bytes, 256-byte
+ * aligned, garbage afterwards.  Errors and ownership as for starkv_decode.
+ */
+size_t starkv_uncompressed_decode_workspace_size(const starkv_dims* dims, int32_t batch,
+                                                 int32_t max_context_len);
+starkv_status starkv_uncompressed_decode(const starkv_dims* dims, int32_t batch, int32_t max_context_len,
+                                         const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         float scale, void* workspace, size_t workspace_bytes,
+                                         void* out, void* stream);
+
+/*
  * starkv_check_block_tables - debug check of the device-side contract that
  * starkv_decode and starkv_prefill rely on but cannot verify synchronously
  * (block tables as in the PagedAttention page's block-level management item):
@@ -256,8 +284,9 @@ const char* starkv_status_string(starkv_status status);
 /*
  * Measurement hooks (host-only, process-wide, not for use while another
  * thread is decoding).  Between starkv_profile_begin() and
- * starkv_profile_end(), every starkv_decode and starkv_prefill call brackets
- * its latent attention kernel with a pair of HIP events on its own stream (up
+ * starkv_profile_end(), every starkv_decode, starkv_decode_noalloc,
+ * starkv_prefill and starkv_uncompressed_decode call brackets its attention
+ * kernel with a pair of HIP events on its own stream (up
  * to 4096 calls).  starkv_profile_end() waits for those events, writes the summed
  * kernel time in milliseconds and the number of bracketed launches, and
  * releases the events.  Returns STARKV_ERR_HIP if an event call failed.

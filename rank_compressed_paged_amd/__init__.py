@@ -13,7 +13,7 @@ import os
 
 __all__ = [
     "Dims", "StarkvError", "load_library", "library_path", "status_string",
-    "decode_workspace_size", "decode", "decode_noalloc", "append", "prefill_workspace_size", "prefill", "profile_begin",
+    "decode_workspace_size", "decode", "decode_noalloc", "uncompressed_decode", "append", "prefill_workspace_size", "prefill", "profile_begin",
     "profile_end", "stream_read_probe", "check_block_tables",
     "BLOCK_SIZE",
 ]
@@ -76,6 +76,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.starkv_decode.restype = ctypes.c_int
     lib.starkv_decode_noalloc.argtypes = [dp, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp]
     lib.starkv_decode_noalloc.restype = ctypes.c_int
+    lib.starkv_uncompressed_decode_workspace_size.argtypes = [dp, i32, i32]
+    lib.starkv_uncompressed_decode_workspace_size.restype = sz
+    lib.starkv_uncompressed_decode.argtypes = [dp, i32, i32, vp, vp, vp, vp, vp, f32, vp, sz, vp, vp]
+    lib.starkv_uncompressed_decode.restype = ctypes.c_int
     lib.starkv_prefill_workspace_size.argtypes = [dp, i32, i32, i32]
     lib.starkv_prefill_workspace_size.restype = sz
     lib.starkv_prefill.argtypes = [dp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, sz, vp, vp]
@@ -248,6 +252,49 @@ def decode_noalloc(q, b_k, b_v, k_cache, v_cache, block_tables, context_lens, sc
                                      *[ctypes.c_void_p(p) for p in ptrs], float(scale), ctypes.c_void_p(optr),
                                      _stream(stream))
     _check(code, "starkv_decode_noalloc")
+    return out
+
+
+def uncompressed_decode(q, k_cache, v_cache, block_tables, context_lens, scale, *,
+                        max_context_len=None, workspace=None, out=None, stream=None):
+    """The baseline the latent path is compared with: single-query attention
+    over a plain paged fp16 cache of full-width keys and values.
+
+    q [B, H, d] fp16; k_cache, v_cache [NB, H_kv, 16, d] fp16; block_tables
+    [B, MB] int32; context_lens [B] int32.  Returns out [B, H, d] fp16.
+    """
+    import torch
+    lib = load_library()
+    batch, heads, d = q.shape
+    nb, kvh, bs, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache / v_cache must be [NB, H_kv, 16, d] with q's head_dim")
+    dims = Dims.make(heads, d, 1, 32, nb, block_tables.shape[1], block_size=bs, kv_heads=kvh)
+    if max_context_len is None:
+        max_context_len = BLOCK_SIZE * block_tables.shape[1]
+    ptrs = [
+        _need(q, "q", torch.float16, 3), _need(k_cache, "k_cache", torch.float16, 4),
+        _need(v_cache, "v_cache", torch.float16, 4), _need(block_tables, "block_tables", torch.int32, 2),
+        _need(context_lens, "context_lens", torch.int32, 1),
+    ]
+    if block_tables.shape[0] != batch or context_lens.shape[0] != batch:
+        raise ValueError("block_tables / context_lens rows must match q's batch")
+    need = lib.starkv_uncompressed_decode_workspace_size(ctypes.byref(dims), batch, int(max_context_len))
+    if need == 0:
+        _check(2 if heads % kvh == 0 else 1, "starkv_uncompressed_decode_workspace_size")
+    if workspace is None:
+        workspace = _scratch(need + 256, q.device, stream)
+    ws_ptr = _need(workspace, "workspace", torch.uint8, 1)
+    pad = (-ws_ptr) % 256
+    if out is None:
+        out = torch.empty_like(q)
+        _own_out(out, q.device, stream)
+    optr = _need(out, "out", torch.float16, 3)
+    code = lib.starkv_uncompressed_decode(ctypes.byref(dims), batch, int(max_context_len),
+                                          *[ctypes.c_void_p(p) for p in ptrs], float(scale),
+                                          ctypes.c_void_p(ws_ptr + pad), workspace.numel() - pad,
+                                          ctypes.c_void_p(optr), _stream(stream))
+    _check(code, "starkv_uncompressed_decode")
     return out
 
 

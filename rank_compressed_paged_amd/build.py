@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libstarkv.so")
 SOURCES = ["starkv_api.hip", "decode_kernels.hip", "attn_kernel.hip", "append_kernels.hip", "prefill_kernels.hip",
-           "probe_kernels.hip"]
+           "uncompressed_kernels.hip", "probe_kernels.hip"]
 ARCH = "gfx950"
 
 

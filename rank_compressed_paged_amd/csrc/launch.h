@@ -100,6 +100,41 @@ struct AppendLaunch {
 
 hipError_t append_enqueue(const AppendLaunch& a);
 
+// ------------------------------------------------ uncompressed paged decode
+// Partition of a sequence per workgroup: the largest power of two in
+// [kPlainMinPB, kPlainMaxPB] blocks that still leaves kPlainTargetWGs
+// workgroups (host-only, so the workspace size needs no device query).
+constexpr int kPlainMaxPB = 64;
+constexpr int kPlainMinPB = 4;
+constexpr long long kPlainTargetWGs = 1024;
+
+struct PlainLayout {
+  int pb;                // blocks per partition
+  int maxparts;          // partitions of the longest sequence
+  size_t off_acc, off_ml, bytes;   // bytes = 0 when no sequence needs a merge
+};
+
+PlainLayout plain_layout(int batch, int H, int KV, int D, int max_context_len);
+bool plain_shape_supported(int H, int KV, int D);
+
+struct PlainLaunch {
+  int batch, H, KV, D, MB;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float scale;
+  char* ws;
+  PlainLayout lay;
+  void* out;
+  hipStream_t stream;
+  hipEvent_t ev_start;   // optional: brackets the attention kernel
+  hipEvent_t ev_stop;
+};
+
+hipError_t plain_enqueue(const PlainLaunch& a);
+
 // ---------------------------------------------------------------- prefill
 constexpr int kPfRows = 64;                  // query rows per tile
 constexpr int kPfWaves = 8;

@@ -104,6 +104,21 @@ bool prefill_args_ok(const starkv_dims* d, int32_t batch, int32_t num_queries, i
   return (long long)num_queries * ((max_context_len + kBlock - 1) / kBlock) < (1LL << 40);
 }
 
+// Dims of the uncompressed baseline: rank fields are not used.
+starkv_status check_plain_dims(const starkv_dims* d) {
+  if (!d) return STARKV_ERR_INVALID_ARG;
+  if (d->num_heads <= 0 || d->head_dim <= 0 || d->block_size <= 0 || d->num_blocks <= 0 ||
+      d->max_blocks_per_seq <= 0)
+    return STARKV_ERR_INVALID_ARG;
+  if (d->num_kv_heads < 0 || (d->num_kv_heads > 0 && d->num_heads % d->num_kv_heads != 0))
+    return STARKV_ERR_INVALID_ARG;
+  if (d->block_size != kBlock) return STARKV_ERR_UNSUPPORTED;
+  const int kv = d->num_kv_heads > 0 ? d->num_kv_heads : d->num_heads;
+  if (!plain_shape_supported(d->num_heads, kv, d->head_dim)) return STARKV_ERR_UNSUPPORTED;
+  if ((long long)d->num_heads * d->head_dim > (1 << 20)) return STARKV_ERR_UNSUPPORTED;
+  return STARKV_OK;
+}
+
 // Shared body of starkv_decode and starkv_decode_noalloc.  `tight`: carve the
 // workspace for the launch grid actually used (the no-allocation scratch),
 // instead of for the grid cap that starkv_decode_workspace_size assumes.  The
@@ -323,6 +338,47 @@ starkv_status starkv_append(const starkv_dims* dims, int32_t n_tokens, const voi
   a.v_cache = v_cache;
   a.stream = static_cast<hipStream_t>(stream);
   return append_enqueue(a) == hipSuccess ? STARKV_OK : STARKV_ERR_HIP;
+}
+
+size_t starkv_uncompressed_decode_workspace_size(const starkv_dims* dims, int32_t batch, int32_t max_context_len) {
+  if (check_plain_dims(dims) != STARKV_OK || !decode_args_ok(dims, batch, max_context_len)) return 0;
+  const int kv = dims->num_kv_heads > 0 ? dims->num_kv_heads : dims->num_heads;
+  const PlainLayout lay = plain_layout(batch, dims->num_heads, kv, dims->head_dim, max_context_len);
+  return lay.bytes > 0 ? lay.bytes : 256;
+}
+
+starkv_status starkv_uncompressed_decode(const starkv_dims* dims, int32_t batch, int32_t max_context_len,
+                                         const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                         void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const starkv_status ds = check_plain_dims(dims);
+  if (ds != STARKV_OK) return ds;
+  if (!decode_args_ok(dims, batch, max_context_len)) return STARKV_ERR_INVALID_ARG;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !workspace || !out)
+    return STARKV_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_tables, 4) ||
+      !aligned(context_lens, 4) || !aligned(workspace, 256) || !aligned(out, 2))
+    return STARKV_ERR_INVALID_ARG;
+  if (!(scale == scale)) return STARKV_ERR_INVALID_ARG;
+  PlainLaunch a{};
+  a.batch = batch;
+  a.H = dims->num_heads;
+  a.KV = dims->num_kv_heads > 0 ? dims->num_kv_heads : dims->num_heads;
+  a.D = dims->head_dim;
+  a.MB = dims->max_blocks_per_seq;
+  a.lay = plain_layout(batch, a.H, a.KV, a.D, max_context_len);
+  if (workspace_bytes < (a.lay.bytes > 0 ? a.lay.bytes : 256)) return STARKV_ERR_WORKSPACE;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.scale = scale;
+  a.ws = static_cast<char*>(workspace);
+  a.out = out;
+  a.stream = static_cast<hipStream_t>(stream);
+  profile_events(a.ev_start, a.ev_stop);
+  return plain_enqueue(a) == hipSuccess ? STARKV_OK : STARKV_ERR_HIP;
 }
 
 starkv_status starkv_profile_begin(void) {
