@@ -140,6 +140,82 @@ def cpu_baseline(case, cfg, k_new, v_new, scale, budget_s=12.0):
                       f"{int(lens[0]) + 1} tokens), fp64 numpy, {dt:.1f} s wall"}
 
 
+def oracle_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_config(cfg, budget_s=10.0):
+    """The oracle on a bounded sample of decode workload `cfg`: whole steps
+    (append the step's new token, then decode over the grown context) of one
+    (layer, sequence) pair at a time, in order, until the budget is spent.
+    The job's oracle time is the sample's mean per pair times batch x layers;
+    tokens/s = batch / that time.  Inputs are regenerated per layer (not
+    timed) from the same seeds as the GPU run."""
+    import oracle
+    from rank_compressed_paged_amd import synth
+    pairs, spent, t_all = 0, 0.0, time.perf_counter()
+    for layer in range(cfg.layers):
+        case = synth.make_config_case(cfg, layer=layer, spare_tokens=1)
+        k_new, v_new = synth.make_new_rows(cfg.seed, cfg.batch, cfg.kv, cfg.head_dim, key=(layer,))
+        scale = 1.0 / math.sqrt(cfg.head_dim)
+        for b in range(cfg.batch):
+            L = int(case["context_lens"][b])
+            nblk = (L + 1 + 15) // 16
+            blocks = case["block_tables"][b, :nblk]
+            kp, vp = case["k_pool"][blocks], case["v_pool"][blocks]      # compact pool: input preparation
+            table = np.arange(nblk, dtype=np.int32)[None]
+            t0 = time.perf_counter()
+            kp, vp = oracle.append(k_new[b:b + 1], v_new[b:b + 1], case["b_k"], case["b_v"], table, [0], [L], kp, vp)
+            oracle.decode(case["q"][b:b + 1], case["b_k"], case["b_v"], kp, vp, table, np.array([L + 1]), scale)
+            spent += time.perf_counter() - t0
+            pairs += 1
+            if spent >= budget_s:
+                break
+        del case
+        if spent >= budget_s:
+            break
+    per_pair = spent / pairs
+    job_s = per_pair * cfg.batch * cfg.layers
+    return {"value": cfg.batch / job_s, "unit": "tokens/s", "cores": oracle_threads(), "kind": "oracle",
+            "sample": f"{pairs} of {cfg.batch * cfg.layers} (layer, sequence) pairs, one full step each (append 1 "
+                      f"token + decode), {spent:.1f} s of oracle time scaled to the whole step; fp64 numpy; "
+                      f"{time.perf_counter() - t_all:.1f} s wall with input generation"}
+
+
+def cpu_baseline_prefill(cfg, case, k_new, v_new, budget_s=10.0):
+    """The oracle on a bounded sample of prefill workload `cfg`: one
+    sequence's chunk at a time (append its rows, then causal attention of the
+    chunk), scaled to the batch; tokens/s counts prefill rows."""
+    import oracle
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    qs = case["query_start"]
+    done, spent = 0, 0.0
+    for b in range(cfg.batch):
+        L = int(case["context_lens"][b])
+        nblk = (L + 15) // 16
+        blocks = case["block_tables"][b, :nblk]
+        kp, vp = case["k_pool"][blocks], case["v_pool"][blocks]
+        table = np.arange(nblk, dtype=np.int32)[None]
+        r0, r1 = int(qs[b]), int(qs[b + 1])
+        t0 = time.perf_counter()
+        kp, vp = oracle.append(k_new[r0:r1], v_new[r0:r1], case["b_k"], case["b_v"], table,
+                               np.zeros(r1 - r0, np.int32), np.arange(L - (r1 - r0), L, dtype=np.int32), kp, vp)
+        oracle.prefill(case["q"][r0:r1], case["b_k"], case["b_v"], kp, vp, table, np.array([0, r1 - r0]),
+                       np.array([L]), scale)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    rows = int(qs[done])
+    return {"value": rows / spent, "unit": "prefill tokens/s", "cores": oracle_threads(), "kind": "oracle",
+            "sample": f"{done} of {cfg.batch} sequences (append the chunk + causal attention of its {cfg.chunk} rows "
+                      f"over {cfg.seq} positions), fp64 numpy, {spent:.1f} s"}
+
+
 def graph_replay_ms(step, steps: int, out, flush=None) -> float:
     """Capture one step (every launch of the path) in a HIP graph through
     torch's CUDAGraph, check that replays reproduce the eager step's output bit
@@ -182,7 +258,7 @@ def graph_replay_ms(step, steps: int, out, flush=None) -> float:
     return total / steps
 
 
-def config_report(cfg_id: int, steps: int, warmup: int, graph: bool = False):
+def config_report(cfg_id: int, steps: int, warmup: int, graph: bool = False, cpu: bool = True):
     """Timing of one of the decode workloads 1-7 (a separate JSON line).
 
     A step appends one token per sequence, then decodes; for the 32-layer stack
@@ -279,6 +355,9 @@ def config_report(cfg_id: int, steps: int, warmup: int, graph: bool = False):
         else:
             ms = graph_replay_ms(lambda: step(warmup), steps, out, flush)
             line["graph"] = {"ms_per_step": ms, "decode_tokens_per_s": cfg.batch / (ms / 1e3)}
+    if cpu:
+        del layers
+        line["cpu_baseline"] = cpu_baseline_config(cfg)
     print(json.dumps(line), flush=True)
 
 
@@ -383,7 +462,7 @@ def speedup_grid(reps: int, warmup: int):
         "reps": reps, "warmup": warmup, "grid": rows}), flush=True)
 
 
-def prefill_report(cfg_id: int, steps: int, warmup: int):
+def prefill_report(cfg_id: int, steps: int, warmup: int, cpu: bool = True):
     """Time prefill workload N: a step appends every sequence's chunk (its K/V
     rows into the latent cache) and runs the causal prefill of the chunk.
 
@@ -445,6 +524,8 @@ def prefill_report(cfg_id: int, steps: int, warmup: int):
         "attn_frac_of_f16_mfma_peak": flops / attn_s / 1e12 / PEAK_MFMA_F16_TFLOPS,
         "pairs_per_launch": cfg.pairs(),
     }
+    if cpu:
+        line["cpu_baseline"] = cpu_baseline_prefill(cfg, case, k_new, v_new)
     print(json.dumps(line), flush=True)
 
 
@@ -473,10 +554,10 @@ def main():
         calib_copy()
         return
     if args.config:
-        config_report(args.config, args.steps, args.warmup, args.graph)
+        config_report(args.config, args.steps, args.warmup, args.graph, cpu=not args.no_cpu_baseline)
         return
     if args.prefill:
-        prefill_report(args.prefill, args.steps, args.warmup)
+        prefill_report(args.prefill, args.steps, args.warmup, cpu=not args.no_cpu_baseline)
         return
     if args.grid:
         speedup_grid(args.steps, args.warmup)
