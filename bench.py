@@ -92,16 +92,8 @@ def read_ceiling(dev, nbytes=1 << 32, reps=5):
             if block * per_cu > 2048:
                 continue
             starkv.stream_read_probe(buf, sink, grid, block)
-            times = []
-            for _ in range(reps):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                starkv.stream_read_probe(buf, sink, grid, block)
-                e1.record()
-                e1.synchronize()
-                times.append(e0.elapsed_time(e1) / 1e3)
-            gbps = nbytes / sorted(times)[len(times) // 2] / 1e9
+            ms = back_to_back_ms(lambda i: starkv.stream_read_probe(buf, sink, grid, block), reps)
+            gbps = nbytes / (ms / 1e3) / 1e9
             if gbps > best[0]:
                 best = (gbps, {"grid": grid, "block": block})
     del buf
@@ -216,12 +208,53 @@ def cpu_baseline_prefill(cfg, case, k_new, v_new, budget_s=10.0):
                       f"over {cfg.seq} positions), fp64 numpy, {spent:.1f} s"}
 
 
+def back_to_back_ms(call, reps: int, flush=None) -> float:
+    """Milliseconds per call.
+
+    Without `flush`: `reps` calls issued back to back between one pair of
+    events (an event recorded between two kernels leaves the GPU idle for
+    microseconds, so none is recorded per call).
+
+    With `flush` (a 1 GiB fill that evicts the last-level cache): each call is
+    bracketed together with the fill that precedes it, [event, fill, call,
+    event], and the same bracket around the fill alone is subtracted.  The
+    fill keeps the GPU busy while the host enqueues the call, and the event
+    markers' own cost appears in both brackets."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    if flush is not None:
+        flush.fill_(0)                 # first touch of the buffer stays outside the timing
+        torch.cuda.synchronize()
+    if flush is None:
+        e0.record()
+        for i in range(reps):
+            call(i)
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+    with_call, alone = 0.0, 0.0
+    for i in range(reps):
+        e0.record()
+        flush.fill_(i & 0xFF)
+        call(i)
+        e1.record()
+        e1.synchronize()
+        with_call += e0.elapsed_time(e1)
+        e0.record()
+        flush.fill_(i & 0xFF)
+        e1.record()
+        e1.synchronize()
+        alone += e0.elapsed_time(e1)
+    return (with_call - alone) / reps
+
+
 def graph_replay_ms(step, steps: int, out, flush=None) -> float:
     """Capture one step (every launch of the path) in a HIP graph through
     torch's CUDAGraph, check that replays reproduce the eager step's output bit
     for bit (with eager work between the replays), then time `steps` replays
-    (back to back, or one by one around a cache flush).  Returns milliseconds
-    per replay."""
+    back to back (with a cache flush before each when `flush` is given, its
+    time subtracted).  Returns milliseconds per replay."""
     import torch
 
     step()
@@ -236,26 +269,9 @@ def graph_replay_ms(step, steps: int, out, flush=None) -> float:
         torch.cuda.synchronize()
         if not torch.equal(out.view(torch.int16), ref.view(torch.int16)):
             raise RuntimeError("graph replay differs from the eager step")
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    if flush is None:                  # back to back, like the eager timing
-        e0.record()
-        for _ in range(steps):
-            graph.replay()
-        e1.record()
-        e1.synchronize()
-        total = e0.elapsed_time(e1)
-    else:                              # cache written between replays, outside the events
-        total = 0.0
-        for i in range(steps):
-            flush.fill_(i & 0xFF)
-            e0.record()
-            graph.replay()
-            e1.record()
-            e1.synchronize()
-            total += e0.elapsed_time(e1)
+    ms = back_to_back_ms(lambda i: graph.replay(), steps, flush)
     del graph
-    return total / steps
+    return ms
 
 
 def config_report(cfg_id: int, steps: int, warmup: int, graph: bool = False, cpu: bool = True):
@@ -264,10 +280,11 @@ def config_report(cfg_id: int, steps: int, warmup: int, graph: bool = False, cpu
     A step appends one token per sequence, then decodes; for the 32-layer stack
     a step runs that for every layer (tokens/s = batch / summed layer time).
     Uniform workloads overwrite the token at position L each step; the ragged
-    one grows every sequence by one token per step.  Workloads that fit the
-    256 MB last-level cache get a 1 GiB write between steps, outside the timed
-    events.  With `graph`, the same step is also captured in a HIP graph and
-    its replays are timed (uniform workloads only).
+    one grows every sequence by one token per step.  The timed steps run back
+    to back between one pair of events; workloads that fit the 256 MB
+    last-level cache get a 1 GiB write before every step, whose time (measured
+    alone in the same way) is subtracted.  With `graph`, the same step is also captured in a
+    HIP graph and its replays are timed (uniform workloads only).
     """
     import torch
 
@@ -318,29 +335,20 @@ def config_report(cfg_id: int, steps: int, warmup: int, graph: bool = False, cpu
     for s in range(warmup):
         step(s)
     torch.cuda.synchronize()
+    tokens = sum(int(pos_all[s].astype(np.int64).sum()) + cfg.batch for s in range(warmup, warmup + steps))
+    ms = back_to_back_ms(lambda i: step(warmup + i), steps, flush)
+    # the same steps again with the attention kernel's dispatch timed (events
+    # attached to a launch cost the step time; kept out of the value above)
     starkv.profile_begin()
-    total_ms = 0.0
-    tokens = 0
-    step_ms = []
-    for s in range(warmup, warmup + steps):
-        if flush is not None:
-            flush.fill_(s & 0xFF)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        tokens += step(s)
-        e1.record()
-        e1.synchronize()
-        step_ms.append(e0.elapsed_time(e1))
-        total_ms += step_ms[-1]
+    ms_profiled = back_to_back_ms(lambda i: step(warmup + i), steps, flush)
     attn_ms, launches = starkv.profile_end()
+    total_ms = ms * steps
     latent = tokens * sum(layer_bytes)
     line = {
         "config": cfg.index, "workload": cfg.name, "batch": cfg.batch, "layers": cfg.layers,
         "heads": cfg.heads, "kv_heads": cfg.kv,
         "mean_latent_elems_per_token_layer": sum(layer_bytes) / 2 / cfg.layers,
         "steps": steps, "warmup": warmup, "ms_per_step": total_ms / steps,
-        "step_ms_p10_median_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
         "decode_tokens_per_s": cfg.batch * steps / (total_ms / 1e3),
         "attn_kernel_us_per_launch": attn_ms / launches * 1e3,
         "latent_gb_per_step": latent / steps / 1e9,
@@ -348,6 +356,7 @@ def config_report(cfg_id: int, steps: int, warmup: int, graph: bool = False, cpu
         "attn_frac_of_8tbps": latent / (attn_ms / 1e3) / 1e9 / PEAK_HBM_GBPS,
         "step_latent_gbps": latent / (total_ms / 1e3) / 1e9,
         "cache_flush_between_steps": flush is not None,
+        "roofline_pass_ms_per_step": ms_profiled,
     }
     if graph:
         if grow:
@@ -375,9 +384,9 @@ def speedup_grid(reps: int, warmup: int):
     in {1, 16, 64}, one starkv_decode call (query projection, latent
     attention, merge, up-projection; 32 heads, d 128, r_k 64, r_v 1024)
     against one starkv_uncompressed_decode call (plain paged fp16 K/V, same
-    block tables and lengths).  Each call is timed alone between HIP events
-    (median of `reps`), after a 1 GiB cache flush when the data it reads
-    would otherwise stay in the 256 MB last-level cache.  Both attention
+    block tables and lengths).  `reps` calls run back to back between one pair
+    of HIP events, each after a 1 GiB cache flush (its time subtracted) when
+    the data it reads would otherwise stay in the 256 MB last-level cache.  Both attention
     kernels' HBM roofline fractions are reported (algorithmic bytes: 6,144 B
     per latent token, H*d*2*2 = 16,384 B per uncompressed token)."""
     import torch
@@ -396,20 +405,11 @@ def speedup_grid(reps: int, warmup: int):
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
+        ms = back_to_back_ms(lambda i: call(), reps, flush if cold else None)
         starkv.profile_begin()
-        ts = []
-        for i in range(reps):
-            if cold:
-                flush.fill_(i & 0xFF)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            call()
-            e1.record()
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
+        back_to_back_ms(lambda i: call(), reps, flush if cold else None)
         attn_ms, n = starkv.profile_end()
-        return float(np.median(ts)), attn_ms / n
+        return ms, attn_ms / n
 
     for batch in batches:
         seed = 20261203 + 500 + batch
@@ -502,15 +502,9 @@ def prefill_report(cfg_id: int, steps: int, warmup: int, cpu: bool = True):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    starkv.profile_begin()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    e1.synchronize()
-    total_ms = e0.elapsed_time(e1)
+    total_ms = back_to_back_ms(lambda i: step(), steps) * steps
+    starkv.profile_begin()                 # roofline pass: the attention kernel's dispatch timed
+    back_to_back_ms(lambda i: step(), steps)
     attn_ms, launches = starkv.profile_end()
     flops = 2.0 * cfg.heads * (cfg.rank_k + cfg.rank_v) * cfg.pairs()
     attn_s = attn_ms / launches / 1e3
@@ -595,12 +589,20 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    starkv.profile_begin()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    # roofline pass: the same K steps again, the attention kernel's own
+    # dispatch timed by HIP events on its stream (attaching them costs step
+    # time, so this pass is not the value)
+    starkv.profile_begin()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt_profiled = time.perf_counter() - t1
     attn_ms, launches = starkv.profile_end()
     assert launches == args.steps, (launches, args.steps)
     assert torch.isfinite(out.float()).all().item()
@@ -639,6 +641,7 @@ def main():
             "traffic": traffic,
         },
         "attn_kernel_us": attn_avg_s * 1e6,
+        "roofline_pass_ms_per_step": 1e3 * dt_profiled / args.steps,
         "latent_bytes_per_step": latent_bytes,
         "step_latent_gbps": latent_bytes / (dt / args.steps) / 1e9,
     }

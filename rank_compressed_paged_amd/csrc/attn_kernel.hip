@@ -508,7 +508,7 @@ int attn_resident_grid(int H, int KV, int RK, int RV, int device) {
 
 template <typename Inst>
 static void launch_attn(const DecodeLaunch& a, const float* qt, int32_t* plan, float* pz, float* pml) {
-  hipLaunchKernelGGL(Inst::kernel, dim3(a.grid), dim3(Inst::threads), 0, a.stream, qt,
+  launch_timed(Inst::kernel, dim3(a.grid), dim3(Inst::threads), a.stream, a.ev_attn_start, a.ev_attn_stop, qt,
                      static_cast<const f16*>(a.k_cache), static_cast<const f16*>(a.v_cache), a.block_tables,
                      a.s.MB, a.context_lens, plan, a.batch, pz, pml, kRescaleTau);
 }

@@ -839,12 +839,8 @@ hipError_t decode_enqueue(const DecodeLaunch& a) {
   hipError_t err = launch_qproj(s, a.batch, a.q, a.b_k, scale2, qt, a.context_lens, a.grid, plan, a.stream);
   if (err != hipSuccess) return err;
 
-  // 2. latent attention
-  if (a.ev_attn_start && hipEventRecord(a.ev_attn_start, a.stream) != hipSuccess) return hipErrorUnknown;
+  // 2. latent attention (timed by its own dispatch when events are given)
   err = launch_attn_kernel(a, qt, plan, pz, pml);
-  if (err != hipSuccess) return err;
-  if (a.ev_attn_stop && hipEventRecord(a.ev_attn_stop, a.stream) != hipSuccess) return hipErrorUnknown;
-  err = hipGetLastError();
   if (err != hipSuccess) return err;
 
   // 3. merge, 4. up-projection (one launch for few (sequence, head) pairs at d = 128)

@@ -1,11 +1,24 @@
 // Host-side launchers shared between the C ABI and the kernel files.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace starkv {
+
+// Kernel launch that, given events, has the dispatch itself record the
+// kernel's start and end into them: no event packets are queued between the
+// kernels, so measuring does not add idle time between launches.
+template <typename F, typename... Args>
+inline void launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t st, hipEvent_t start, hipEvent_t stop,
+                         Args... args) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, start, stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
 
 // Attention workgroups never take fewer than this many 16-token blocks when
 // the batch is big enough: each range flushes H*r_v fp32 of partial state, so

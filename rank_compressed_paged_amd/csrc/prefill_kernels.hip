@@ -683,7 +683,7 @@ static hipError_t launch_pf_attn(const PrefillLaunch& a, const float* qt, float 
   const long long units_ub = (long long)(((long long)a.lay.tile_cap * a.lay.max_ranges + 7) / 8) * 8 * s.H;
   long long grid = units_ub < res ? units_ub : res;
   grid = ((grid + 7) / 8) * 8;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPfWaves * 64), 0, a.stream, qt,
+  launch_timed(kernel, dim3((unsigned)grid), dim3(kPfWaves * 64), a.stream, a.ev_attn_start, a.ev_attn_stop, qt,
                      static_cast<const f16*>(a.q), static_cast<const f16*>(a.b_k), s.D, scale2,
                      static_cast<const f16*>(a.k_cache), static_cast<const f16*>(a.v_cache), a.block_tables, s.MB,
                      a.query_start, a.context_lens, plan, a.rows, a.lay.tile_cap, s.H, s.H / s.KV, s.KV, pz, pml,
@@ -711,7 +711,6 @@ hipError_t prefill_enqueue(const PrefillLaunch& a, int device) {
     if (err != hipSuccess) return err;
   }
 
-  if (a.ev_attn_start && hipEventRecord(a.ev_attn_start, a.stream) != hipSuccess) return hipErrorUnknown;
   err = hipErrorInvalidValue;
   // one context range for every row: the attention kernel writes Z itself
   float* zdirect = a.lay.max_ranges == 1 ? zf : nullptr;
@@ -721,7 +720,6 @@ hipError_t prefill_enqueue(const PrefillLaunch& a, int device) {
   STARKV_PREFILL_SHAPES(X)
 #undef X
   if (err != hipSuccess) return err;
-  if (a.ev_attn_stop && hipEventRecord(a.ev_attn_stop, a.stream) != hipSuccess) return hipErrorUnknown;
 
   if (!zdirect) {
     const PrefillPlan P{plan, a.rows, a.lay.tile_cap};

@@ -296,7 +296,7 @@ bool plain_shape_supported(int H, int KV, int D) {
 template <int D, int G>
 static void launch_plain(const PlainLaunch& a, float* pacc, float* pml) {
   const dim3 grid((unsigned)((size_t)a.batch * a.KV * a.lay.maxparts));
-  hipLaunchKernelGGL((plain_attn_kernel<D, G>), grid, dim3(256), 0, a.stream, static_cast<const f16*>(a.q),
+  launch_timed(plain_attn_kernel<D, G>, grid, dim3(256), a.stream, a.ev_start, a.ev_stop, static_cast<const f16*>(a.q),
                      static_cast<const f16*>(a.k_cache), static_cast<const f16*>(a.v_cache), a.block_tables, a.MB,
                      a.context_lens, a.H, a.KV, a.lay.pb, a.lay.maxparts, a.scale * kLog2e, kRescaleTau, pacc, pml,
                      static_cast<f16*>(a.out));
@@ -306,7 +306,6 @@ hipError_t plain_enqueue(const PlainLaunch& a) {
   float* pacc = reinterpret_cast<float*>(a.ws + a.lay.off_acc);
   float* pml = reinterpret_cast<float*>(a.ws + a.lay.off_ml);
   const int G = a.H / a.KV;
-  if (a.ev_start && hipEventRecord(a.ev_start, a.stream) != hipSuccess) return hipErrorUnknown;
   bool launched = false;
 #define PLAIN_CASE(d, gg)                                   \
   if (!launched && a.D == d && G == gg) {                   \
@@ -319,7 +318,6 @@ hipError_t plain_enqueue(const PlainLaunch& a) {
   if (!launched) return hipErrorInvalidValue;
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (a.ev_stop && hipEventRecord(a.ev_stop, a.stream) != hipSuccess) return hipErrorUnknown;
   if (a.lay.maxparts > 1) {
     const dim3 grid((unsigned)((size_t)a.batch * a.H));
     if (a.D == 128)
