@@ -43,7 +43,8 @@ METRIC = "decode tokens/s and achieved HBM GB/s (32h, d=128, r_k=64) at batch 64
 PEAK_HBM_GBPS = 8000.0
 COPY_BYTES = 1 << 31
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_b64_l8192_traffic.json")
-KERNEL_SOURCES = ["rank_compressed_paged_amd/csrc/attn_kernel.hip", "rank_compressed_paged_amd/csrc/common.h"]
+KERNEL_SOURCES = ["rank_compressed_paged_amd/csrc/attn_kernel.h", "rank_compressed_paged_amd/csrc/attn_inst_exact.hip",
+                  "rank_compressed_paged_amd/csrc/common.h"]
 
 
 def kernel_source_hash() -> str:

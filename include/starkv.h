@@ -64,14 +64,15 @@ typedef struct {
   int32_t num_kv_heads;       /* H_kv key/value heads, dividing H; 0 means H */
 } starkv_dims;
 
-/* Latent shapes with a decode kernel built into this library, as
- * (H, H_kv, r_k, r_v):
- *   (32, 32, r_k in {32, 64}, r_v in {256, 512, 768, 1024}) - ranks may differ
- *   from layer to layer: each layer is its own call;
- *   (32, 8, 64, {256, 512, 1024}), (32, 8, 32, {256, 512}) and
- *   (32, 4, 64, {256, 512}) - grouped query heads;
- *   (4, 4, 16, 64) and (8, 2, 32, 64) - small shapes.
- *   Others -> STARKV_ERR_UNSUPPORTED.
+/* Layer shapes with a decode kernel built into this library:
+ *   multi-head layers (H_kv = H) of 1 to 32 query heads at r_k in {16, 32, 64};
+ *   grouped-query layers of up to 32 query heads, H_kv dividing H,
+ *   H/H_kv <= 16, at r_k in {32, 64};
+ *   each at r_v in {256, 512, 768, 1024} (ranks may differ from layer to
+ *   layer: each layer is its own call); plus the small shapes (H, H_kv, r_k,
+ *   r_v) = (4, 4, 16, 64) and (8, 2, 32, 64).
+ *   Others -> STARKV_ERR_UNSUPPORTED (more than 32 query heads, which are the
+ *   rows of one MFMA tile, among them).
  *   starkv_append supports any r_k % 8 == 0 and r_v % 32 == 0 up to 1024. */
 
 /*

@@ -1,5 +1,6 @@
-// STAR-KV latent attention kernel for gfx950 (MI355X): the HBM-bound scan of
-// the decode path.
+// STAR-KV latent attention kernel template for gfx950 (MI355X): the
+// HBM-bound scan of the decode path.  Its instances are compiled in the
+// attn_inst_*.hip files and dispatched by attn_dispatch.hip.
 //
 // Every workgroup owns an equal range of 16-token blocks of the ragged batch
 // (the plan written by the query-projection launch).  Per block:
@@ -22,6 +23,8 @@
 // paged storage); paging per the botdigit PagedAttention page, block-level
 // management item; block size 16 per the Proxima README measured results.
 
+#pragma once
+
 #include <math.h>
 
 #include <type_traits>
@@ -35,55 +38,62 @@ namespace starkv {
 // 2. latent attention over a range of paged blocks
 // ---------------------------------------------------------------------------
 
-template <int H, int HKV, int RK, int RV, int NW>
+// One instantiation serves a family of layer shapes: H and H_kv are runtime
+// arguments.  Multi-head layers (UPW = 0) take any H <= HP query heads; the
+// K block of a layer with H < HP is smaller than the HP-head block the loads
+// are laid out for, and the surplus lanes re-read a clamped address whose
+// scores are dropped.  Grouped layers (UPW > 0: 16x16x32 MFMA scores) take any
+// H <= 32 and H_kv dividing it with G = H/H_kv in [2, 16] and
+// H_kv * r_k/32 <= NW * UPW score units per block.
+template <int HP, int RK, int RV, int NW, int UPW>
 struct AttnCfg {
-  static constexpr int G = H / HKV;                       // query heads per key/value head
+  static constexpr bool kMfmaScores = UPW > 0;
   static constexpr int kThreads = NW * 64;
-  static constexpr int kBlockKHalves = HKV * kBlock * RK; // one block's K latents
-  static constexpr int kPieces = kBlockKHalves / 512;     // 1 KiB pieces (one wave load each)
-  static constexpr int PPW = kPieces / NW;                // pieces per wave
-  static constexpr int LPT = RK / 8;                      // lanes sharing one token's dot
+  static constexpr int KSTEPS = RK >= 32 ? RK / 32 : 1;   // grouped heads: 32-latent k-steps of a key head
+  // key/value heads of the largest K block this instance is laid out for
+  static constexpr int kKvMax = kMfmaScores ? UPW * NW / KSTEPS : HP;
+  static constexpr int kBlockKHalvesMax = kKvMax * kBlock * RK;
+  static constexpr int PPW = kMfmaScores ? UPW : kBlockKHalvesMax / 512 / NW;   // K loads per wave per block
+  static constexpr int LPT = RK / 8;                      // lanes sharing one token's dot (multi-head)
   static constexpr int kHeadHalves = kBlock * RK;
   static constexpr int TILES = RV / 32;                   // 32-wide MFMA tiles of the V latent
   static constexpr int TPW = TILES / NW;
   // Blocks in flight per workgroup: enough that about 128 KiB of latents are
   // outstanding per CU (one resident workgroup), so small blocks (grouped
   // heads, low ranks) still cover the HBM latency.
-  static constexpr int kBlockBytes = 2 * (kBlockKHalves + RV * kBlock);
+  static constexpr int kBlockBytes = 2 * (kBlockKHalvesMax + RV * kBlock);
   static constexpr int NBUF = kBlockBytes >= 64 * 1024 ? 2 : (kBlockBytes >= 43 * 1024 ? 3 : 4);
-  // Grouped heads score on MFMA: a wave owns KPW key/value heads and KSW of
-  // the RK/32 k-steps of each; WPK waves split one head's k-steps and the
-  // softmax adds their SPLIT partial score tiles.
-  static constexpr bool kMfmaScores = G > 1;
-  static constexpr int KSTEPS = RK / 32;
-  static constexpr int WPK = NW >= HKV ? NW / HKV : 1;
-  static constexpr int KPW = HKV >= NW ? HKV / NW : 1;
-  static constexpr int KSW = KSTEPS >= WPK ? KSTEPS / WPK : 1;
-  static constexpr int SPLIT = kMfmaScores ? WPK : 1;
-  static_assert(!kMfmaScores || (G <= 16 && RK % 32 == 0 && (NW % HKV == 0 || HKV % NW == 0) &&
-                                 KSTEPS % WPK == 0 && KPW * KSW == PPW),
-                "grouped-head MFMA score tiling");
-  static_assert(H >= 1 && H <= 32, "heads are MFMA rows");
-  static_assert(HKV >= 1 && H % HKV == 0, "query heads split evenly over key/value heads");
-  static_assert(kBlockKHalves % 512 == 0 && kPieces % NW == 0 && PPW >= 1, "K pieces per wave");
-  static_assert(LPT >= 2 && LPT <= 16 && 512 % RK == 0, "r_k in {16, 32, 64}");
+  // a wave's score units are whole key heads: their k-steps are summed in
+  // registers and one score plane suffices; otherwise one plane per k-step
+  static constexpr bool kWholeHeads = kMfmaScores && UPW % KSTEPS == 0;
+  static constexpr int SPLIT = kMfmaScores && !kWholeHeads ? KSTEPS : 1;
+  static_assert(HP >= 1 && HP <= 32, "query heads are MFMA rows");
+  static_assert(!kMfmaScores || (RK % 32 == 0 && (UPW == 1 || UPW == 2 || UPW == 4)), "grouped-head MFMA scores");
+  static_assert(kMfmaScores || (kBlockKHalvesMax % 512 == 0 && (kBlockKHalvesMax / 512) % NW == 0 && PPW >= 1),
+                "K pieces per wave");
+  static_assert(kMfmaScores || (LPT >= 2 && LPT <= 16 && 512 % RK == 0), "r_k in {16, 32, 64}");
   static_assert(RV % 32 == 0 && TILES % NW == 0 && TPW >= 1, "V tiles per wave");
 };
 
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-template <int H, int HKV, int RK, int RV, int NW>
+template <int HP, int RK, int RV, int NW, int UPW, int HX, int KVX>
 __global__ void __launch_bounds__(NW * 64)
 attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f16* __restrict__ vpool,
             const int32_t* __restrict__ block_tables, int mb_stride,
             const int32_t* __restrict__ context_lens, const int32_t* __restrict__ plan, int batch,
-            float* __restrict__ part_z, float* __restrict__ part_ml, float tau) {
-  using C = AttnCfg<H, HKV, RK, RV, NW>;
+            int h_arg, int kv_arg, float* __restrict__ part_z, float* __restrict__ part_ml, float tau) {
+  using C = AttnCfg<HP, RK, RV, NW, UPW>;
+  // HX, KVX > 0: an instance built for exactly these head counts (constants
+  // in the code); 0: taken from the arguments
+  const int H = HX > 0 ? HX : h_arg;
+  const int KV = KVX > 0 ? KVX : kv_arg;
   constexpr int NB = C::NBUF;
+  constexpr int QROWS = C::kMfmaScores ? 32 : HP;     // q~ rows staged per sequence
   __shared__ float s_lds[NB][C::SPLIT][32][kBlock];
   constexpr int QCAP = 2;            // sequences whose q~ is staged up front
-  __shared__ __attribute__((aligned(16))) float q_lds[QCAP][H * RK];
+  __shared__ __attribute__((aligned(16))) float q_lds[QCAP][QROWS * RK];
   // Partial-state stash.  On gfx9 stores share the in-order vector-memory
   // counter with the latent prefetch, so a partial written in the middle of a
   // range makes later prefetch waits also wait for those stores, which drain
@@ -103,6 +113,9 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
   const int end = min(start + W, total);
   const int32_t* __restrict__ prefix = pv.prefix();
   const int32_t* __restrict__ slot_base = pv.slot_base();
+  const int G = H / KV;                                   // query heads per key/value head
+  const int kbh = KV * kBlock * RK;                       // halves of one block's K latents
+  const int units = KV * C::KSTEPS;                       // grouped heads: score units per block
 
   // sequence holding block `start` (from the plan)
   const int lo = pv.first_seq()[blockIdx.x];
@@ -120,41 +133,40 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     return block_tables[(size_t)it.b * mb_stride + (it.gi - it.lo)];
   };
 
-  // lane roles for the key scores.  VALU path: a wave reads PPW contiguous
-  // 1 KiB pieces of the block, LPT lanes per token.  MFMA path: key/value head
-  // kv_of(u), k-step ks_of(s); lane l reads token l%16, latents 8*(l/16)..+7
-  // of that k-step.
+  // lane roles for the key scores.  Multi-head: a wave reads PPW contiguous
+  // 1 KiB pieces of the block, LPT lanes per token; pieces past the layer's K
+  // block (H < HP) re-read a clamped address and score nothing.  Grouped
+  // heads: unit u = w*UPW + j is (key head u / KSTEPS, k-step u % KSTEPS);
+  // lane l reads token l%16, latents 8*(l/16)..+7 of that k-step.
   const int c8 = lane % C::LPT;                     // which 8 latents of a token
-  auto piece_head = [&](int j) { return ((w * C::PPW + j) * 512 + lane * 8) / C::kHeadHalves; };
-  auto piece_tok = [&](int j) { return (((w * C::PPW + j) * 512 + lane * 8) / RK) % kBlock; };
-  auto kv_of = [&](int u) { return C::WPK > 1 ? w / C::WPK : w * C::KPW + u; };
-  auto ks_of = [&](int s) { return (w % C::WPK) * C::KSW + s; };
+  auto piece_elem = [&](int j) { return (w * C::PPW + j) * 512 + lane * 8; };
+  auto piece_head = [&](int j) { return piece_elem(j) / C::kHeadHalves; };
+  auto piece_tok = [&](int j) { return (piece_elem(j) / RK) % kBlock; };
+  auto unit_of = [&](int j) { return w * UPW + j; };
 
   // Latents are read exactly once: non-temporal loads stream them past the
   // caches instead of evicting the small reused data (q~, tables, partials).
   // `spare` loads (issued only to keep the in-order wait counts exact, see
-  // below) make every wave read the same first piece of a block it already
-  // holds, so they cost one cached 1 KiB row per wave instead of a block.
-  auto load_k = [&](half8 (&dst)[C::PPW], int phys, bool spare) {
+  // below) re-read pieces at the start of a block the wave already holds, so
+  // they cost cached rows instead of a block.
+  // multi-head: piece j of this wave starts at k_base + 512 j halves (clamped
+  // to the block when the layer has fewer than HP heads)
+  auto k_base = [&](bool spare) { return (spare ? 0 : w * C::PPW * 512) + lane * 8; };
+  auto k_offset = [&](int base, int j, bool spare) -> int {
     if constexpr (C::kMfmaScores) {
-      // spare loads take the pieces wave 0 would read: distinct addresses, so
-      // the compiler cannot merge them and every path issues PPW loads
-      const f16* blk = kpool + (size_t)phys * C::kBlockKHalves + (lane & 15) * RK + (lane >> 4) * 8;
-#pragma unroll
-      for (int u = 0; u < C::KPW; ++u)
-#pragma unroll
-        for (int s = 0; s < C::KSW; ++s) {
-          const int j = u * C::KSW + s;
-          const int kvh = spare ? j / C::KSTEPS : kv_of(u);
-          const int ks = spare ? j % C::KSTEPS : ks_of(s);
-          dst[j] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(blk + kvh * kBlock * RK + ks * 32));
-        }
+      const int u = spare ? min(j, units - 1) : min(unit_of(j), units - 1);
+      return (u / C::KSTEPS) * kBlock * RK + (lane & 15) * RK + (u % C::KSTEPS) * 32 + (lane >> 4) * 8;
     } else {
-      const half8* base = reinterpret_cast<const half8*>(kpool + (size_t)phys * C::kBlockKHalves) +
-                          (spare ? 0 : (w * C::PPW) * 64) + lane;
-#pragma unroll
-      for (int j = 0; j < C::PPW; ++j) dst[j] = __builtin_nontemporal_load(base + j * 64);
+      if constexpr (HX == HP) return base + j * 512;      // the K block is exactly HP heads
+      return min(base + j * 512, kbh - 8);
     }
+  };
+  auto load_k = [&](half8 (&dst)[C::PPW], int phys, bool spare) {
+    const f16* blk = kpool + (size_t)phys * kbh;
+    const int base = k_base(spare);
+#pragma unroll
+    for (int j = 0; j < C::PPW; ++j)
+      dst[j] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(blk + k_offset(base, j, spare)));
   };
   auto load_v = [&](half8 (&dst)[C::TPW], int phys, bool spare) {
     const half8* base = reinterpret_cast<const half8*>(vpool + (size_t)phys * (RV * kBlock)) +
@@ -179,13 +191,12 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
   // load issued behind the latent prefetch would drain it; only ranges
   // touching more than QCAP sequences pay that, once per extra sequence.
   const int b_first = cur.b;
+  const int QV = H * RK / 4;                             // float4 words of one sequence's q~
   auto stage_q = [&](int slot_q, int b) {
     const floatx4* qsrc = reinterpret_cast<const floatx4*>(qt + (size_t)b * H * RK);
-    for (int i = threadIdx.x; i < H * RK / 4; i += C::kThreads)
-      reinterpret_cast<floatx4*>(q_lds[slot_q])[i] = qsrc[i];
+    for (int i = threadIdx.x; i < QV; i += C::kThreads) reinterpret_cast<floatx4*>(q_lds[slot_q])[i] = qsrc[i];
   };
-  constexpr int QV = H * RK / 4;                         // float4 words of one sequence's q~
-  constexpr int QPT = (QV + C::kThreads - 1) / C::kThreads;
+  constexpr int QPT = (QROWS * RK / 4 + C::kThreads - 1) / C::kThreads;
   floatx4 q0reg[QCAP][QPT];
 #pragma unroll
   for (int sq = 0; sq < QCAP; ++sq)
@@ -197,31 +208,31 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     }
 
   const float* qcur = q_lds[0];
-  // MFMA path: the wave's A operands (q~ of its group's query heads, rows
+  // MFMA path: the wave's A operands (q~ of its units' query heads, rows
   // beyond the group zero) as fp16 high + low parts, held for a segment.
   // x - hi is exact in fp32, so hi + lo carries q~ to about 2^-22 relative.
-  half8 qa_hi[C::KPW * C::KSW], qa_lo[C::KPW * C::KSW];
+  constexpr int QA = C::kMfmaScores ? C::PPW : 1;
+  half8 qa_hi[QA], qa_lo[QA];
   auto load_qa = [&]() {
     const int i = lane & 15;
 #pragma unroll
-    for (int u = 0; u < C::KPW; ++u)
+    for (int j = 0; j < QA; ++j) {
+      half8 hi{}, lo{};
+      const int u = unit_of(j);
+      if (i < G && u < units) {
+        const floatx4* qp = reinterpret_cast<const floatx4*>(qcur + ((u / C::KSTEPS) * G + i) * RK +
+                                                             (u % C::KSTEPS) * 32 + (lane >> 4) * 8);
+        const floatx4 q0 = qp[0], q1 = qp[1];
 #pragma unroll
-      for (int s = 0; s < C::KSW; ++s) {
-        half8 hi{}, lo{};
-        if (i < C::G) {
-          const floatx4* qp =
-              reinterpret_cast<const floatx4*>(qcur + (kv_of(u) * C::G + i) * RK + ks_of(s) * 32 + (lane >> 4) * 8);
-          const floatx4 q0 = qp[0], q1 = qp[1];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = e < 4 ? q0[e] : q1[e - 4];
-            hi[e] = (f16)x;
-            lo[e] = (f16)(x - (float)hi[e]);
-          }
+        for (int e = 0; e < 8; ++e) {
+          const float x = e < 4 ? q0[e] : q1[e - 4];
+          hi[e] = (f16)x;
+          lo[e] = (f16)(x - (float)hi[e]);
         }
-        qa_hi[u * C::KSW + s] = hi;
-        qa_lo[u * C::KSW + s] = lo;
       }
+      qa_hi[j] = hi;
+      qa_lo[j] = lo;
+    }
   };
 
   // Block i is consumed from buffer (i - start) % NB while the next NB blocks
@@ -258,7 +269,7 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int rrow = (r & 3) + 8 * (r >> 2);
-      if (rrow >= H) continue;                         // compile-time for H = 32
+      if (rrow >= HP) continue;                        // compile-time
       float* zr = zp + (size_t)rrow * RV;
 #pragma unroll
       for (int t = 0; t < C::TPW; ++t)
@@ -302,30 +313,36 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
 
     // latent-key scores of this block -> LDS
     if constexpr (C::kMfmaScores) {
+      // register r of lane l: query head 4*(l/16)+r of the unit's group, token l%16
+      constexpr int STEP = C::kWholeHeads ? C::KSTEPS : 1;   // units summed in registers
 #pragma unroll
-      for (int u = 0; u < C::KPW; ++u) {
+      for (int j0 = 0; j0 < C::PPW; j0 += STEP) {
         floatx4 sc{};
 #pragma unroll
-        for (int s = 0; s < C::KSW; ++s) {
-          sc = mfma16x16x32(qa_hi[u * C::KSW + s], kb[BUF][u * C::KSW + s], sc);
-          sc = mfma16x16x32(qa_lo[u * C::KSW + s], kb[BUF][u * C::KSW + s], sc);
+        for (int j = j0; j < j0 + STEP; ++j) {
+          sc = mfma16x16x32(qa_hi[j], kb[BUF][j], sc);
+          sc = mfma16x16x32(qa_lo[j], kb[BUF][j], sc);
         }
-        // register r of lane l: query head row 4*(l/16)+r of the group, token l%16
+        const int u = unit_of(j0);
+        if (u < units) {
+          const int plane = C::kWholeHeads ? 0 : u % C::KSTEPS;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * (lane >> 4) + r;
-          if (i < C::G) s_lds[BUF][w % C::WPK][kv_of(u) * C::G + i][lane & 15] = sc[r];
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * (lane >> 4) + r;
+            if (i < G) s_lds[BUF][plane][(u / C::KSTEPS) * G + i][lane & 15] = sc[r];
+          }
         }
       }
     } else {
       // each piece's register is refilled with the next block's piece as soon
       // as it has been read, so the ring stays full while the dots run
-      const half8* nbase = reinterpret_cast<const half8*>(kpool + (size_t)pphys * C::kBlockKHalves) +
-                           (more ? (w * C::PPW) * 64 : 0) + lane;
+      const f16* nblk = kpool + (size_t)pphys * kbh;
+      const int nbase = k_base(!more);
 #pragma unroll
       for (int j = 0; j < C::PPW; ++j) {
         const half8 kx = kb[BUF][j];
-        const floatx4* qp = reinterpret_cast<const floatx4*>(qcur + piece_head(j) * RK + c8 * 8);
+        const int ph = piece_head(j);                     // < HP; rows from H on are never scored
+        const floatx4* qp = reinterpret_cast<const floatx4*>(qcur + ph * RK + c8 * 8);
         const floatx4 q0 = qp[0], q1 = qp[1];
         float s = q0[0] * (float)kx[0];
         s += q0[1] * (float)kx[1];
@@ -335,9 +352,9 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
         s += q1[1] * (float)kx[5];
         s += q1[2] * (float)kx[6];
         s += q1[3] * (float)kx[7];
-        kb[BUF][j] = __builtin_nontemporal_load(nbase + j * 64);
+        kb[BUF][j] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(nblk + k_offset(nbase, j, !more)));
         s = group_sum<C::LPT>(s);
-        if (c8 == 0) s_lds[BUF][0][piece_head(j)][piece_tok(j)] = s;
+        if (c8 == 0 && ph < H) s_lds[BUF][0][ph][piece_tok(j)] = s;
       }
     }
     if constexpr (C::kMfmaScores) load_k(kb[BUF], pphys, !more);
@@ -440,91 +457,16 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     store_partial(stash_slot, [&](int t, int r) { return stash[w][t][r][lane]; }, stash_m, stash_l);
 }
 
-// ---------------------------------------------------------------------------
-// host side
-// ---------------------------------------------------------------------------
-
-template <int H, int HKV, int RK, int RV, int NW>
-struct AttnInst {
-  static constexpr auto kernel = attn_kernel<H, HKV, RK, RV, NW>;
-  static constexpr int threads = NW * 64;
-};
-
-// Shapes built into the library: (H, H_kv, r_k, r_v, waves per workgroup).
-// The method picks ranks per layer (adaptive rank control), so 32-head layers
-// come with r_k in {32, 64} and r_v in {256, 512, 768, 1024}; grouped-query
-// layers (32 query heads over 8 or 4 key/value heads) with r_v up to the value
-// width H_kv*d; (4, 4, 16, 64) and (8, 2, 32, 64) are the small parity shapes.
-#define STARKV_ATTN_SHAPES(X) \
-  X(32, 32, 64, 1024, 8)      \
-  X(32, 32, 64, 768, 8)       \
-  X(32, 32, 64, 512, 8)       \
-  X(32, 32, 64, 256, 8)       \
-  X(32, 32, 32, 1024, 8)      \
-  X(32, 32, 32, 768, 8)       \
-  X(32, 32, 32, 512, 8)       \
-  X(32, 32, 32, 256, 8)       \
-  X(32, 8, 64, 1024, 8)       \
-  X(32, 8, 64, 512, 8)        \
-  X(32, 8, 64, 256, 8)        \
-  X(32, 8, 32, 512, 8)        \
-  X(32, 8, 32, 256, 8)        \
-  X(32, 4, 64, 512, 8)        \
-  X(32, 4, 64, 256, 8)        \
-  X(4, 4, 16, 64, 2)          \
-  X(8, 2, 32, 64, 2)
-
-int attn_shape_index(int H, int KV, int RK, int RV) {
-  int i = 0;
-#define X(h, kv, rk, rv, nw)                                  \
-  if (H == h && KV == kv && RK == rk && RV == rv) return i; \
-  ++i;
-  STARKV_ATTN_SHAPES(X)
-#undef X
-  return -1;
-}
-
-bool attn_shape_supported(int H, int KV, int RK, int RV) { return attn_shape_index(H, KV, RK, RV) >= 0; }
-
-template <typename Inst>
-static int resident_for(int device) {
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Inst::kernel, Inst::threads, 0) != hipSuccess ||
-      per_cu < 1)
-    per_cu = 1;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
-    cus = 1;
-  return per_cu * cus;
-}
-
-int attn_resident_grid(int H, int KV, int RK, int RV, int device) {
-#define X(h, kv, rk, rv, nw) \
-  if (H == h && KV == kv && RK == rk && RV == rv) return resident_for<AttnInst<h, kv, rk, rv, nw>>(device);
-  STARKV_ATTN_SHAPES(X)
-#undef X
-  return 1;
-}
-
-template <typename Inst>
-static void launch_attn(const DecodeLaunch& a, const float* qt, int32_t* plan, float* pz, float* pml) {
-  launch_timed(Inst::kernel, dim3(a.grid), dim3(Inst::threads), a.stream, a.ev_attn_start, a.ev_attn_stop, qt,
-                     static_cast<const f16*>(a.k_cache), static_cast<const f16*>(a.v_cache), a.block_tables,
-                     a.s.MB, a.context_lens, plan, a.batch, pz, pml, kRescaleTau);
-}
-
-hipError_t launch_attn_kernel(const DecodeLaunch& a, const float* qt, int32_t* plan, float* pz, float* pml) {
-  const Shape& s = a.s;
-  bool launched = false;
-#define X(h, kv, rk, rv, nw)                                                          \
-  if (!launched && s.H == h && s.KV == kv && s.RK == rk && s.RV == rv) {          \
-    launch_attn<AttnInst<h, kv, rk, rv, nw>>(a, qt, plan, pz, pml);               \
-    launched = true;                                                              \
+// Instance table entry (AttnKey -> AttnEntry, types in launch.h).
+#define STARKV_ATTN_ENTRY(hp, rk, rv, nw, upw, hx, kvx)                                                      \
+  if (key.hpad == hp && key.rank_k == rk && key.rank_v == rv && key.waves == nw && key.units_pw == upw &&     \
+      key.exact_h == hx && key.exact_kv == kvx) {                                                            \
+    e.fn = reinterpret_cast<const void*>(&attn_kernel<hp, rk, rv, nw, upw, hx, kvx>);                         \
+    e.threads = nw * 64;                                                                                     \
+    return true;                                                                                             \
   }
-  STARKV_ATTN_SHAPES(X)
-#undef X
-  if (!launched) return hipErrorInvalidValue;
-  return hipGetLastError();
-}
+#define STARKV_ATTN_RV(X, hp, rk, nw, upw, hx, kvx) \
+  X(hp, rk, 256, nw, upw, hx, kvx) X(hp, rk, 512, nw, upw, hx, kvx) X(hp, rk, 768, nw, upw, hx, kvx) \
+  X(hp, rk, 1024, nw, upw, hx, kvx)
 
 }  // namespace starkv

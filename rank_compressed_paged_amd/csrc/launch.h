@@ -47,9 +47,6 @@ DecodeLayout decode_layout(const Shape& s, int batch, int max_context_len, int g
 
 // Returns true if a latent attention kernel is built for (H, H_kv, r_k, r_v).
 bool attn_shape_supported(int H, int KV, int RK, int RV);
-// Position of (H, H_kv, r_k, r_v) among the built shapes (< kMaxAttnShapes), or -1.
-int attn_shape_index(int H, int KV, int RK, int RV);
-constexpr int kMaxAttnShapes = 32;
 
 struct DecodeLaunch {
   Shape s;
@@ -70,6 +67,21 @@ struct DecodeLaunch {
   hipEvent_t ev_attn_start;       // optional (nullptr): brackets the attention kernel
   hipEvent_t ev_attn_stop;
 };
+
+// An attention kernel instance: keyed by (padded query heads HP, r_k, r_v,
+// waves, MFMA score units per wave (0 = multi-head VALU scores), exact H or 0,
+// exact H_kv or 0); every instance has the same signature.
+struct AttnKey {
+  int hpad, rank_k, rank_v, waves, units_pw, exact_h, exact_kv;
+};
+struct AttnEntry {
+  const void* fn;
+  int threads;
+};
+// Instance tables, one per source file (true if the key is built there).
+bool attn_entry_exact(const AttnKey& key, AttnEntry& e);
+bool attn_entry_mha(const AttnKey& key, AttnEntry& e);
+bool attn_entry_gqa(const AttnKey& key, AttnEntry& e);
 
 // Occupancy-derived attention grid for this device (workgroups resident at once).
 int attn_resident_grid(int H, int KV, int RK, int RV, int device);

@@ -45,24 +45,10 @@ bool decode_args_ok(const starkv_dims* d, int32_t batch, int32_t max_context_len
   return blocks < (1LL << 30);
 }
 
-// Attention grid per (device, shape), filled on first use.
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_resident[kMaxDevices][kMaxAttnShapes];
-
-int resident_grid(int H, int KV, int RK, int RV, int device) {
-  const int idx = attn_shape_index(H, KV, RK, RV);
-  if (device < 0 || device >= kMaxDevices || idx < 0 || idx >= kMaxAttnShapes)
-    return attn_resident_grid(H, KV, RK, RV, device);
-  std::atomic<int>& cell = g_resident[device][idx];
-  int v = cell.load(std::memory_order_relaxed);
-  if (v <= 0) {
-    v = attn_resident_grid(H, KV, RK, RV, device);
-    cell.store(v, std::memory_order_relaxed);
-  }
-  return v;
-}
+int resident_grid(int H, int KV, int RK, int RV, int device) { return attn_resident_grid(H, KV, RK, RV, device); }
 
 // Compute units per device, filled on first use.
+constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
 
 int device_cus(int device) {

@@ -110,7 +110,10 @@ def test_grouped_heads_checks(lib):
     assert ctypes.sizeof(starkv.Dims) == 8 * 4                     # eight int32 fields, no padding
     assert call_decode(lib, main_dims(kv_heads=5)) == INVALID         # must divide the query heads
     assert call_decode(lib, main_dims(kv_heads=-1)) == INVALID
-    assert call_decode(lib, main_dims(kv_heads=16)) == UNSUPPORTED    # valid, no kernel built
+    assert call_decode(lib, main_dims(kv_heads=16), ws_bytes=1024) == WORKSPACE   # 32/16 is built
+    assert call_decode(lib, main_dims(kv_heads=1)) == UNSUPPORTED     # 32 query heads per key head
+    assert call_decode(lib, main_dims(heads=40, kv_heads=8)) == UNSUPPORTED   # more than 32 query heads
+    assert call_decode(lib, main_dims(heads=28, kv_heads=4, rank_k=16)) == UNSUPPORTED   # grouped: r_k 32 or 64
     assert call_decode(lib, main_dims(kv_heads=8), ws_bytes=1024) == WORKSPACE   # (32, 8, 64, 1024) is built
     zero = main_dims()
     zero.num_kv_heads = 0                                             # 0 means "same as num_heads"
@@ -206,3 +209,20 @@ def test_b_v_must_be_16_byte_aligned(lib):
 def test_rank_k_bounded(lib):
     assert call_decode(lib, main_dims(rank_k=264, head_dim=256)) == UNSUPPORTED
     assert ws_size(lib, main_dims(rank_k=264, head_dim=256), 4, 64) == 0
+
+
+def test_every_documented_layer_shape_is_accepted(lib):
+    """Multi-head layers of 1..32 heads at r_k 16/32/64 and grouped layers with
+    H/H_kv <= 16 at r_k 32/64, each at r_v 256..1024, pass the host checks
+    (the workspace check comes after the shape check)."""
+    for rv in (256, 512, 768, 1024):
+        for h in range(1, 33):
+            for rk in (16, 32, 64):
+                assert call_decode(lib, main_dims(heads=h, kv_heads=h, rank_k=rk, rank_v=rv),
+                                   ws_bytes=1024) == WORKSPACE, (h, rk, rv)
+            for kv in range(1, h):
+                if h % kv or h // kv > 16:
+                    continue
+                for rk in (32, 64):
+                    assert call_decode(lib, main_dims(heads=h, kv_heads=kv, rank_k=rk, rank_v=rv),
+                                       ws_bytes=1024) == WORKSPACE, (h, kv, rk, rv)
