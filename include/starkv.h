@@ -83,8 +83,14 @@ typedef struct {
  *   c_v[i,:]   = fp16( w_v . vec(v[i]) )        w_v [r_v][H_kv*d], vec = heads concatenated
  * computed with fp32 accumulation and rounded once to fp16 (nearest even).
  * The down-projections are stored output-major (row r is the weight vector of
- * latent r).  With orthonormal-row up-projections B, w = B gives the
- * least-squares latents, so callers may pass b_k / b_v of starkv_decode.
+ * latent r), like a linear layer's weight: w_k[h] is the transpose of an
+ * input-major a_k[h] [d][r_k], and w_v of a_v [H_kv*d][r_v].  This is a
+ * deliberate choice of layout, not the input-major one: both operands of the
+ * projection's MFMA (a new row and a weight row) are then contiguous along
+ * the contraction, so every MFMA fragment is one 16-byte load with no
+ * transpose.  A caller holding input-major weights transposes them once.
+ * With orthonormal-row up-projections B, w = B gives the least-squares
+ * latents, so callers may pass b_k / b_v of starkv_decode.
  *
  *   n_tokens     number of rows, at most 2^24 (else STARKV_ERR_INVALID_ARG);
  *                0 is a no-op returning STARKV_OK.  A call too large for one
