@@ -386,9 +386,17 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
       const float alpha = row_live ? fast_exp2(m_run - m_new) : 1.f;
       l_run *= alpha;
       m_run = m_new;
+      // accumulator register r of lane l holds row mfma_row(r, l), which
+      // depends on l only through l/32: read the 32 rows' factors into scalar
+      // registers and pick per half (no per-register lane indices to hold)
+      float a_row[32];
+#pragma unroll
+      for (int hh = 0; hh < 32; ++hh)
+        a_row[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), hh));
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float a = __shfl(alpha, mfma_row(r, lane), 64);
+        const int r0 = (r & 3) + 8 * (r >> 2);
+        const float a = half_ ? a_row[r0 + 4] : a_row[r0];
 #pragma unroll
         for (int t = 0; t < C::TPW; ++t) acc[t][r] *= a;
       }

@@ -182,19 +182,44 @@ template <int RK, int RV>
 struct PfCfg {
   static constexpr int KS = RK / 32;               // 16x16x32 k-steps of a score tile
   static constexpr int TPW = RV / 32 / kPfWaves;   // 32-dim V tiles per wave
-  static constexpr int VB = 3;                     // V blocks in registers (held or in flight)
+  // V blocks in registers (held or in flight): two at r_v = 1024, where the
+  // z accumulators take half of a wave's 256 registers
+  static constexpr int VB = RV >= 1024 ? 2 : 3;
+  static constexpr int UNR = VB == 3 ? 3 : 6;      // step unroll: V ring period and the period 3 of P
   static constexpr int KSTG = 4;                   // K ring stages in LDS
   static constexpr int CPR = RK / 8;               // 16-byte chunks per token row of a K block
   // K of a block is loaded by the four non-scorer waves, one piece per lane:
   // 2*16*RK bytes / 256 lanes = RK/8 bytes, 16 pieces per token row
   using KPiece = std::conditional_t<RK == 64, uint2, uint32_t>;
   static constexpr int PPC = 16 / (int)sizeof(KPiece);   // pieces per 16-byte chunk
+  // Wide latents (r_v = 1024) need all the registers for the z accumulators
+  // and the V ring: the scorers then keep the q~ score operands in LDS
+  // (written once per unit, read at every block) instead of registers.
+  static constexpr bool kQInLds = RV >= 1024;
   static_assert(RK % 32 == 0 && KS >= 1 && KS <= 2, "r_k in {32, 64}");
   static_assert(RV % (32 * kPfWaves) == 0 && TPW >= 1 && TPW <= 4, "r_v in {256, 512, 768, 1024}");
 };
 
 template <int N>
 using PfIC = std::integral_constant<int, N>;
+
+// The value, opaque to the compiler at this point: lane-dependent indices
+// derived from it are recomputed where they are used instead of being hoisted
+// out of the loops (32 precomputed row indices would hold 32 registers for
+// the whole kernel).
+__device__ __forceinline__ int pf_opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// f(PfIC<0>), ..., f(PfIC<N-1>), in order
+template <int N, typename F>
+__device__ __forceinline__ void pf_unroll(F&& f) {
+  if constexpr (N > 0) {
+    pf_unroll<N - 1>(f);
+    f(PfIC<N - 1>{});
+  }
+}
 
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
@@ -233,6 +258,8 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
   __shared__ float lrow_lds[kPfRows];      // row sums, for the single-range direct write
   // q~ of a scorer wave's 16 rows, from its MFMA result layout to the A layout
   __shared__ __attribute__((aligned(16))) float qf_lds[4][16][RK + 4];
+  // score operands of the scorer waves, when they are not held in registers
+  __shared__ __attribute__((aligned(16))) half8 qop_lds[C::kQInLds ? 4 : 1][C::KS][2][64];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -334,13 +361,19 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
         }
         qh[ks] = hi8;
         ql[ks] = lo8;
+        if constexpr (C::kQInLds) {
+          qop_lds[w][ks][0][lane] = hi8;
+          qop_lds[w][ks][1][lane] = lo8;
+        }
       }
     }
 
     // Plain (temporal) loads: unlike decode, every K and V block here is
     // re-read by the other heads' workgroups on this XCD and must stay in L2
     // (non-temporal loads cost 25% at 4 x 512 rows over 8192 positions).
-    const f16* vbase = vpool + ((size_t)(w * C::TPW * 32 + c32)) * kBlock + 8 * half_;
+    // per-lane V offset in halves (32-bit) on a uniform block base, so the
+    // loads can take the scalar-base address form
+    const uint32_t v_lane = (uint32_t)((w * C::TPW * 32 + c32) * kBlock + 8 * half_);
     // K of a block, loaded by the non-scorer waves (wave w-4 takes pieces
     // 64*(w-4) .. +63, 512 or 256 contiguous bytes): piece g = token g/16,
     // piece g%16 of its row; stored to its swizzled place in a ring stage
@@ -363,9 +396,10 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
     half8 vb[C::VB][C::TPW];
     auto load_v = [&](auto bufc, int phys) __attribute__((always_inline)) {
       constexpr int BUF = decltype(bufc)::value;
-      const f16* p = vbase + (size_t)phys * RV * kBlock;
+      const f16* p = vpool + (size_t)phys * RV * kBlock;
 #pragma unroll
-      for (int t = 0; t < C::TPW; ++t) vb[BUF][t] = *reinterpret_cast<const half8*>(p + t * 32 * kBlock);
+      for (int t = 0; t < C::TPW; ++t)
+        vb[BUF][t] = *reinterpret_cast<const half8*>(p + (v_lane + (uint32_t)(t * 32 * kBlock)));
     };
 
     floatx16 acc[2][C::TPW];
@@ -392,8 +426,13 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
       for (int ks = 0; ks < C::KS; ++ks) {
         const int c = 4 * ks + (lane >> 4);
         const half8 kf = *reinterpret_cast<const half8*>(&k_lds[ks4][(t * C::CPR + (c ^ swz(t))) * 8]);
-        sh = mfma16x16x32(kf, qh[ks], sh);
-        sl = mfma16x16x32(kf, ql[ks], sl);
+        if constexpr (C::kQInLds) {
+          sh = mfma16x16x32(kf, qop_lds[w][ks][0][lane], sh);
+          sl = mfma16x16x32(kf, qop_lds[w][ks][1][lane], sl);
+        } else {
+          sh = mfma16x16x32(kf, qh[ks], sh);
+          sl = mfma16x16x32(kf, ql[ks], sl);
+        }
       }
       return sh + sl;
     };
@@ -459,11 +498,12 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
       for (int rt = 0; rt < 2; ++rt) pa[rt] = *reinterpret_cast<const half8*>(&p_lds[PB][rt * 32 + c32][8 * half_]);
       const int4 fl = *reinterpret_cast<const int4*>(&flag_lds[PB][0]);
       if (fl.x | fl.y | fl.z | fl.w) {
+        const float* arow = &a_lds[PB][pf_opaque(4 * half_)];   // + mfma_row(r, lane) - 4*half_
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float a = a_lds[PB][rt * 32 + mfma_row(r, lane)];
+            const float a = arow[rt * 32 + (r & 3) + 8 * (r >> 2)];
 #pragma unroll
             for (int t = 0; t < C::TPW; ++t) acc[rt][t][r] *= a;
           }
@@ -499,70 +539,77 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
     // scalar load.
     const int phys0 = table[0];
     auto tab = [&](int b) { return b < nblk ? table[b] : phys0; };
-    int pv = tab(3);
+    int pv = tab(C::VB);
+    // Step ib uses V registers ib % VB and P buffer ib % 3; the loop runs
+    // UNR steps per trip so both are compile-time, and a partial trip runs
+    // the steps that remain.
+    auto run = [&](auto step) __attribute__((always_inline)) {
+      int ib = 0;
+      for (; ib + C::UNR - 1 < nblk; ib += C::UNR)
+        pf_unroll<C::UNR>([&](auto kc) __attribute__((always_inline)) {
+          constexpr int K = decltype(kc)::value;
+          step(PfIC<K % C::VB>{}, PfIC<K % 3>{}, ib + K);
+        });
+      pf_unroll<C::UNR - 1>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int K = decltype(kc)::value;
+        if (ib + K < nblk) step(PfIC<K % C::VB>{}, PfIC<K % 3>{}, ib + K);
+      });
+    };
     if (scorer) {
       load_v(PfIC<0>{}, phys0);
       load_v(PfIC<1>{}, tab(1));
-      load_v(PfIC<2>{}, tab(2));
+      if constexpr (C::VB > 2) load_v(PfIC<2>{}, tab(2));
       barrier_lds();                         // K of blocks 0, 1 stored
       softmax(0, score_mfma(0), 0);
       if (nblk > 1) softmax(1, score_mfma(1), 1);
       barrier_lds();                         // K of block 2 stored
-      auto step = [&](auto bufc, int ib) __attribute__((always_inline)) {
+      run([&](auto vbuf, auto pbuf, int ib) __attribute__((always_inline)) {
+        constexpr int PB = decltype(pbuf)::value;
         const int pv_now = pv;
-        pv = tab(ib + 4);
+        pv = tab(ib + C::VB + 1);
         const floatx4 sc = score_mfma((ib + 2) & 3);   // block ib+2 (a spare block past the end)
-        if (ib + 2 < nblk) softmax((decltype(bufc)::value + 2) % 3, sc, ib + 2);
-        accumulate(bufc, decltype(bufc)::value, ib);
-        load_v(bufc, pv_now);
+        if (ib + 2 < nblk) softmax((PB + 2) % 3, sc, ib + 2);
+        accumulate(vbuf, PB, ib);
+        load_v(vbuf, pv_now);                          // V of block ib+VB
         barrier_lds();
-      };
-      int ib = 0;
-      for (; ib + 2 < nblk; ib += 3) {
-        step(PfIC<0>{}, ib);
-        step(PfIC<1>{}, ib + 1);
-        step(PfIC<2>{}, ib + 2);
-      }
-      if (ib < nblk) step(PfIC<0>{}, ib);
-      if (ib + 1 < nblk) step(PfIC<1>{}, ib + 1);
+      });
     } else {
       // K of block b in flight in kr[b % 3] (blocks 3, 4 on entry).  The
-      // loads are issued in the loop's own order (K of block b+3 ahead of V of
-      // block b+1), so the compiler's wait counts at the loop entry match
-      // those of its back edge.
+      // loads are issued in the loop's own order (step ib issues K of block
+      // ib+5, then V of block ib+VB), so the compiler's wait counts at the loop
+      // entry match those of its back edge.
       KP kr[3];
       const KP k0 = load_k(phys0), k1 = load_k(tab(1));
       kr[2] = load_k(tab(2));
-      load_v(PfIC<0>{}, phys0);
-      kr[0] = load_k(tab(3));
-      load_v(PfIC<1>{}, tab(1));
-      kr[1] = load_k(tab(4));
-      load_v(PfIC<2>{}, tab(2));
+      if constexpr (C::VB == 3) {
+        load_v(PfIC<0>{}, phys0);
+        kr[0] = load_k(tab(3));
+        load_v(PfIC<1>{}, tab(1));
+        kr[1] = load_k(tab(4));
+        load_v(PfIC<2>{}, tab(2));
+      } else {
+        kr[0] = load_k(tab(3));
+        load_v(PfIC<0>{}, phys0);
+        kr[1] = load_k(tab(4));
+        load_v(PfIC<1>{}, tab(1));
+      }
       store_k(0, k0);
       store_k(1, k1);
       barrier_lds_b();
       store_k(2, kr[2]);
       barrier_lds_b();
       int pk = tab(5);
-      auto step = [&](auto bufc, int ib) __attribute__((always_inline)) {
-        constexpr int BUF = decltype(bufc)::value;
+      run([&](auto vbuf, auto pbuf, int ib) __attribute__((always_inline)) {
+        constexpr int PB = decltype(pbuf)::value;
         const int pv_now = pv, pk_now = pk;
-        pv = tab(ib + 4);
+        pv = tab(ib + C::VB + 1);
         pk = tab(ib + 6);
-        kr[(BUF + 2) % 3] = load_k(pk_now);
-        accumulate(bufc, BUF, ib);
-        load_v(bufc, pv_now);
-        store_k((ib + 3) & 3, kr[BUF]);      // K of block ib+3
+        kr[(PB + 2) % 3] = load_k(pk_now);   // K of block ib+5
+        accumulate(vbuf, PB, ib);
+        load_v(vbuf, pv_now);                // V of block ib+VB
+        store_k((ib + 3) & 3, kr[PB]);       // K of block ib+3
         barrier_lds_b();
-      };
-      int ib = 0;
-      for (; ib + 2 < nblk; ib += 3) {
-        step(PfIC<0>{}, ib);
-        step(PfIC<1>{}, ib + 1);
-        step(PfIC<2>{}, ib + 2);
-      }
-      if (ib < nblk) step(PfIC<0>{}, ib);
-      if (ib + 1 < nblk) step(PfIC<1>{}, ib + 1);
+      });
     }
 
     if (zdirect) {
@@ -573,11 +620,12 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
         if (lane < 16) lrow_lds[srow] = l_row;
       }
       __syncthreads();
+      const int rlane = pf_opaque(4 * half_);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int rr = rt * 32 + mfma_row(r, lane);
+          const int rr = rt * 32 + (r & 3) + 8 * (r >> 2) + rlane;     // mfma_row(r, lane)
           if (rr < nrows) {
             const float inv = 1.f / lrow_lds[rr];
             float* zp = zdirect + ((size_t)(row0 + rr) * H + h) * RV + w * C::TPW * 32 + c32;
@@ -598,11 +646,12 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
         part_ml[((size_t)sl * H + h) * 2 + 1] = l_row;
       }
     }
+    const int* srowp = &slot_lds[pf_opaque(4 * half_)];      // + mfma_row(r, lane) - 4*half_
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int sl = slot_lds[rt * 32 + mfma_row(r, lane)];
+        const int sl = srowp[rt * 32 + (r & 3) + 8 * (r >> 2)];
         if (sl >= 0) {
           float* zp = part_z + ((size_t)sl * H + h) * RV + w * C::TPW * 32 + c32;
 #pragma unroll
