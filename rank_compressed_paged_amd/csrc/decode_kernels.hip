@@ -697,7 +697,8 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 DecodeLayout decode_layout(const Shape& s, int batch, int max_context_len, int grid) {
   DecodeLayout L{};
   const long long blocks_ub = (long long)batch * ((max_context_len + kBlock - 1) / kBlock);
-  long long cap = (blocks_ub + kMinBlocksPerWG - 1) / kMinBlocksPerWG;
+  const int wmin = min_blocks_per_wg(blocks_ub);
+  long long cap = (blocks_ub + wmin - 1) / wmin;
   if (cap < 1) cap = 1;
   if (cap > kMaxGrid) cap = kMaxGrid;
   if (grid > 0 && grid < cap) cap = grid;      // carved for a known launch grid

@@ -20,10 +20,15 @@ inline void launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t st, hipEve
     hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
 }
 
-// Attention workgroups never take fewer than this many 16-token blocks when
-// the batch is big enough: each range flushes H*r_v fp32 of partial state, so
-// short ranges would spend more HBM traffic on partials than on latents.
-constexpr int kMinBlocksPerWG = 8;
+// Shortest range of 16-token blocks an attention workgroup takes, by the
+// host's bound on the batch's blocks.  Each range flushes H*r_v fp32 of
+// partial state at its end, all ranges at about the same time: longer ranges
+// mean fewer partials and a shorter write burst.  Small decodes (up to 1,024
+// blocks) are latency-bound instead and want every block in flight at once.
+// Measured on MI355X at 32 heads, r_v 1024: 4 blocks took a 1 x 1,024-token
+// decode's attention from 22 to 15 us; 12 blocks took 16 x 2,048 tokens from
+// 46 to 43 us (8 and 16 were slower); larger batches fill every CU anyway.
+constexpr int min_blocks_per_wg(long long blocks_ub) { return blocks_ub <= 1024 ? 4 : 12; }
 // Hard cap on attention workgroups (sizes the workspace without a device query).
 constexpr int kMaxGrid = 1024;
 // Lazy-rescale threshold (log2 units) of the running softmax maximum.

@@ -121,19 +121,20 @@ def permute_batch(case, perm):
 @pytest.mark.parametrize("batch", [48, 8])
 def test_batch_order_invariance_bit_identical(batch):
     """Permuting the batch rows permutes the outputs bit for bit.  Every
-    sequence here holds the same number of blocks, 40 (lengths differ inside
-    the last block), and the batch at most 2,048 blocks, so the plan launches
-    one workgroup per 8 blocks and each range is a whole fifth of one sequence
-    in any order: no rounding depends on a row's place in the batch.  48 rows
-    take the MFMA projections, 8 the VALU ones."""
+    sequence here holds the same number of blocks, 36 (lengths differ inside
+    the last block), and the batch few enough blocks that the plan launches
+    one workgroup per shortest range (12 blocks above 1,024 blocks, 4 up to
+    there): each range is a whole third (ninth) of one sequence in any order,
+    so no rounding depends on a row's place in the batch.  48 rows take the
+    MFMA projections, 8 the VALU ones."""
     dev = gpu()
     rng = np.random.default_rng(700 + batch)
-    lens = (16 * 40 - rng.integers(0, 16, size=batch)).astype(np.int32)
-    assert batch * 40 <= 2048
+    lens = (16 * 36 - rng.integers(0, 16, size=batch)).astype(np.int32)
+    assert batch * 36 <= 256 * 12                # one workgroup per range on 256 CUs
     case = small_main_case(700 + batch, lens)
     perm = rng.permutation(batch)
     moved = permute_batch(case, perm)
-    log(f"batch order: {batch} rows of 625..640 tokens")
+    log(f"batch order: {batch} rows of 561..576 tokens")
     for scale in (1.0 / math.sqrt(128), 1.0):
         a = decode_gpu(to_dev(case, dev), lens, scale, dev).cpu().numpy()
         b = decode_gpu(to_dev(moved, dev), moved["context_lens"], scale, dev).cpu().numpy()
