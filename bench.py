@@ -3,7 +3,9 @@
 A step is one pass of the whole path over the batch: append one new K/V row
 per sequence into the latent paged cache (projection + scatter), then decode
 every sequence over its latent cache (query projection, latent scores, split
-softmax, V-latent accumulation, merge, up-projection).  Workload: batch 64,
+softmax, V-latent accumulation, merge, up-projection), through
+starkv_decode_step (the append and the query projection share its first
+launch).  Workload: batch 64,
 32 heads, head_dim 128, r_k 64, r_v 1024, 8192 cached tokens per sequence;
 each step writes the token at position 8192 (overwriting the previous step's,
 so every step does identical work) and decodes over 8193 tokens.
@@ -327,10 +329,9 @@ def config_report(cfg_id: int, steps: int, warmup: int, graph: bool = False, cpu
     def step(s):
         pos_np, pos, lens = pos_all[s], pos_dev[s], lens_dev[s]
         for g in layers:
-            starkv.append(g["k_new"], g["v_new"], g["b_k"], g["b_v"], g["block_tables"], seqs, pos,
-                          g["k_pool"], g["v_pool"])
-            starkv.decode(g["q"], g["b_k"], g["b_v"], g["k_pool"], g["v_pool"], g["block_tables"], lens, scale,
-                          max_context_len=max_len, workspace=ws, out=out)
+            starkv.decode_step(g["k_new"], g["v_new"], g["b_k"], g["b_v"], seqs, pos, g["q"], g["b_k"], g["b_v"],
+                               g["k_pool"], g["v_pool"], g["block_tables"], lens, scale, max_context_len=max_len,
+                               workspace=ws, out=out)
         return int(pos_np.astype(np.int64).sum()) + cfg.batch
 
     for s in range(warmup):
@@ -583,9 +584,9 @@ def main():
     out = torch.empty_like(g["q"])
 
     def step():
-        starkv.append(kn, vn, g["b_k"], g["b_v"], g["block_tables"], seqs, pos, g["k_pool"], g["v_pool"])
-        starkv.decode(g["q"], g["b_k"], g["b_v"], g["k_pool"], g["v_pool"], g["block_tables"], lens, scale,
-                      max_context_len=max_len, workspace=ws, out=out)
+        starkv.decode_step(kn, vn, g["b_k"], g["b_v"], seqs, pos, g["q"], g["b_k"], g["b_v"], g["k_pool"],
+                           g["v_pool"], g["block_tables"], lens, scale, max_context_len=max_len, workspace=ws,
+                           out=out)
 
     for _ in range(args.warmup):
         step()

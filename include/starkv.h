@@ -161,6 +161,28 @@ starkv_status starkv_decode(const starkv_dims* dims, int32_t batch, int32_t max_
                             void* out, void* stream);
 
 /*
+ * starkv_decode_step - one decode step of a serving loop: starkv_append of the
+ * step's new rows, then starkv_decode of the batch (the method's two steps:
+ * new K/V rows projected into latents and written in compressed paged form,
+ * then attention over the latents; Proxima README, opening description of
+ * STAR-KV).  The result, the pools afterwards and every argument's meaning,
+ * layout, alignment and error are exactly those of the two calls in that
+ * order on `stream` (context_lens already count the new tokens); the append's
+ * projection, the query projection and the decode plan share the first
+ * launch, so the step takes one launch fewer and the two projections run side
+ * by side.  n_new == 0 is a plain decode.  Workspace: as for starkv_decode.
+ */
+starkv_status starkv_decode_step(const starkv_dims* dims, int32_t batch, int32_t max_context_len,
+                                 int32_t n_new, const void* k_new, const void* v_new,
+                                 const void* w_k, const void* w_v,
+                                 const int32_t* token_seq, const int32_t* token_pos,
+                                 const void* q, const void* b_k, const void* b_v,
+                                 void* k_cache, void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 float scale, void* workspace, size_t workspace_bytes,
+                                 void* out, void* stream);
+
+/*
  * starkv_decode_noalloc - starkv_decode for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc): the same operation, arguments and results (bit for
@@ -292,7 +314,8 @@ const char* starkv_status_string(starkv_status status);
  * Measurement hooks (host-only, process-wide, not for use while another
  * thread is decoding).  Between starkv_profile_begin() and
  * starkv_profile_end(), every starkv_decode, starkv_decode_noalloc,
- * starkv_prefill and starkv_uncompressed_decode call brackets its attention
+ * starkv_decode_step, starkv_prefill and starkv_uncompressed_decode call
+ * brackets its attention
  * kernel with a pair of HIP events on its own stream (up
  * to 4096 calls).  starkv_profile_end() waits for those events, writes the summed
  * kernel time in milliseconds and the number of bracketed launches, and

@@ -13,7 +13,7 @@ import os
 
 __all__ = [
     "Dims", "StarkvError", "load_library", "library_path", "status_string",
-    "decode_workspace_size", "decode", "decode_noalloc", "uncompressed_decode", "append", "prefill_workspace_size", "prefill", "profile_begin",
+    "decode_workspace_size", "decode", "decode_noalloc", "decode_step", "uncompressed_decode", "append", "prefill_workspace_size", "prefill", "profile_begin",
     "profile_end", "stream_read_probe", "check_block_tables",
     "BLOCK_SIZE",
 ]
@@ -76,6 +76,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.starkv_decode.restype = ctypes.c_int
     lib.starkv_decode_noalloc.argtypes = [dp, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp]
     lib.starkv_decode_noalloc.restype = ctypes.c_int
+    lib.starkv_decode_step.argtypes = [dp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp,
+                                       sz, vp, vp]
+    lib.starkv_decode_step.restype = ctypes.c_int
     lib.starkv_uncompressed_decode_workspace_size.argtypes = [dp, i32, i32]
     lib.starkv_uncompressed_decode_workspace_size.restype = sz
     lib.starkv_uncompressed_decode.argtypes = [dp, i32, i32, vp, vp, vp, vp, vp, f32, vp, sz, vp, vp]
@@ -223,6 +226,56 @@ def decode(q, b_k, b_v, k_cache, v_cache, block_tables, context_lens, scale, *,
                              float(scale), ctypes.c_void_p(ws_ptr + pad), workspace.numel() - pad,
                              ctypes.c_void_p(optr), _stream(stream))
     _check(code, "starkv_decode")
+    return out
+
+
+def decode_step(k_new, v_new, w_k, w_v, token_seq, token_pos, q, b_k, b_v, k_cache, v_cache, block_tables,
+                context_lens, scale, *, max_context_len=None, workspace=None, out=None, stream=None):
+    """append(k_new, v_new, w_k, w_v, ..., token_seq, token_pos) then decode(...),
+    in one library call whose first launch holds the append and the query
+    projection (starkv_decode_step).  context_lens count the new tokens.
+    Arguments as in append() and decode(); returns out [B, H, d] fp16."""
+    import torch
+    lib = load_library()
+    batch, heads, d = q.shape
+    n = k_new.shape[0]
+    dims = dims_of(k_cache, v_cache, block_tables, d, heads=heads)
+    kvh = dims.num_kv_heads
+    if max_context_len is None:
+        max_context_len = BLOCK_SIZE * block_tables.shape[1]
+    ptrs = [
+        _need(k_new, "k_new", torch.float16, 3), _need(v_new, "v_new", torch.float16, 3),
+        _need(w_k, "w_k", torch.float16, 3), _need(w_v, "w_v", torch.float16, 2),
+        _need(token_seq, "token_seq", torch.int32, 1), _need(token_pos, "token_pos", torch.int32, 1),
+        _need(q, "q", torch.float16, 3), _need(b_k, "b_k", torch.float16, 3), _need(b_v, "b_v", torch.float16, 2),
+        _need(k_cache, "k_cache", torch.float16, 4), _need(v_cache, "v_cache", torch.float16, 3),
+        _need(block_tables, "block_tables", torch.int32, 2), _need(context_lens, "context_lens", torch.int32, 1),
+    ]
+    if tuple(k_new.shape) != (n, kvh, d) or tuple(v_new.shape) != (n, kvh, d):
+        raise ValueError("new rows must be [n, H_kv, d]")
+    if token_seq.shape[0] != n or token_pos.shape[0] != n:
+        raise ValueError("token_seq / token_pos must have one entry per new row")
+    if block_tables.shape[0] != batch or context_lens.shape[0] != batch:
+        raise ValueError("block_tables / context_lens rows must match q's batch")
+    if tuple(w_k.shape) != (kvh, dims.rank_k, d) or tuple(w_v.shape) != (dims.rank_v, kvh * d):
+        raise ValueError("down-projection shapes do not match the caches")
+    if tuple(b_k.shape) != (kvh, dims.rank_k, d) or tuple(b_v.shape) != (dims.rank_v, kvh * d):
+        raise ValueError("projection shapes do not match the caches")
+    need = lib.starkv_decode_workspace_size(ctypes.byref(dims), batch, int(max_context_len))
+    if need == 0:
+        _check(1, "starkv_decode_workspace_size")
+    if workspace is None:
+        workspace = _scratch(need + 256, q.device, stream)
+    ws_ptr = _need(workspace, "workspace", torch.uint8, 1)
+    pad = (-ws_ptr) % 256
+    if out is None:
+        out = torch.empty_like(q)
+        _own_out(out, q.device, stream)
+    optr = _need(out, "out", torch.float16, 3)
+    code = lib.starkv_decode_step(ctypes.byref(dims), batch, int(max_context_len), n,
+                                  *[ctypes.c_void_p(p) for p in ptrs], float(scale), ctypes.c_void_p(ws_ptr + pad),
+                                  workspace.numel() - pad, ctypes.c_void_p(optr), _stream(stream))
+    _check(code, "starkv_decode_step")
     return out
 
 

@@ -21,6 +21,7 @@
 
 #include <algorithm>
 
+#include "append_bodies.h"
 #include "common.h"
 #include "launch.h"
 
@@ -30,13 +31,13 @@ namespace starkv {
 // 1. query projection + plan
 // ---------------------------------------------------------------------------
 
-constexpr int kPlanThreads = 256;
-
+// Inclusive scan over the NT threads of a workgroup.
+template <int NT>
 __device__ int block_inclusive_scan(int v, int* sh) {
   const int tid = threadIdx.x;
   sh[tid] = v;
   __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
+  for (int off = 1; off < NT; off <<= 1) {
     int t = (tid >= off) ? sh[tid - off] : 0;
     __syncthreads();
     sh[tid] += t;
@@ -48,20 +49,22 @@ __device__ int block_inclusive_scan(int v, int* sh) {
 // Equal split of the batch's blocks over `grid` workgroups.  prefix[b] is the
 // first global block of sequence b; a sequence spanning workgroups g0..g1 owns
 // partial slots slot_base[b] .. slot_base[b] + (g1 - g0); first[g] is the
-// (non-empty) sequence holding workgroup g's first block.
+// (non-empty) sequence holding workgroup g's first block.  Run by all NT
+// threads of one workgroup.
+template <int NT>
 __device__ void build_plan(const int32_t* __restrict__ lens, int batch, int grid,
                            int32_t* __restrict__ plan) {
-  __shared__ int sh[kPlanThreads];
+  __shared__ int sh[NT];
   const int tid = threadIdx.x;
   int32_t* prefix = plan + 2;
   int32_t* sbase = plan + 3 + batch;
   int32_t* first = plan + 4 + 2 * batch;
   int carry = 0;
-  for (int base = 0; base < batch; base += kPlanThreads) {
+  for (int base = 0; base < batch; base += NT) {
     const int i = base + tid;
     const int v = (i < batch) ? (lens[i] + kBlock - 1) / kBlock : 0;
-    const int x = block_inclusive_scan(v, sh);
-    const int chunk = sh[kPlanThreads - 1];
+    const int x = block_inclusive_scan<NT>(v, sh);
+    const int chunk = sh[NT - 1];
     if (i < batch) prefix[i + 1] = carry + x;
     carry += chunk;
     __syncthreads();
@@ -69,17 +72,17 @@ __device__ void build_plan(const int32_t* __restrict__ lens, int batch, int grid
   const int total = carry;
   const int W = max(1, (total + grid - 1) / grid);
   int carry1 = 0, carry2 = 0;
-  for (int base = 0; base < batch; base += kPlanThreads) {
+  for (int base = 0; base < batch; base += NT) {
     const int i = base + tid;
     const int v = (i < batch) ? (lens[i] + kBlock - 1) / kBlock : 0;
-    const int x = block_inclusive_scan(v, sh);
-    const int chunk1 = sh[kPlanThreads - 1];
+    const int x = block_inclusive_scan<NT>(v, sh);
+    const int chunk1 = sh[NT - 1];
     __syncthreads();
     const int incl = carry1 + x;
     const int excl = incl - v;
     const int np = (v > 0) ? ((incl - 1) / W - excl / W + 1) : 0;
-    const int y = block_inclusive_scan(np, sh);
-    const int chunk2 = sh[kPlanThreads - 1];
+    const int y = block_inclusive_scan<NT>(np, sh);
+    const int chunk2 = sh[NT - 1];
     if (i < batch) sbase[i + 1] = carry2 + y;
     // ranges starting inside this sequence: g*W in [excl, incl), g < grid
     if (i < batch && v > 0)
@@ -96,23 +99,19 @@ __device__ void build_plan(const int32_t* __restrict__ lens, int batch, int grid
   }
 }
 
-// MFMA path: a workgroup of 4 waves takes a 32-row batch tile and four
-// (head, 32-latent) output tiles; both operands are contiguous along d.
-__global__ void __launch_bounds__(256)
-qproj_plan_mfma_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, float* __restrict__ qt,
-                       int batch, int H, int KV, int D, int RK, float scale2,
-                       const int32_t* __restrict__ lens, int grid, int32_t* __restrict__ plan) {
-  if (lens != nullptr && blockIdx.x == gridDim.x - 1) {
-    build_plan(lens, batch, grid, plan);
-    return;
-  }
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+// MFMA q~ projection, one unit = a 32-row batch tile and four (head,
+// 32-latent) output tiles, run by 256 threads (tid; four waves); both
+// operands are contiguous along d.
+__device__ __forceinline__ void qproj_mfma_body(int unit, int tid, const f16* __restrict__ q,
+                                                const f16* __restrict__ bk, float* __restrict__ qt, int batch, int H,
+                                                int KV, int D, int RK, float scale2) {
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const int rtiles = RK / 32;
   const int npairs = H * rtiles;
   const int groups = (npairs + 3) / 4;
-  const int btile = blockIdx.x / groups;
-  const int pair = (blockIdx.x % groups) * 4 + w;
+  const int btile = unit / groups;
+  const int pair = (unit % groups) * 4 + w;
   if (pair >= npairs) return;
   const int head = pair / rtiles;
   const int r = (pair % rtiles) * 32 + (lane & 31);
@@ -143,16 +142,10 @@ qproj_plan_mfma_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, fl
   }
 }
 
-// VALU path (small batches): one thread per (b, h, r).
-__global__ void __launch_bounds__(256)
-qproj_plan_valu_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, float* __restrict__ qt,
-                       int batch, int H, int KV, int D, int RK, float scale2,
-                       const int32_t* __restrict__ lens, int grid, int32_t* __restrict__ plan) {
-  if (lens != nullptr && blockIdx.x == gridDim.x - 1) {
-    build_plan(lens, batch, grid, plan);
-    return;
-  }
-  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+// VALU q~ projection: one thread per (row, head, latent) output idx.
+__device__ __forceinline__ void qproj_valu_body(long long idx, const f16* __restrict__ q, const f16* __restrict__ bk,
+                                                float* __restrict__ qt, int batch, int H, int KV, int D, int RK,
+                                                float scale2) {
   if (idx >= (long long)batch * H * RK) return;
   const int r = (int)(idx % RK);
   const int head = (int)((idx / RK) % H);
@@ -162,6 +155,56 @@ qproj_plan_valu_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, fl
   qt[idx] = dot_f16(qp, bp, D) * scale2;
 }
 
+__global__ void __launch_bounds__(256)
+qproj_plan_mfma_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, float* __restrict__ qt,
+                       int batch, int H, int KV, int D, int RK, float scale2,
+                       const int32_t* __restrict__ lens, int grid, int32_t* __restrict__ plan) {
+  if (lens != nullptr && blockIdx.x == gridDim.x - 1) {
+    build_plan<256>(lens, batch, grid, plan);
+    return;
+  }
+  qproj_mfma_body(blockIdx.x, threadIdx.x, q, bk, qt, batch, H, KV, D, RK, scale2);
+}
+
+// VALU path (small batches): one thread per (b, h, r).
+__global__ void __launch_bounds__(256)
+qproj_plan_valu_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, float* __restrict__ qt,
+                       int batch, int H, int KV, int D, int RK, float scale2,
+                       const int32_t* __restrict__ lens, int grid, int32_t* __restrict__ plan) {
+  if (lens != nullptr && blockIdx.x == gridDim.x - 1) {
+    build_plan<256>(lens, batch, grid, plan);
+    return;
+  }
+  qproj_valu_body((long long)blockIdx.x * blockDim.x + threadIdx.x, q, bk, qt, batch, H, KV, D, RK, scale2);
+}
+
+// Prologue of a decode step (starkv_decode_step): one launch of 512-thread
+// workgroups runs the step's append (the first nA workgroups: V and K roles as
+// in a shared append launch), the q~ projection (the next nQ: two 256-thread
+// MFMA units, or 512 VALU outputs, each) and, in the last workgroup, the
+// plan.  The three are independent: the append writes the new tokens' slots,
+// which only the attention launch after this one reads.
+__global__ void __launch_bounds__(512)
+step_prologue_kernel(const f16* __restrict__ k, const f16* __restrict__ v, const f16* __restrict__ wk,
+                     const f16* __restrict__ wv, int n, SlotOf where, f16* __restrict__ kc, f16* __restrict__ vc,
+                     AppendRoles roles, int nA, const f16* __restrict__ q, const f16* __restrict__ bk,
+                     float* __restrict__ qt, int batch, int H, int KV, int D, int RK, int RV, float scale2,
+                     bool qmfma, int nQ, const int32_t* __restrict__ lens, int grid, int32_t* __restrict__ plan) {
+  const int bid = blockIdx.x;
+  if (bid < nA) {
+    append_role(bid, roles, k, v, wk, wv, n, KV, D, RK, RV, where, kc, vc);
+    return;
+  }
+  if (bid < nA + nQ) {
+    const int qb = bid - nA;
+    if (qmfma)
+      qproj_mfma_body(2 * qb + ((int)threadIdx.x >> 8), threadIdx.x & 255, q, bk, qt, batch, H, KV, D, RK, scale2);
+    else
+      qproj_valu_body((long long)qb * 512 + threadIdx.x, q, bk, qt, batch, H, KV, D, RK, scale2);
+    return;
+  }
+  build_plan<512>(lens, batch, grid, plan);
+}
 
 // ---------------------------------------------------------------------------
 // 3. merge of a sequence's partials
@@ -827,21 +870,18 @@ hipError_t table_check_enqueue(const int32_t* block_tables, const int32_t* conte
   return hipGetLastError();
 }
 
-hipError_t decode_enqueue(const DecodeLaunch& a) {
+// Launches 2-4 of a decode (attention, merge, up-projection), after q~ and
+// the plan are in the workspace.
+static hipError_t decode_after_prologue(const DecodeLaunch& a) {
   const Shape& s = a.s;
   int32_t* plan = reinterpret_cast<int32_t*>(a.ws + a.lay.off_plan);
   float* qt = reinterpret_cast<float*>(a.ws + a.lay.off_qt);
   float* pml = reinterpret_cast<float*>(a.ws + a.lay.off_ml);
   float* pz = reinterpret_cast<float*>(a.ws + a.lay.off_z);
   float* zf = reinterpret_cast<float*>(a.ws + a.lay.off_zf);
-  const float scale2 = a.scale * kLog2e;
-
-  // 1. query projection + plan (plan = last workgroup)
-  hipError_t err = launch_qproj(s, a.batch, a.q, a.b_k, scale2, qt, a.context_lens, a.grid, plan, a.stream);
-  if (err != hipSuccess) return err;
 
   // 2. latent attention (timed by its own dispatch when events are given)
-  err = launch_attn_kernel(a, qt, plan, pz, pml);
+  hipError_t err = launch_attn_kernel(a, qt, plan, pz, pml);
   if (err != hipSuccess) return err;
 
   // 3. merge, 4. up-projection (one launch for few (sequence, head) pairs at d = 128)
@@ -854,6 +894,46 @@ hipError_t decode_enqueue(const DecodeLaunch& a) {
   err = launch_merge(s, a.batch, pz, pml, plan, a.context_lens, zf, a.stream);
   if (err != hipSuccess) return err;
   return launch_upproj(s, a.batch, zf, a.b_v, a.out, a.stream);
+}
+
+hipError_t decode_enqueue(const DecodeLaunch& a) {
+  int32_t* plan = reinterpret_cast<int32_t*>(a.ws + a.lay.off_plan);
+  float* qt = reinterpret_cast<float*>(a.ws + a.lay.off_qt);
+  // 1. query projection + plan (plan = last workgroup)
+  const hipError_t err =
+      launch_qproj(a.s, a.batch, a.q, a.b_k, a.scale * kLog2e, qt, a.context_lens, a.grid, plan, a.stream);
+  if (err != hipSuccess) return err;
+  return decode_after_prologue(a);
+}
+
+hipError_t decode_step_enqueue(const DecodeLaunch& a, const AppendLaunch& ap) {
+  const Shape& s = a.s;
+  if (ap.n == 0) return decode_enqueue(a);
+  const AppendRoles r = append_roles(s, ap.n);
+  const long long nA = r.nv + r.kwg;
+  // the many-token V side has its own kernel: append, then decode
+  if (r.vrows || nA * 512 > (1LL << 30)) {
+    const hipError_t err = append_enqueue(ap);
+    if (err != hipSuccess) return err;
+    return decode_enqueue(a);
+  }
+  int32_t* plan = reinterpret_cast<int32_t*>(a.ws + a.lay.off_plan);
+  float* qt = reinterpret_cast<float*>(a.ws + a.lay.off_qt);
+  const bool qmfma = a.batch >= kSmallBatch && s.RK % 32 == 0 && s.D % 16 == 0;
+  const long long units = ((a.batch + 31LL) / 32) * ((s.H * (s.RK / 32) + 3) / 4);
+  const long long nQ = qmfma ? (units + 1) / 2 : ((long long)a.batch * s.H * s.RK + 511) / 512;
+  const long long grid = nA + nQ + 1;
+  if (grid * 512 > (1LL << 31)) return hipErrorInvalidConfiguration;
+  const SlotOf where{ap.block_tables, ap.token_seq, ap.token_pos, s.MB};
+  hipLaunchKernelGGL(step_prologue_kernel, dim3((unsigned)grid), dim3(512), 0, a.stream,
+                     static_cast<const f16*>(ap.k), static_cast<const f16*>(ap.v), static_cast<const f16*>(ap.w_k),
+                     static_cast<const f16*>(ap.w_v), ap.n, where, static_cast<f16*>(ap.k_cache),
+                     static_cast<f16*>(ap.v_cache), r, (int)nA, static_cast<const f16*>(a.q),
+                     static_cast<const f16*>(a.b_k), qt, a.batch, s.H, s.KV, s.D, s.RK, s.RV, a.scale * kLog2e, qmfma,
+                     (int)nQ, a.context_lens, a.grid, plan);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return decode_after_prologue(a);
 }
 
 }  // namespace starkv

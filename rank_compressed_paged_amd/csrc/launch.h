@@ -130,6 +130,11 @@ struct AppendLaunch {
 
 hipError_t append_enqueue(const AppendLaunch& a);
 
+// A decode step: the append's rows, then the decode, with the append, the q~
+// projection and the plan in one first launch (append then decode when the
+// append needs the many-token V kernel).
+hipError_t decode_step_enqueue(const DecodeLaunch& a, const AppendLaunch& ap);
+
 // ------------------------------------------------ uncompressed paged decode
 // Partition of a sequence per workgroup: the largest power of two in
 // [kPlainMinPB, kPlainMaxPB] blocks that still leaves kPlainTargetWGs

@@ -105,14 +105,15 @@ starkv_status check_plain_dims(const starkv_dims* d) {
   return STARKV_OK;
 }
 
-// Shared body of starkv_decode and starkv_decode_noalloc.  `tight`: carve the
-// workspace for the launch grid actually used (the no-allocation scratch),
-// instead of for the grid cap that starkv_decode_workspace_size assumes.  The
-// grid, and so every partial split and every result bit, is the same.
-starkv_status decode_call(const starkv_dims* dims, int32_t batch, int32_t max_context_len, const void* q,
+// Checks of starkv_decode, starkv_decode_noalloc and starkv_decode_step, and
+// their launch description.  `tight`: carve the workspace for the launch grid
+// actually used (the no-allocation scratch), instead of for the grid cap that
+// starkv_decode_workspace_size assumes.  The grid, and so every partial split
+// and every result bit, is the same.
+starkv_status make_decode(const starkv_dims* dims, int32_t batch, int32_t max_context_len, const void* q,
                           const void* b_k, const void* b_v, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, const int32_t* context_lens, float scale, void* workspace,
-                          size_t workspace_bytes, bool tight, void* out, void* stream) {
+                          size_t workspace_bytes, bool tight, void* out, void* stream, DecodeLaunch& a) {
   const starkv_status ds = check_dims(dims);
   if (ds != STARKV_OK) return ds;
   if (!decode_args_ok(dims, batch, max_context_len)) return STARKV_ERR_INVALID_ARG;
@@ -137,8 +138,7 @@ starkv_status decode_call(const starkv_dims* dims, int32_t batch, int32_t max_co
     lay = decode_layout(s, batch, max_context_len, grid);
     if (workspace_bytes < lay.bytes) return STARKV_ERR_WORKSPACE;
   }
-
-  DecodeLaunch a{};
+  a = DecodeLaunch{};
   a.s = s;
   a.batch = batch;
   a.grid = grid;
@@ -154,9 +154,50 @@ starkv_status decode_call(const starkv_dims* dims, int32_t batch, int32_t max_co
   a.lay = lay;
   a.out = out;
   a.stream = static_cast<hipStream_t>(stream);
+  return STARKV_OK;
+}
 
+starkv_status decode_call(const starkv_dims* dims, int32_t batch, int32_t max_context_len, const void* q,
+                          const void* b_k, const void* b_v, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, float scale, void* workspace,
+                          size_t workspace_bytes, bool tight, void* out, void* stream) {
+  DecodeLaunch a{};
+  const starkv_status st = make_decode(dims, batch, max_context_len, q, b_k, b_v, k_cache, v_cache, block_tables,
+                                       context_lens, scale, workspace, workspace_bytes, tight, out, stream, a);
+  if (st != STARKV_OK) return st;
   profile_events(a.ev_attn_start, a.ev_attn_stop);
   return decode_enqueue(a) == hipSuccess ? STARKV_OK : STARKV_ERR_HIP;
+}
+
+// Checks of starkv_append (and of the append part of starkv_decode_step) and
+// its launch description; n_tokens == 0 gives a launch with n = 0.
+starkv_status make_append(const starkv_dims* dims, int32_t n_tokens, const void* k, const void* v, const void* w_k,
+                          const void* w_v, const int32_t* block_tables, const int32_t* token_seq,
+                          const int32_t* token_pos, void* k_cache, void* v_cache, void* stream, AppendLaunch& a) {
+  const starkv_status ds = check_dims(dims);
+  if (ds != STARKV_OK) return ds;
+  if (n_tokens < 0 || n_tokens > (1 << 24)) return STARKV_ERR_INVALID_ARG;
+  a = AppendLaunch{};
+  a.s = shape_of(dims);
+  a.n = n_tokens;
+  a.stream = static_cast<hipStream_t>(stream);
+  if (n_tokens == 0) return STARKV_OK;
+  if (!k || !v || !w_k || !w_v || !block_tables || !token_seq || !token_pos || !k_cache || !v_cache)
+    return STARKV_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) ||
+      !aligned(block_tables, 4) || !aligned(token_seq, 4) || !aligned(token_pos, 4) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16))
+    return STARKV_ERR_INVALID_ARG;
+  a.k = k;
+  a.v = v;
+  a.w_k = w_k;
+  a.w_v = w_v;
+  a.block_tables = block_tables;
+  a.token_seq = token_seq;
+  a.token_pos = token_pos;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  return STARKV_OK;
 }
 
 }  // namespace
@@ -297,33 +338,35 @@ starkv_status starkv_append(const starkv_dims* dims, int32_t n_tokens, const voi
                             const void* w_k, const void* w_v, const int32_t* block_tables,
                             const int32_t* token_seq, const int32_t* token_pos, void* k_cache, void* v_cache,
                             void* stream) {
-  const starkv_status ds = check_dims(dims);
-  if (ds != STARKV_OK) return ds;
-  if (n_tokens < 0 || n_tokens > (1 << 24)) return STARKV_ERR_INVALID_ARG;
-  if (n_tokens == 0) return STARKV_OK;
-  if (!k || !v || !w_k || !w_v || !block_tables || !token_seq || !token_pos || !k_cache || !v_cache)
-    return STARKV_ERR_INVALID_ARG;
-  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) ||
-      !aligned(block_tables, 4) || !aligned(token_seq, 4) || !aligned(token_pos, 4) || !aligned(k_cache, 16) ||
-      !aligned(v_cache, 16))
-    return STARKV_ERR_INVALID_ARG;
+  AppendLaunch a{};
+  const starkv_status st =
+      make_append(dims, n_tokens, k, v, w_k, w_v, block_tables, token_seq, token_pos, k_cache, v_cache, stream, a);
+  if (st != STARKV_OK || n_tokens == 0) return st;
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) return STARKV_ERR_HIP;
-  AppendLaunch a{};
-  a.s = shape_of(dims);
-  a.n = n_tokens;
   a.cus = device_cus(device);
-  a.k = k;
-  a.v = v;
-  a.w_k = w_k;
-  a.w_v = w_v;
-  a.block_tables = block_tables;
-  a.token_seq = token_seq;
-  a.token_pos = token_pos;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.stream = static_cast<hipStream_t>(stream);
   return append_enqueue(a) == hipSuccess ? STARKV_OK : STARKV_ERR_HIP;
+}
+
+starkv_status starkv_decode_step(const starkv_dims* dims, int32_t batch, int32_t max_context_len, int32_t n_new,
+                                 const void* k_new, const void* v_new, const void* w_k, const void* w_v,
+                                 const int32_t* token_seq, const int32_t* token_pos, const void* q, const void* b_k,
+                                 const void* b_v, void* k_cache, void* v_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, float scale, void* workspace, size_t workspace_bytes,
+                                 void* out, void* stream) {
+  AppendLaunch ap{};
+  starkv_status st = make_append(dims, n_new, k_new, v_new, w_k, w_v, block_tables, token_seq, token_pos, k_cache,
+                                 v_cache, stream, ap);
+  if (st != STARKV_OK) return st;
+  DecodeLaunch a{};
+  st = make_decode(dims, batch, max_context_len, q, b_k, b_v, k_cache, v_cache, block_tables, context_lens, scale,
+                   workspace, workspace_bytes, false, out, stream, a);
+  if (st != STARKV_OK) return st;
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return STARKV_ERR_HIP;
+  ap.cus = device_cus(device);
+  profile_events(a.ev_attn_start, a.ev_attn_stop);
+  return decode_step_enqueue(a, ap) == hipSuccess ? STARKV_OK : STARKV_ERR_HIP;
 }
 
 size_t starkv_uncompressed_decode_workspace_size(const starkv_dims* dims, int32_t batch, int32_t max_context_len) {

@@ -1,0 +1,81 @@
+"""starkv_decode_step (append + decode with the append, query projection and
+plan in one first launch) against starkv_append followed by starkv_decode:
+bit-identical outputs and pool images (the same kernel bodies run in both),
+across the append paths (VALU both sides, MFMA both sides, the large MFMA
+V side, the many-token fallback), grouped heads, r_k 16 and head_dim 64;
+plus parity with the oracle."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from helpers import DECODE_TOL, gpu, log, normwise_err, to_dev
+from rank_compressed_paged_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+CASES = [  # (heads, kv_heads, d, r_k, r_v, batch, new tokens per sequence)
+    (32, 32, 128, 64, 1024, 4, 1),      # VALU both sides, VALU q~
+    (32, 32, 128, 64, 1024, 24, 1),     # MFMA both sides (one shared launch), MFMA q~
+    (32, 32, 128, 64, 1024, 64, 1),     # large MFMA V side (two launches as a plain append)
+    (32, 32, 128, 64, 512, 20, 16),     # 320 new rows: many-token V kernel, append then decode
+    (32, 8, 128, 64, 512, 16, 2),       # grouped heads
+    (16, 16, 64, 16, 256, 40, 1),       # r_k 16: VALU K side beside the MFMA V side
+]
+
+
+@pytest.mark.parametrize("h,kv,d,rk,rv,batch,per", CASES)
+def test_step_equals_append_then_decode(h, kv, d, rk, rv, batch, per):
+    import torch
+    import rank_compressed_paged_amd as starkv
+    dev = gpu()
+    rng = np.random.default_rng(1200 + batch + per)
+    lens = rng.integers(1, 700, size=batch).astype(np.int32)
+    lens[0] = 0 if batch > 8 else lens[0]          # an empty sequence gets its first tokens
+    case = synth.make_case(1200 + h + batch, batch, h, d, rk, rv, lens, spare_tokens=per, kv_heads=kv)
+    seqs = np.repeat(np.arange(batch, dtype=np.int32), per)
+    poss = np.concatenate([np.arange(n, n + per, dtype=np.int32) for n in lens])
+    k_new, v_new = synth.make_new_rows(1200 + per, len(seqs), kv, d)
+    new_lens = (lens + per).astype(np.int32)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    scale = 1.0 / math.sqrt(d)
+    log(f"step H={h}/{kv} d={d} r_k={rk} r_v={rv} batch={batch} new={len(seqs)}")
+    a = to_dev(case, dev)
+    starkv.append(t(k_new), t(v_new), a["b_k"], a["b_v"], a["block_tables"], t(seqs), t(poss), a["k_pool"],
+                  a["v_pool"])
+    ref = starkv.decode(a["q"], a["b_k"], a["b_v"], a["k_pool"], a["v_pool"], a["block_tables"], t(new_lens), scale,
+                        max_context_len=int(new_lens.max()))
+    b = to_dev(case, dev)
+    got = starkv.decode_step(t(k_new), t(v_new), b["b_k"], b["b_v"], t(seqs), t(poss), b["q"], b["b_k"], b["b_v"],
+                             b["k_pool"], b["v_pool"], b["block_tables"], t(new_lens), scale,
+                             max_context_len=int(new_lens.max()))
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(b["k_pool"].view(torch.int16), a["k_pool"].view(torch.int16))
+    assert torch.equal(b["v_pool"].view(torch.int16), a["v_pool"].view(torch.int16))
+    kp, vp = oracle.append(k_new, v_new, case["b_k"], case["b_v"], case["block_tables"], seqs, poss,
+                           case["k_pool"], case["v_pool"])
+    want = oracle.decode(case["q"], case["b_k"], case["b_v"], kp, vp, case["block_tables"], new_lens, scale)
+    err = normwise_err(got.float().cpu().numpy(), want).max()
+    log(f"  normwise max {err:.3e}")
+    assert err <= DECODE_TOL
+
+
+def test_step_without_new_rows_is_a_decode():
+    import torch
+    import rank_compressed_paged_amd as starkv
+    dev = gpu()
+    lens = np.array([300, 47, 1000, 0], np.int32)
+    case = synth.make_case(1300, 4, 32, 128, 64, 1024, lens)
+    g = to_dev(case, dev)
+    empty_rows = torch.empty((0, 32, 128), dtype=torch.float16, device=dev)
+    empty_idx = torch.empty((0,), dtype=torch.int32, device=dev)
+    got = starkv.decode_step(empty_rows, empty_rows, g["b_k"], g["b_v"], empty_idx, empty_idx, g["q"], g["b_k"],
+                             g["b_v"], g["k_pool"], g["v_pool"], g["block_tables"], g["context_lens"], 1.0,
+                             max_context_len=1000)
+    ref = starkv.decode(g["q"], g["b_k"], g["b_v"], g["k_pool"], g["v_pool"], g["block_tables"], g["context_lens"],
+                        1.0, max_context_len=1000)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
