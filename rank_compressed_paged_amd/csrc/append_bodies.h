@@ -93,9 +93,11 @@ __device__ __forceinline__ void append_k_valu_body(int idx, const f16* __restric
   const int t = idx / (RK * H);
   const f16* x = k + ((size_t)t * H + h) * D;
   const f16* wrow = wk + ((size_t)h * RK + r) * D;
-  const float acc = dot_f16(x, wrow, D);
+  // the destination slot is looked up first: its table entry is then in
+  // flight with the operand loads instead of two round trips after them
   int phys, slot;
   where(t, phys, slot);
+  const float acc = dot_f16(x, wrow, D);
   kc[(((size_t)phys * H + h) * kBlock + slot) * RK + r] = (f16)acc;
 }
 
@@ -293,6 +295,13 @@ __device__ __forceinline__ void append_v_valu_body(int bx, int by, const f16* __
   const int j = bx * 8 + (threadIdx.x >> 6);
   const int t0 = by * kAppendGroup;
   const int cnt = min(kAppendGroup, n - t0);
+  // destination slots of the group's tokens (lane r looks up token t0 + r):
+  // sequence and position ahead of the operand loads, the table entry once
+  // the rows are staged, so the lookups overlap the contraction
+  const bool looker = lane < cnt;
+  const int lseq = looker ? where.seq[t0 + lane] : 0;
+  const int lpos = looker ? where.pos[t0 + lane] : 0;
+  int lphys = 0;
   float acc[kAppendGroup] = {};
   for (int kc = 0; kc < K; kc += kAppendChunk) {
     const int kn = min(kAppendChunk, K - kc);       // multiple of 8
@@ -319,6 +328,7 @@ __device__ __forceinline__ void append_v_valu_body(int bx, int by, const f16* __
       if (idx < cnt * (kn / 8)) *reinterpret_cast<half8*>(&vl[idx / (kn / 8)][(idx % (kn / 8)) * 8]) = vv[i];
     }
     __syncthreads();
+    if (kc == 0 && looker) lphys = where.bt[(size_t)lseq * where.mb + lpos / kBlock];
 #pragma unroll
     for (int r = 0; r < kAppendGroup; ++r) {
       if (r < cnt) {
@@ -340,11 +350,8 @@ __device__ __forceinline__ void append_v_valu_body(int bx, int by, const f16* __
     float s = acc[r];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (lane == 0 && r < cnt) {
-      int phys, slot;
-      where(t0 + r, phys, slot);
-      vc[((size_t)phys * RV + j) * kBlock + slot] = (f16)s;
-    }
+    const int phys = __shfl(lphys, r, 64), slot = __shfl(lpos, r, 64) % kBlock;
+    if (lane == 0 && r < cnt) vc[((size_t)phys * RV + j) * kBlock + slot] = (f16)s;
   }
 }
 
