@@ -307,8 +307,10 @@ starkv_status starkv_uncompressed_decode(const starkv_dims* dims, int32_t batch,
 starkv_status starkv_check_block_tables(const starkv_dims* dims, int32_t batch, const int32_t* block_tables,
                                         const int32_t* context_lens, int32_t* error_count, void* stream);
 
-/* Static, human-readable name of a status code (host-only). */
-const char* starkv_status_string(starkv_status status);
+/* Static, human-readable name of a status code (host-only).  Takes the code
+ * as an int so that any value is valid to pass; a value that is not a
+ * starkv_status gives a name that says the status is unknown. */
+const char* starkv_status_string(int status);
 
 /*
  * Measurement hooks (host-only, process-wide, not for use while another

@@ -1,9 +1,13 @@
 """Compile libstarkv.so (HIP, gfx950) in-tree with hipcc.
 
     python -m rank_compressed_paged_amd.build
+    python -m rank_compressed_paged_amd.build --host-sanitize OUT.so
 
 Each source is compiled to an object file in its own hipcc process (in
-parallel), then the objects are linked into the shared library.
+parallel), then the objects are linked into the shared library.  The second
+form builds a copy whose host code (argument checks, layouts, launch set-up)
+carries AddressSanitizer and UndefinedBehaviorSanitizer; the device code is
+built as usual.  Load it with the ASan runtime preloaded (host_asan_runtime()).
 """
 
 from __future__ import annotations
@@ -40,12 +44,31 @@ FLAGS = [
 ]
 
 
-def compile_command(src: str, obj: str) -> list:
-    return [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+# host-side sanitizers only (each -fsanitize= applies to the host pass alone)
+HOST_SANITIZE = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined".split()
+HOST_SANITIZE_COMPILE = HOST_SANITIZE + "-Xarch_host -fno-sanitize-recover=undefined -g".split()
 
 
-def link_command(objs: list, out: str) -> list:
-    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out]
+def compile_command(src: str, obj: str, extra: tuple = ()) -> list:
+    return [hipcc(), *FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+
+
+def link_command(objs: list, out: str, extra: tuple = ()) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", out]
+
+
+def host_asan_runtime() -> str:
+    """Path of the compiler's shared ASan runtime (to LD_PRELOAD into Python)."""
+    out = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                         text=True).stdout.strip()
+    if not os.path.isabs(out) or not os.path.exists(out):
+        import glob
+        rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+        cands = sorted(glob.glob(os.path.join(rocm, "llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")))
+        if not cands:
+            raise RuntimeError("no shared ASan runtime found next to hipcc")
+        out = cands[-1]
+    return out
 
 
 def _run(cmd):
@@ -54,11 +77,13 @@ def _run(cmd):
     return r.returncode, errs
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+def build(verbose: bool = False, jobs: int | None = None, out: str = LIB, host_sanitize: bool = False) -> str:
     jobs = jobs or min(len(SOURCES), max(1, os.cpu_count() or 1))
+    cflags = tuple(HOST_SANITIZE_COMPILE) if host_sanitize else ()
+    lflags = tuple(["-shared-libasan", *HOST_SANITIZE]) if host_sanitize else ()
     with tempfile.TemporaryDirectory(prefix="starkv_build_") as tmp:
         objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-        cmds = [compile_command(s, o) for s, o in zip(SOURCES, objs)]
+        cmds = [compile_command(s, o, cflags) for s, o in zip(SOURCES, objs)]
         if verbose:
             for c in cmds:
                 print(" ".join(c), flush=True)
@@ -69,16 +94,19 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
                 raise RuntimeError(f"hipcc failed on {src} ({rc}):\n{errs}")
             if verbose and errs.strip():
                 print(errs, file=sys.stderr)
-        tmp_lib = LIB + ".tmp"
-        cmd = link_command(objs, tmp_lib)
+        tmp_lib = out + ".tmp"
+        cmd = link_command(objs, tmp_lib, lflags)
         if verbose:
             print(" ".join(cmd), flush=True)
         rc, errs = _run(cmd)
         if rc != 0:
             raise RuntimeError(f"link failed ({rc}):\n{errs}")
-    os.replace(tmp_lib, LIB)
-    return LIB
+    os.replace(tmp_lib, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if len(sys.argv) == 3 and sys.argv[1] == "--host-sanitize":
+        print(build(verbose=True, out=os.path.abspath(sys.argv[2]), host_sanitize=True))
+    else:
+        print(build(verbose=True))

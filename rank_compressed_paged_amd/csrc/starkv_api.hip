@@ -232,7 +232,7 @@ starkv_status scratch_of(int device, void** ptr) {
 
 extern "C" {
 
-const char* starkv_status_string(starkv_status status) {
+const char* starkv_status_string(int status) {
   switch (status) {
     case STARKV_OK: return "STARKV_OK";
     case STARKV_ERR_INVALID_ARG: return "STARKV_ERR_INVALID_ARG: null pointer, bad size or misalignment";
