@@ -280,19 +280,26 @@ __device__ __forceinline__ void append_v_rows_body(int bid, const f16* __restric
   }
 }
 
-// V side, VALU (fewer than 16 tokens): a workgroup of eight waves owns eight
-// joint latents and up to four tokens.  The tokens' v rows are staged in LDS
-// once; each wave fetches its whole w_v row with 16-byte loads before any
-// arithmetic, then reduces one dot product per token across its lanes.
+// V side, VALU (fewer than 16 tokens): a workgroup of eight waves owns vlat
+// (4 or 8) joint latents and up to four tokens; wave w takes latent
+// vlat*bx + w % vlat over part w / vlat of each contraction pass, so at vlat
+// 4 a launch's w_v rows are spread over twice the compute units.  Per pass the tokens' v rows are
+// staged in LDS: their loads are issued before the w_v loads, so the staging
+// waits for them alone while w_v is still in flight.  Each wave sums its
+// products per token (DPP within 16-lane rows, then the four rows by
+// readlane) and the two halves meet in LDS.
 constexpr int kAppendGroup = 4;
 constexpr int kAppendChunk = 4096;                  // contraction elements per pass
 
-__device__ __forceinline__ void append_v_valu_body(int bx, int by, const f16* __restrict__ v,
+__device__ __forceinline__ void append_v_valu_body(int bx, int by, int vlat, const f16* __restrict__ v,
                                                    const f16* __restrict__ wv, int n, int K, int RV, SlotOf where,
                                                    f16* __restrict__ vc) {
   __shared__ __attribute__((aligned(16))) f16 vl[kAppendGroup][kAppendChunk];
+  __shared__ float red[4][kAppendGroup];
   const int lane = threadIdx.x & 63;
-  const int j = bx * 8 + (threadIdx.x >> 6);
+  const int w = threadIdx.x >> 6;
+  const int j = bx * vlat + w % vlat;
+  const int hf = w / vlat;                          // contraction part (0, or 0/1 at vlat 4)
   const int t0 = by * kAppendGroup;
   const int cnt = min(kAppendGroup, n - t0);
   // destination slots of the group's tokens (lane r looks up token t0 + r):
@@ -305,13 +312,9 @@ __device__ __forceinline__ void append_v_valu_body(int bx, int by, const f16* __
   float acc[kAppendGroup] = {};
   for (int kc = 0; kc < K; kc += kAppendChunk) {
     const int kn = min(kAppendChunk, K - kc);       // multiple of 8
-    half8 wr[kAppendChunk / 512];
-#pragma unroll
-    for (int i = 0; i < kAppendChunk / 512; ++i) {
-      const int k = i * 512 + lane * 8;
-      wr[i] = (j < RV && k < kn) ? *reinterpret_cast<const half8*>(wv + (size_t)j * K + kc + k) : half8{};
-    }
-    // token rows -> LDS: every load of a thread is issued before its first write
+    const int hk = vlat == 4 ? ((kn + 15) / 16) * 8 : kn;   // parts [0, hk) and [hk, kn)
+    const int k0 = hf * hk, k1 = hf ? kn : hk;
+    // token rows -> registers (issued first), then this wave's w_v half
     constexpr int kPer = kAppendGroup * kAppendChunk / 8 / 512;
     half8 vv[kPer];
 #pragma unroll
@@ -319,6 +322,12 @@ __device__ __forceinline__ void append_v_valu_body(int bx, int by, const f16* __
       const int idx = threadIdx.x + 512 * i;
       const int r = idx / (kn / 8), c = idx % (kn / 8);
       vv[i] = idx < cnt * (kn / 8) ? *reinterpret_cast<const half8*>(v + (size_t)(t0 + r) * K + kc + c * 8) : half8{};
+    }
+    half8 wr[kAppendChunk / 512];
+#pragma unroll
+    for (int i = 0; i < kAppendChunk / 512; ++i) {
+      const int k = k0 + i * 512 + lane * 8;
+      wr[i] = (j < RV && k < k1) ? *reinterpret_cast<const half8*>(wv + (size_t)j * K + kc + k) : half8{};
     }
     __builtin_amdgcn_sched_barrier(0);              // keep the loads ahead of the LDS writes
     __syncthreads();                                // previous pass's readers are done
@@ -334,8 +343,8 @@ __device__ __forceinline__ void append_v_valu_body(int bx, int by, const f16* __
       if (r < cnt) {
 #pragma unroll
         for (int i = 0; i < kAppendChunk / 512; ++i) {
-          const int k = i * 512 + lane * 8;
-          if (k < kn) {
+          const int k = k0 + i * 512 + lane * 8;
+          if (k < k1) {
             const half8 x = *reinterpret_cast<const half8*>(&vl[r][k]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[r] += (float)x[e] * (float)wr[i][e];
@@ -344,12 +353,25 @@ __device__ __forceinline__ void append_v_valu_body(int bx, int by, const f16* __
       }
     }
   }
-  if (j >= RV) return;                              // no barrier follows
+  float sum[kAppendGroup];
 #pragma unroll
   for (int r = 0; r < kAppendGroup; ++r) {
-    float s = acc[r];
+    // DPP sums within each 16-lane row, then the four row sums by readlane
+    const int g = __builtin_bit_cast(int, group_sum<16>(acc[r]));
+    sum[r] = (__builtin_bit_cast(float, __builtin_amdgcn_readlane(g, 0)) +
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(g, 16))) +
+             (__builtin_bit_cast(float, __builtin_amdgcn_readlane(g, 32)) +
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(g, 48)));
+  }
+  if (hf == 1 && lane == 0) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    for (int r = 0; r < kAppendGroup; ++r) red[w & 3][r] = sum[r];
+  }
+  __syncthreads();
+  if (hf == 1 || j >= RV) return;                   // no barrier follows
+#pragma unroll
+  for (int r = 0; r < kAppendGroup; ++r) {
+    const float s = vlat == 4 ? sum[r] + red[w & 3][r] : sum[r];
     const int phys = __shfl(lphys, r, 64), slot = __shfl(lpos, r, 64) % kBlock;
     if (lane == 0 && r < cnt) vc[((size_t)phys * RV + j) * kBlock + slot] = (f16)s;
   }
@@ -357,54 +379,76 @@ __device__ __forceinline__ void append_v_valu_body(int bx, int by, const f16* __
 
 // Workgroups and roles of an append.  Both sides can share one launch of
 // 512-thread workgroups: the first nv run the V side, the next kwg the K side
-// (VALU: 512 outputs each; MFMA: eight 32 x 32 tiles, one per wave).
+// (VALU: 512 outputs each; MFMA: ktpw 32 x 32 tiles, one per wave).
 struct AppendRoles {
   bool vrows;            // many tokens: V side on append_v_rows (its own launch)
   bool vmfma, kmfma;     // MFMA (else VALU) bodies
   long long nv;          // V-side workgroups
-  int vgx;               // VALU V side: workgroups per token group (r_v / 8)
+  int vlat;              // VALU V side: latents per workgroup (4: contraction in two parts, or 8)
+  int vgx;               // VALU V side: workgroups per token group (r_v / vlat)
   long long kwg;         // K-side workgroups in a shared launch
   long long ktiles;      // MFMA K tiles
+  int ktpw;              // MFMA K tiles per shared-launch workgroup (one per wave, 1 to 8)
   long long kgrid;       // K side in its own launch: workgroups of 64 (MFMA) or 256 (VALU) threads
   long long vgrid;       // V side in its own launch
 };
 
-inline AppendRoles append_roles(const Shape& s, int n) {
+// slots: compute units this launch's append workgroups may fill (0: unknown).
+// While they fit, the VALU V side splits its contraction over two waves per
+// latent and MFMA K tiles spread one per workgroup (both: fewer bytes in
+// flight per compute unit); otherwise eight latents or tiles per workgroup.
+inline AppendRoles append_roles(const Shape& s, int n, long long slots = 0) {
   AppendRoles r{};
   const int K = s.KV * s.D;
-  r.kmfma = n >= 16 && s.RK % 32 == 0 && s.D % 16 == 0;
+  r.kmfma = s.RK % 32 == 0 && s.D % 16 == 0;      // also for small n: rows read along d
   r.vrows = n >= 256 && s.RV % kAppendRowsLat == 0 && K % kAppendRowsSpan == 0;
   r.vmfma = !r.vrows && n >= 16 && s.RV % 16 == 0 && K % (32 * kAppendVWaves) == 0;
   const long long nn = n;
   r.ktiles = ((nn + 31) / 32) * s.KV * (s.RK / 32);
+  const long long kvalu = (nn * s.KV * s.RK + 511) / 512;
+  const long long kwg8 = r.kmfma ? (r.ktiles + 7) / 8 : kvalu;
   if (r.vmfma) {
     r.nv = ((s.RV / 16 + 7) / 8) * 8LL * ((nn + 15) / 16);
   } else {
-    r.vgx = (s.RV + 7) / 8;
-    r.nv = (long long)r.vgx * ((nn + kAppendGroup - 1) / kAppendGroup);
+    const long long groups = (nn + kAppendGroup - 1) / kAppendGroup;
+    r.vlat = (slots > 0 && ((s.RV + 3) / 4) * groups + kwg8 <= slots) ? 4 : 8;
+    r.vgx = (s.RV + r.vlat - 1) / r.vlat;
+    r.nv = (long long)r.vgx * groups;
   }
-  r.kwg = r.kmfma ? (r.ktiles + kAppendVWaves - 1) / kAppendVWaves : (nn * s.KV * s.RK + 511) / 512;
+  r.ktpw = 8;
+  if (r.kmfma && slots > 0)
+    for (int t = 1; t < 8; t *= 2)
+      if (r.nv + (r.ktiles + t - 1) / t <= slots) {
+        r.ktpw = t;
+        break;
+      }
+  r.kwg = r.kmfma ? (r.ktiles + r.ktpw - 1) / r.ktpw : kvalu;
   r.kgrid = r.kmfma ? r.ktiles : (nn * s.KV * s.RK + 255) / 256;
   r.vgrid = r.vrows ? (nn + kAppendRowsTok - 1) / kAppendRowsTok * ((s.RV / kAppendRowsLat + 7) / 8) * 8 : r.nv;
   return r;
 }
 
-// One role of a shared append launch (512 threads, workgroup bid).
+// One role of a shared append launch (512 threads, workgroup bid).  The
+// body choices are template arguments (VM: V side on MFMA, else VALU; KM: K
+// side on MFMA, else VALU) so that a launch carries only the registers of the
+// bodies it runs.
+template <bool VM, bool KM>
 __device__ __forceinline__ void append_role(int bid, const AppendRoles& r, const f16* __restrict__ k,
                                             const f16* __restrict__ v, const f16* __restrict__ wk,
                                             const f16* __restrict__ wv, int n, int KV, int D, int RK, int RV,
                                             SlotOf where, f16* __restrict__ kc, f16* __restrict__ vc) {
   if (bid < r.nv) {                          // whole workgroup: the V side's barriers see every wave
-    if (r.vmfma)
+    if constexpr (VM)
       append_v_mfma_body(bid, v, wv, n, KV * D, RV, where, vc);
     else
-      append_v_valu_body(bid % r.vgx, bid / r.vgx, v, wv, n, KV * D, RV, where, vc);
+      append_v_valu_body(bid % r.vgx, bid / r.vgx, r.vlat, v, wv, n, KV * D, RV, where, vc);
     return;
   }
   const int kb = bid - (int)r.nv;
-  if (r.kmfma) {
-    const int tile = kb * kAppendVWaves + ((int)threadIdx.x >> 6);
-    if (tile < r.ktiles) append_k_mfma_body(tile, threadIdx.x & 63, k, wk, n, KV, D, RK, where, kc);
+  if constexpr (KM) {
+    const int wave = (int)threadIdx.x >> 6;
+    const long long tile = (long long)kb * r.ktpw + wave;
+    if (wave < r.ktpw && tile < r.ktiles) append_k_mfma_body((int)tile, threadIdx.x & 63, k, wk, n, KV, D, RK, where, kc);
   } else {
     append_k_valu_body(kb * 512 + (int)threadIdx.x, k, wk, n, KV, D, RK, where, kc);
   }

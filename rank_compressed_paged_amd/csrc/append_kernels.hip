@@ -32,9 +32,9 @@ append_v_rows_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
 }
 
 __global__ void __launch_bounds__(512)
-append_v_valu_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV,
+append_v_valu_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int n, int K, int RV, int vlat,
                      SlotOf where, f16* __restrict__ vc) {
-  append_v_valu_body(blockIdx.x, blockIdx.y, v, wv, n, K, RV, where, vc);
+  append_v_valu_body(blockIdx.x, blockIdx.y, vlat, v, wv, n, K, RV, where, vc);
 }
 
 // Both sides in one launch of 512-thread workgroups (roles in append_role):
@@ -44,11 +44,12 @@ append_v_valu_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
 // heads, r_v 1024 on 256 units).  Past that, a V-side workgroup (164 VGPRs per
 // lane) leaves too few registers on its unit for a second one, so K-side
 // workgroups would wait for the V side: those appends use two launches.
+template <bool VM, bool KM>
 __global__ void __launch_bounds__(512)
 append_kv_kernel(const f16* __restrict__ k, const f16* __restrict__ v, const f16* __restrict__ wk,
                  const f16* __restrict__ wv, int n, int KV, int D, int RK, int RV, SlotOf where,
                  f16* __restrict__ kc, f16* __restrict__ vc, AppendRoles roles) {
-  append_role(blockIdx.x, roles, k, v, wk, wv, n, KV, D, RK, RV, where, kc, vc);
+  append_role<VM, KM>(blockIdx.x, roles, k, v, wk, wv, n, KV, D, RK, RV, where, kc, vc);
 }
 
 hipError_t append_enqueue(const AppendLaunch& a) {
@@ -62,16 +63,19 @@ hipError_t append_enqueue(const AppendLaunch& a) {
   f16* vc = static_cast<f16*>(a.v_cache);
   // new rows, w_k and the K pool are per key/value head
   const int K = s.KV * s.D;
-  const AppendRoles r = append_roles(s, a.n);
+  const AppendRoles r = append_roles(s, a.n, a.cus);
   // grid sizes in 64-bit: no launch below exceeds 2^31 threads, so thread
   // and tile indices inside the kernels stay in int
   const long long grid_kv = r.nv + r.kwg;
   if (!r.vrows && grid_kv * 512 > (1LL << 31)) return hipErrorInvalidValue;
+  // one launch when every workgroup of both sides gets a compute unit at once
+  // (or both sides are VALU): MFMA-sized V workgroups fill their compute units
   const bool both_valu = !r.kmfma && !r.vrows && !r.vmfma;
-  const bool both_mfma = r.kmfma && r.vmfma && grid_kv <= a.cus;
-  if (both_valu || both_mfma) {
-    hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)grid_kv), dim3(512), 0, a.stream, k, v, wk, wv, a.n, s.KV,
-                       s.D, s.RK, s.RV, where, kc, vc, r);
+  if (both_valu || (!r.vrows && grid_kv <= a.cus)) {
+    const auto kern = r.vmfma ? (r.kmfma ? append_kv_kernel<true, true> : append_kv_kernel<true, false>)
+                              : (r.kmfma ? append_kv_kernel<false, true> : append_kv_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid_kv), dim3(512), 0, a.stream, k, v, wk, wv, a.n, s.KV, s.D, s.RK,
+                       s.RV, where, kc, vc, r);
     return hipGetLastError();
   }
   if (r.kgrid * (r.kmfma ? 64 : 256) > (1LL << 31) || ((r.vrows || r.vmfma) && r.vgrid * 512 > (1LL << 31)))
@@ -92,7 +96,7 @@ hipError_t append_enqueue(const AppendLaunch& a) {
                        a.n, K, s.RV, where, vc);
   else
     hipLaunchKernelGGL(append_v_valu_kernel, dim3(r.vgx, (unsigned)((a.n + kAppendGroup - 1) / kAppendGroup)),
-                       dim3(512), 0, a.stream, v, wv, a.n, K, s.RV, where, vc);
+                       dim3(512), 0, a.stream, v, wv, a.n, K, s.RV, r.vlat, where, vc);
   return hipGetLastError();
 }
 

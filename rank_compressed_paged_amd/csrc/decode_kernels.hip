@@ -31,19 +31,29 @@ namespace starkv {
 // 1. query projection + plan
 // ---------------------------------------------------------------------------
 
-// Inclusive scan over the NT threads of a workgroup.
+// Inclusive scan over the NT threads of a workgroup: shuffles within each
+// wave, then one exchange of the wave totals through LDS (sh: NT / 64 ints).
+// *total gets the sum over all NT threads.
 template <int NT>
-__device__ int block_inclusive_scan(int v, int* sh) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    int t = (tid >= off) ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += t;
-    __syncthreads();
+__device__ int block_inclusive_scan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
   }
-  return sh[tid];
+  if (lane == 63) sh[w] = v;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const int x = sh[i];
+    before += i < w ? x : 0;
+    all += x;
+  }
+  __syncthreads();                                   // sh is free again
+  *total = all;
+  return v + before;
 }
 
 // Equal split of the batch's blocks over `grid` workgroups.  prefix[b] is the
@@ -54,8 +64,11 @@ __device__ int block_inclusive_scan(int v, int* sh) {
 template <int NT>
 __device__ void build_plan(const int32_t* __restrict__ lens, int batch, int grid,
                            int32_t* __restrict__ plan) {
-  __shared__ int sh[NT];
+  static_assert(NT % 64 == 0, "whole waves");
+  __shared__ int sh[NT / 64];
+  __shared__ int pf[NT + 1];                          // prefix, when batch <= NT
   const int tid = threadIdx.x;
+  const bool one_pass = batch <= NT;
   int32_t* prefix = plan + 2;
   int32_t* sbase = plan + 3 + batch;
   int32_t* first = plan + 4 + 2 * batch;
@@ -63,11 +76,11 @@ __device__ void build_plan(const int32_t* __restrict__ lens, int batch, int grid
   for (int base = 0; base < batch; base += NT) {
     const int i = base + tid;
     const int v = (i < batch) ? (lens[i] + kBlock - 1) / kBlock : 0;
-    const int x = block_inclusive_scan<NT>(v, sh);
-    const int chunk = sh[NT - 1];
+    int chunk;
+    const int x = block_inclusive_scan<NT>(v, sh, &chunk);
     if (i < batch) prefix[i + 1] = carry + x;
+    if (one_pass) pf[tid + 1] = x;
     carry += chunk;
-    __syncthreads();
   }
   const int total = carry;
   const int W = max(1, (total + grid - 1) / grid);
@@ -75,21 +88,32 @@ __device__ void build_plan(const int32_t* __restrict__ lens, int batch, int grid
   for (int base = 0; base < batch; base += NT) {
     const int i = base + tid;
     const int v = (i < batch) ? (lens[i] + kBlock - 1) / kBlock : 0;
-    const int x = block_inclusive_scan<NT>(v, sh);
-    const int chunk1 = sh[NT - 1];
-    __syncthreads();
+    int chunk1, chunk2;
+    const int x = block_inclusive_scan<NT>(v, sh, &chunk1);
     const int incl = carry1 + x;
     const int excl = incl - v;
     const int np = (v > 0) ? ((incl - 1) / W - excl / W + 1) : 0;
-    const int y = block_inclusive_scan<NT>(np, sh);
-    const int chunk2 = sh[NT - 1];
+    const int y = block_inclusive_scan<NT>(np, sh, &chunk2);
     if (i < batch) sbase[i + 1] = carry2 + y;
     // ranges starting inside this sequence: g*W in [excl, incl), g < grid
-    if (i < batch && v > 0)
+    if (!one_pass && i < batch && v > 0)
       for (int g = (excl + W - 1) / W; g * W < incl; ++g) first[g] = i;
     carry1 += chunk1;
     carry2 += chunk2;
+  }
+  if (one_pass) {
+    // one range per thread: the last sequence whose first block is at or
+    // before the range's first block (it is non-empty and holds that block)
+    if (tid == 0) pf[0] = 0;
     __syncthreads();
+    for (int g = tid; g < grid && g * W < total; g += NT) {
+      int lo = 0, hi = batch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pf[mid] <= g * W) lo = mid; else hi = mid - 1;
+      }
+      first[g] = lo;
+    }
   }
   if (tid == 0) {
     plan[0] = W;
@@ -180,27 +204,32 @@ qproj_plan_valu_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, fl
 
 // Prologue of a decode step (starkv_decode_step): one launch of 512-thread
 // workgroups runs the step's append (the first nA workgroups: V and K roles as
-// in a shared append launch), the q~ projection (the next nQ: two 256-thread
-// MFMA units, or 512 VALU outputs, each) and, in the last workgroup, the
-// plan.  The three are independent: the append writes the new tokens' slots,
-// which only the attention launch after this one reads.
+// in a shared append launch), the q~ projection (the next nQ: one 256-thread
+// MFMA unit each, the other half of the workgroup idle so that B_k's rows are
+// fetched by twice the compute units; or 512 VALU outputs each) and, in the
+// last workgroup, the plan.  The three are independent: the append writes the
+// new tokens' slots, which only the attention launch after this one reads.
+// VM: V side on MFMA; MF: K side and q~ on MFMA (template arguments, so that
+// a launch holds only the registers of the bodies it runs).
+template <bool VM, bool MF>
 __global__ void __launch_bounds__(512)
 step_prologue_kernel(const f16* __restrict__ k, const f16* __restrict__ v, const f16* __restrict__ wk,
                      const f16* __restrict__ wv, int n, SlotOf where, f16* __restrict__ kc, f16* __restrict__ vc,
                      AppendRoles roles, int nA, const f16* __restrict__ q, const f16* __restrict__ bk,
                      float* __restrict__ qt, int batch, int H, int KV, int D, int RK, int RV, float scale2,
-                     bool qmfma, int nQ, const int32_t* __restrict__ lens, int grid, int32_t* __restrict__ plan) {
+                     int nQ, const int32_t* __restrict__ lens, int grid, int32_t* __restrict__ plan) {
   const int bid = blockIdx.x;
   if (bid < nA) {
-    append_role(bid, roles, k, v, wk, wv, n, KV, D, RK, RV, where, kc, vc);
+    append_role<VM, MF>(bid, roles, k, v, wk, wv, n, KV, D, RK, RV, where, kc, vc);
     return;
   }
   if (bid < nA + nQ) {
     const int qb = bid - nA;
-    if (qmfma)
-      qproj_mfma_body(2 * qb + ((int)threadIdx.x >> 8), threadIdx.x & 255, q, bk, qt, batch, H, KV, D, RK, scale2);
-    else
+    if constexpr (MF) {
+      if (threadIdx.x < 256) qproj_mfma_body(qb, threadIdx.x, q, bk, qt, batch, H, KV, D, RK, scale2);
+    } else {
       qproj_valu_body((long long)qb * 512 + threadIdx.x, q, bk, qt, batch, H, KV, D, RK, scale2);
+    }
     return;
   }
   build_plan<512>(lens, batch, grid, plan);
@@ -766,7 +795,7 @@ DecodeLayout decode_layout(const Shape& s, int batch, int max_context_len, int g
 hipError_t launch_qproj(const Shape& s, int rows, const void* q, const void* b_k, float scale2, float* qt,
                         const int32_t* plan_lens, int plan_grid, int32_t* plan, hipStream_t st) {
   const int extra = plan_lens ? 1 : 0;      // last workgroup builds the decode plan
-  if (rows >= kSmallBatch && s.RK % 32 == 0 && s.D % 16 == 0) {
+  if (s.RK % 32 == 0 && s.D % 16 == 0) {
     const int groups = (s.H * (s.RK / 32) + 3) / 4;
     const int nq = ((rows + 31) / 32) * groups;
     hipLaunchKernelGGL(qproj_plan_mfma_kernel, dim3(nq + extra), dim3(256), 0, st, static_cast<const f16*>(q),
@@ -909,7 +938,11 @@ hipError_t decode_enqueue(const DecodeLaunch& a) {
 hipError_t decode_step_enqueue(const DecodeLaunch& a, const AppendLaunch& ap) {
   const Shape& s = a.s;
   if (ap.n == 0) return decode_enqueue(a);
-  const AppendRoles r = append_roles(s, ap.n);
+  const bool qmfma = s.RK % 32 == 0 && s.D % 16 == 0;
+  const long long units = ((a.batch + 31LL) / 32) * ((s.H * (s.RK / 32) + 3) / 4);
+  const long long nQ = qmfma ? units : ((long long)a.batch * s.H * s.RK + 511) / 512;
+  // the append's workgroups spread while all of the launch fits the compute units
+  const AppendRoles r = append_roles(s, ap.n, ap.cus > 0 ? std::max(0LL, ap.cus - nQ - 1) : 0);
   const long long nA = r.nv + r.kwg;
   // the many-token V side has its own kernel: append, then decode
   if (r.vrows || nA * 512 > (1LL << 30)) {
@@ -919,17 +952,18 @@ hipError_t decode_step_enqueue(const DecodeLaunch& a, const AppendLaunch& ap) {
   }
   int32_t* plan = reinterpret_cast<int32_t*>(a.ws + a.lay.off_plan);
   float* qt = reinterpret_cast<float*>(a.ws + a.lay.off_qt);
-  const bool qmfma = a.batch >= kSmallBatch && s.RK % 32 == 0 && s.D % 16 == 0;
-  const long long units = ((a.batch + 31LL) / 32) * ((s.H * (s.RK / 32) + 3) / 4);
-  const long long nQ = qmfma ? (units + 1) / 2 : ((long long)a.batch * s.H * s.RK + 511) / 512;
+  if (qmfma != r.kmfma) return hipErrorInvalidConfiguration;   // one flag for both projections
   const long long grid = nA + nQ + 1;
   if (grid * 512 > (1LL << 31)) return hipErrorInvalidConfiguration;
   const SlotOf where{ap.block_tables, ap.token_seq, ap.token_pos, s.MB};
-  hipLaunchKernelGGL(step_prologue_kernel, dim3((unsigned)grid), dim3(512), 0, a.stream,
+  // MF: the K side and q~ on MFMA (both need r_k % 32 == 0 and d % 16 == 0)
+  const auto kern = r.vmfma ? (qmfma ? step_prologue_kernel<true, true> : step_prologue_kernel<true, false>)
+                            : (qmfma ? step_prologue_kernel<false, true> : step_prologue_kernel<false, false>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, a.stream,
                      static_cast<const f16*>(ap.k), static_cast<const f16*>(ap.v), static_cast<const f16*>(ap.w_k),
                      static_cast<const f16*>(ap.w_v), ap.n, where, static_cast<f16*>(ap.k_cache),
                      static_cast<f16*>(ap.v_cache), r, (int)nA, static_cast<const f16*>(a.q),
-                     static_cast<const f16*>(a.b_k), qt, a.batch, s.H, s.KV, s.D, s.RK, s.RV, a.scale * kLog2e, qmfma,
+                     static_cast<const f16*>(a.b_k), qt, a.batch, s.H, s.KV, s.D, s.RK, s.RV, a.scale * kLog2e,
                      (int)nQ, a.context_lens, a.grid, plan);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
