@@ -632,20 +632,23 @@ upproj_valu_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
 // ---------------------------------------------------------------------------
 // host side
 // Few (sequence, head) pairs with d = 128 (long sequences at small batch): the
-// merge and the up-projection of one (sequence, head) in one 512-thread
-// workgroup, so Z never goes to memory and one launch with its memory round
-// trips is saved.
-//   1. The head's B_v column block is fetched first (thread t: output dims
-//      8*(t%16) .. +7, latent rows (t/16)*r_v/32 .. +r_v/32-1), so it is in
-//      flight during the merge.
-//   2. Merge as in merge_kernel<4>: four slot groups take every fourth slot,
-//      eight slots per round trip, base-2 log-sum-exp online; the groups
-//      combine through LDS into the normalised z (LDS).
-//   3. out[b, h, :] = z . B_v block: per-thread partial sums over its latent
-//      rows, reduced over the 32 row groups through LDS.
+// merge and the up-projection of one (sequence, head) in two 512-thread
+// workgroups, one per half of the 128 output dims, so Z never goes to memory
+// and a pair's bytes are spread over two compute units.  Both halves merge all
+// of the pair's partial states; their ids (half * pairs + pair) put them on
+// one XCD when pairs % 8 == 0, so the second read of a slot can come from L2.
+//   1. Merge as in merge_kernel<4>: four slot groups take every fourth slot,
+//      kMuSlots slots per round trip, base-2 log-sum-exp online.  The half's
+//      B_v columns (thread t: output dims 64*half + 8*(t%8) .. +7, latent rows
+//      (t/8)*r_v/64 .. +r_v/64-1) are fetched right behind the first round's
+//      loads: in flight during the merge without delaying its first round.
+//   2. The groups combine through LDS into the normalised z (LDS).
+//   3. out[b, h, half] = z . B_v columns: per-thread sums over its latent
+//      rows, reduced over the 64 row groups through LDS in two steps.
 constexpr int kMuGroups = 4;
 constexpr int kMuSlots = 8;
 constexpr int kMuD = 128;
+constexpr int kMuCols = 64;              // output dims per workgroup
 
 __global__ void __launch_bounds__(512)
 merge_upproj_small_kernel(const float* __restrict__ part_z, const float* __restrict__ part_ml,
@@ -654,45 +657,56 @@ merge_upproj_small_kernel(const float* __restrict__ part_z, const float* __restr
   __shared__ __attribute__((aligned(16))) float zl[kUpvMaxRV];
   __shared__ __attribute__((aligned(16))) float ca[kMuGroups][kUpvMaxRV];
   __shared__ float cm_s[kMuGroups], cl_s[kMuGroups];
-  __shared__ float red[32][kMuD + 1];
+  __shared__ float red[64][kMuCols + 1];
+  __shared__ float red2[8][kMuCols];
   const int t = threadIdx.x;
-  const int h = blockIdx.x % H, b = blockIdx.x / H;
+  const int pairs = batch * H;
+  const int half_ = blockIdx.x / pairs, bh = blockIdx.x % pairs;
+  const int h = bh % H, b = bh / H;
   const int kvh = h / (H / KV);
   const size_t ld = (size_t)KV * kMuD;
 
-  // 1. B_v rows of this thread (clamped re-reads past r_v/32 rows are unused)
-  const int n8 = (t % 16) * 8, kq = t / 16;
-  const int kpt = RV / 32;                           // r_v is a multiple of 32, at most 1024
-  half8 br[kUpvMaxRV / 32];
-#pragma unroll
-  for (int i = 0; i < kUpvMaxRV / 32; ++i)
-    br[i] = *reinterpret_cast<const half8*>(bv + (size_t)(kq * kpt + min(i, kpt - 1)) * ld + (size_t)kvh * kMuD + n8);
+  // B_v columns and rows of this thread (clamped re-reads past r_v/64 rows are unused)
+  const int n8 = (t % 8) * 8, kq = t / 8;
+  const int kpt = RV / 64;                           // r_v is a multiple of 64, at most 1024
+  const f16* bcol = bv + (size_t)kvh * kMuD + half_ * kMuCols + n8;
+  half8 br[kUpvMaxRV / 64];
 
-  // 2. merge: lane li of slot group g holds latent dims 8*li .. +7
+  // 1. merge: lane li of slot group g holds latent dims 8*li .. +7
   const int g = t / 128, li = t % 128;
   const int d0 = li * 8;
   const PlanView pv{plan, batch};
   const int s0 = pv.slot_base()[b];
   const int s1 = pv.slot_base()[b + 1];
   const bool empty = lens[b] == 0 || s1 <= s0;       // uniform over the workgroup
+  const float* ml = part_ml + (size_t)h * 2;
+  const float* zb = part_z + (size_t)h * RV + (d0 < RV ? d0 : 0);
+  const size_t zs = (size_t)H * RV;                  // slot stride
   floatx4 a0 = {}, a1 = {};
   float M = -INFINITY, den = 0.f;
-  if (!empty) {
-    const float* ml = part_ml + (size_t)h * 2;
-    const float* zb = part_z + (size_t)h * RV + (d0 < RV ? d0 : 0);
-    const size_t zs = (size_t)H * RV;                // slot stride
-    for (int c = s0 + g; c < s1; c += kMuSlots * kMuGroups) {
-      float m[kMuSlots], l[kMuSlots];
-      floatx4 z0[kMuSlots], z1[kMuSlots];
+  float m[kMuSlots], l[kMuSlots];
+  floatx4 z0[kMuSlots], z1[kMuSlots];
+  // every load of a round is unconditional (indices past the end re-read the
+  // last slot and get weight 0), so all of them are in flight at once
+  auto load_round = [&](int c) {
 #pragma unroll
-      for (int u = 0; u < kMuSlots; ++u) {
-        const int sl = min(c + u * kMuGroups, s1 - 1);
-        m[u] = ml[(size_t)sl * H * 2];
-        l[u] = ml[(size_t)sl * H * 2 + 1];
-        z0[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs);
-        z1[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs + 4);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int u = 0; u < kMuSlots; ++u) {
+      const int sl = min(c + u * kMuGroups, s1 - 1);
+      m[u] = ml[(size_t)sl * H * 2];
+      l[u] = ml[(size_t)sl * H * 2 + 1];
+      z0[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs);
+      z1[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs + 4);
+    }
+  };
+  int c = s0 + g;
+  const bool any = !empty && c < s1;                 // uniform over the slot group
+  if (any) load_round(c);
+#pragma unroll
+  for (int i = 0; i < kUpvMaxRV / 64; ++i)
+    br[i] = *reinterpret_cast<const half8*>(bcol + (size_t)(kq * kpt + min(i, kpt - 1)) * ld);
+  __builtin_amdgcn_sched_barrier(0);
+  if (any) {
+    for (;;) {
       float cm = M;
 #pragma unroll
       for (int u = 0; u < kMuSlots; ++u) {
@@ -711,6 +725,10 @@ merge_upproj_small_kernel(const float* __restrict__ part_z, const float* __restr
         den += wgt * l[u];
       }
       M = cm;
+      c += kMuSlots * kMuGroups;
+      if (c >= s1) break;
+      load_round(c);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   *reinterpret_cast<floatx4*>(&ca[g][d0]) = a0;
@@ -720,6 +738,7 @@ merge_upproj_small_kernel(const float* __restrict__ part_z, const float* __restr
     cl_s[g] = den;
   }
   __syncthreads();
+  // 2. the four groups' states -> normalised z
   if (g == 0) {
     float top = -INFINITY;
 #pragma unroll
@@ -741,10 +760,10 @@ merge_upproj_small_kernel(const float* __restrict__ part_z, const float* __restr
   }
   __syncthreads();
 
-  // 3. up-projection
+  // 3. up-projection of this half
   float acc[8] = {};
 #pragma unroll
-  for (int i = 0; i < kUpvMaxRV / 32; ++i) {
+  for (int i = 0; i < kUpvMaxRV / 64; ++i) {
     if (i < kpt) {
       const float z = zl[kq * kpt + i];
 #pragma unroll
@@ -754,11 +773,19 @@ merge_upproj_small_kernel(const float* __restrict__ part_z, const float* __restr
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[kq][n8 + e] = acc[e];
   __syncthreads();
-  if (t < kMuD) {
+  {
+    const int col = t % kMuCols, part = t / kMuCols;   // eight parts of eight row groups
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v += red[part * 8 + q][col];
+    red2[part][col] = v;
+  }
+  __syncthreads();
+  if (t < kMuCols) {
     float sum = 0.f;
 #pragma unroll
-    for (int q = 0; q < 32; ++q) sum += red[q][t];
-    out[((size_t)b * H + h) * kMuD + t] = (f16)sum;
+    for (int q = 0; q < 8; ++q) sum += red2[q][t];
+    out[((size_t)b * H + h) * kMuD + half_ * kMuCols + t] = (f16)sum;
   }
 }
 
@@ -914,8 +941,8 @@ static hipError_t decode_after_prologue(const DecodeLaunch& a) {
   if (err != hipSuccess) return err;
 
   // 3. merge, 4. up-projection (one launch for few (sequence, head) pairs at d = 128)
-  if ((long long)a.batch * s.H < 512 && s.D == kMuD && s.RV <= kUpvMaxRV) {
-    hipLaunchKernelGGL(merge_upproj_small_kernel, dim3(a.batch * s.H), dim3(512), 0, a.stream, pz, pml, plan,
+  if ((long long)a.batch * s.H < 512 && s.D == kMuD && s.RV <= kUpvMaxRV && s.RV % 64 == 0) {
+    hipLaunchKernelGGL(merge_upproj_small_kernel, dim3(2 * a.batch * s.H), dim3(512), 0, a.stream, pz, pml, plan,
                        a.context_lens, static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H,
                        s.KV, s.RV);
     return hipGetLastError();
