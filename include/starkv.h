@@ -195,9 +195,9 @@ starkv_status starkv_decode_step(const starkv_dims* dims, int32_t batch, int32_t
  *
  *   A call whose workspace (carved for its actual launch grid) would exceed
  *   the scratch returns STARKV_ERR_WORKSPACE and enqueues nothing.  At 32
- *   heads and r_v = 1024 that is about (256 + 2*batch) * 128 KiB on a
- *   256-CU GPU, so batches up to about 120 fit; use starkv_decode with a
- *   caller workspace beyond that.
+ *   heads and r_v = 1024 that is about 64 KiB * (256 + batch) + 136 KiB *
+ *   batch on a 256-CU GPU, so batches up to about 240 fit; use starkv_decode
+ *   with a caller workspace beyond that.
  *   Nothing in the scratch needs to start at zero; every call overwrites what
  *   it reads.  All calls on one GPU share that GPU's scratch: two calls whose
  *   kernels may overlap (different streams, or threads without ordering)

@@ -85,7 +85,7 @@ int attn_resident_grid(int H, int KV, int RK, int RV, int device) {
   return per_cu * cus;
 }
 
-hipError_t launch_attn_kernel(const DecodeLaunch& a, const float* qt, int32_t* plan, float* pz, float* pml) {
+hipError_t launch_attn_kernel(const DecodeLaunch& a, const float* qt, int32_t* plan, f16* pz, float* pml) {
   const Shape& s = a.s;
   AttnEntry e{};
   if (!entry_of(s.H, s.KV, s.RK, s.RV, e)) return hipErrorInvalidValue;

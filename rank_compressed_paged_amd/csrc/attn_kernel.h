@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(NW * 64)
 attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f16* __restrict__ vpool,
             const int32_t* __restrict__ block_tables, int mb_stride,
             const int32_t* __restrict__ context_lens, const int32_t* __restrict__ plan, int batch,
-            int h_arg, int kv_arg, float* __restrict__ part_z, float* __restrict__ part_ml, float tau) {
+            int h_arg, int kv_arg, f16* __restrict__ part_z, float* __restrict__ part_ml, float tau) {
   using C = AttnCfg<HP, RK, RV, NW, UPW>;
   // HX, KVX > 0: an instance built for exactly these head counts (constants
   // in the code); 0: taken from the arguments
@@ -261,19 +261,40 @@ attn_kernel(const float* __restrict__ qt, const f16* __restrict__ kpool, const f
     }
   __syncthreads();
 
-  // register r of lane l holds row (r&3) + 8(r>>2) + 4(l>>5): the r part goes
-  // into a uniform base, the lane part into one 32-bit offset
+  // Partial state of a (range, sequence): m and l in fp32, z / l (the range's
+  // normalised output in latent space) in fp16.  Register r of lane l holds
+  // row (r&3) + 8(r>>2) + 4(l>>5): the r part goes into a uniform base, the
+  // lane part into one 32-bit offset.  Registers r and r+1 are rows one apart
+  // and neighbour lanes hold neighbour dims, so one DPP swap of the two lanes
+  // pairs them up: the even lane stores dims (d, d+1) of row r, the odd lane
+  // dims (d-1, d) of row r+1, each as one 4-byte store.
   auto store_partial = [&](int pslot, auto value, float m, float l) {
-    float* zp = part_z + (size_t)pslot * H * RV;
-    const int lane_off = 4 * half_ * RV + w * C::TPW * 32 + (lane & 31);
+    f16* zp = part_z + (size_t)pslot * H * RV;
+    const bool odd = lane & 1;
+    const int lane_off = 4 * half_ * RV + w * C::TPW * 32 + (lane & 31) - (odd ? 1 : 0);
+    // 1 / l of every row, read from the lane that owns it (lane h holds head h)
+    const int inv = __builtin_bit_cast(int, l > 0.f ? 1.f / l : 0.f);
+    float inv_row[32];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int hh = 0; hh < 32; ++hh) inv_row[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(inv, hh));
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
       const int rrow = (r & 3) + 8 * (r >> 2);
       if (rrow >= HP) continue;                        // compile-time
-      float* zr = zp + (size_t)rrow * RV;
+      const float i0 = half_ ? inv_row[rrow + 4] : inv_row[rrow];
+      const float i1 = half_ ? inv_row[rrow + 5] : inv_row[rrow + 1];
+      f16* zr = zp + (size_t)(rrow + (odd ? 1 : 0)) * RV;
+      const bool live_row = rrow + (odd ? 1 : 0) + 4 * half_ < H;
 #pragma unroll
-      for (int t = 0; t < C::TPW; ++t)
-        if (rrow + 4 * half_ < H) zr[lane_off + t * 32] = value(t, r);
+      for (int t = 0; t < C::TPW; ++t) {
+        const float v0 = value(t, r) * i0, v1 = value(t, r + 1) * i1;
+        const float x = odd ? v0 : v1;                  // what the neighbour lane needs
+        const float y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1,
+                                                                              0xF, 0xF, false));  // quad_perm [1,0,3,2]
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const h2 pr = odd ? h2{(f16)y, (f16)v1} : h2{(f16)v0, (f16)y};
+        if (live_row) *reinterpret_cast<h2*>(zr + lane_off + t * 32) = pr;
+      }
     }
     if (w == 0 && half_ == 0 && row_live) {
       part_ml[((size_t)pslot * H + h) * 2 + 0] = m;

@@ -20,6 +20,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "append_bodies.h"
 #include "common.h"
@@ -242,19 +243,23 @@ step_prologue_kernel(const f16* __restrict__ k, const f16* __restrict__ v, const
 // Online log-sum-exp over the slots c0, c0 + W, ... < s1, U per memory round
 // trip.  Every load of a batch is unconditional (indices past the end re-read
 // the last slot and get weight 0), so all of them are in flight before the
-// first use instead of one (m, l) round trip per slot.
-template <int U, int W>
-__device__ __forceinline__ void merge_slots(const float* __restrict__ ml, const float* __restrict__ zb, size_t zs,
+// first use instead of one (m, l) round trip per slot.  ZT = f16: the slot
+// holds z / l (weight 2^(m - M) * l); ZT = float: it holds z (weight 2^(m - M),
+// with l summed separately).
+template <int U, int W, typename ZT>
+__device__ __forceinline__ void merge_slots(const float* __restrict__ ml, const ZT* __restrict__ zb, size_t zs,
                                             int H, int c0, int s1, floatx4& a, float& M, float& den) {
+  constexpr bool kNorm = sizeof(ZT) == 2;
+  typedef typename std::conditional<kNorm, half4, floatx4>::type V4;
   for (int c = c0; c < s1; c += U * W) {
     float m[U], l[U];
-    floatx4 z[U];
+    V4 z[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int sl = min(c + u * W, s1 - 1);
       m[u] = ml[(size_t)sl * H * 2];
       l[u] = ml[(size_t)sl * H * 2 + 1];
-      z[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs);
+      z[u] = *reinterpret_cast<const V4*>(zb + (size_t)sl * zs);
     }
     __builtin_amdgcn_sched_barrier(0);
     float cm = M;
@@ -268,9 +273,15 @@ __device__ __forceinline__ void merge_slots(const float* __restrict__ ml, const 
     den *= sc;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float wgt = fast_exp2(m[u] - cm);
-      a += wgt * z[u];
-      den += wgt * l[u];
+      const float e = fast_exp2(m[u] - cm);
+      if constexpr (kNorm) {
+        const float wgt = e * l[u];
+        a += wgt * floatx4{(float)z[u][0], (float)z[u][1], (float)z[u][2], (float)z[u][3]};
+        den += wgt;
+      } else {
+        a += e * z[u];
+        den += e * l[u];
+      }
     }
     M = cm;
   }
@@ -280,9 +291,9 @@ __device__ __forceinline__ void merge_slots(const float* __restrict__ ml, const 
 // W slot groups (W = 1 or 4) each take every W-th slot, up to sixteen slots per
 // memory round trip, merge them online and combine through LDS.  W = 4 when
 // the launch has few workgroups (long sequences split into many ranges).
-template <int W>
+template <int W, typename ZT>
 __global__ void __launch_bounds__(256)
-merge_kernel(const float* __restrict__ part_z, const float* __restrict__ part_ml,
+merge_kernel(const ZT* __restrict__ part_z, const float* __restrict__ part_ml,
              const int32_t* __restrict__ plan, const int32_t* __restrict__ lens,
              int batch, int H, int RV, float* __restrict__ zf) {
   constexpr int kLanes = 256 / W;                   // threads per slot group
@@ -306,7 +317,7 @@ merge_kernel(const float* __restrict__ part_z, const float* __restrict__ part_ml
     return;
   }
   const float* ml = part_ml + (size_t)h * 2;
-  const float* zb = part_z + (size_t)h * RV + (live ? d : 0);
+  const ZT* zb = part_z + (size_t)h * RV + (live ? d : 0);
   const size_t zs = (size_t)H * RV;                 // slot stride
   floatx4 a = {};
   float M = -INFINITY, den = 0.f;
@@ -637,8 +648,8 @@ upproj_valu_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
 // and a pair's bytes are spread over two compute units.  Both halves merge all
 // of the pair's partial states; their ids (half * pairs + pair) put them on
 // one XCD when pairs % 8 == 0, so the second read of a slot can come from L2.
-//   1. Merge as in merge_kernel<4>: four slot groups take every fourth slot,
-//      kMuSlots slots per round trip, base-2 log-sum-exp online.  The half's
+//   1. Merge as in merge_kernel<4, f16>: four slot groups take every fourth
+//      slot, kMuSlots slots per round trip, base-2 log-sum-exp online.  The half's
 //      B_v columns (thread t: output dims 64*half + 8*(t%8) .. +7, latent rows
 //      (t/8)*r_v/64 .. +r_v/64-1) are fetched right behind the first round's
 //      loads: in flight during the merge without delaying its first round.
@@ -651,7 +662,7 @@ constexpr int kMuD = 128;
 constexpr int kMuCols = 64;              // output dims per workgroup
 
 __global__ void __launch_bounds__(512)
-merge_upproj_small_kernel(const float* __restrict__ part_z, const float* __restrict__ part_ml,
+merge_upproj_small_kernel(const f16* __restrict__ part_z, const float* __restrict__ part_ml,
                           const int32_t* __restrict__ plan, const int32_t* __restrict__ lens,
                           const f16* __restrict__ bv, f16* __restrict__ out, int batch, int H, int KV, int RV) {
   __shared__ __attribute__((aligned(16))) float zl[kUpvMaxRV];
@@ -680,12 +691,12 @@ merge_upproj_small_kernel(const float* __restrict__ part_z, const float* __restr
   const int s1 = pv.slot_base()[b + 1];
   const bool empty = lens[b] == 0 || s1 <= s0;       // uniform over the workgroup
   const float* ml = part_ml + (size_t)h * 2;
-  const float* zb = part_z + (size_t)h * RV + (d0 < RV ? d0 : 0);
+  const f16* zb = part_z + (size_t)h * RV + (d0 < RV ? d0 : 0);
   const size_t zs = (size_t)H * RV;                  // slot stride
   floatx4 a0 = {}, a1 = {};
   float M = -INFINITY, den = 0.f;
   float m[kMuSlots], l[kMuSlots];
-  floatx4 z0[kMuSlots], z1[kMuSlots];
+  half8 zh[kMuSlots];
   // every load of a round is unconditional (indices past the end re-read the
   // last slot and get weight 0), so all of them are in flight at once
   auto load_round = [&](int c) {
@@ -694,8 +705,7 @@ merge_upproj_small_kernel(const float* __restrict__ part_z, const float* __restr
       const int sl = min(c + u * kMuGroups, s1 - 1);
       m[u] = ml[(size_t)sl * H * 2];
       l[u] = ml[(size_t)sl * H * 2 + 1];
-      z0[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs);
-      z1[u] = *reinterpret_cast<const floatx4*>(zb + (size_t)sl * zs + 4);
+      zh[u] = *reinterpret_cast<const half8*>(zb + (size_t)sl * zs);
     }
   };
   int c = s0 + g;
@@ -719,10 +729,10 @@ merge_upproj_small_kernel(const float* __restrict__ part_z, const float* __restr
       den *= sc;
 #pragma unroll
       for (int u = 0; u < kMuSlots; ++u) {
-        const float wgt = fast_exp2(m[u] - cm);
-        a0 += wgt * z0[u];
-        a1 += wgt * z1[u];
-        den += wgt * l[u];
+        const float wgt = fast_exp2(m[u] - cm) * l[u];     // the slot holds z / l
+        a0 += wgt * floatx4{(float)zh[u][0], (float)zh[u][1], (float)zh[u][2], (float)zh[u][3]};
+        a1 += wgt * floatx4{(float)zh[u][4], (float)zh[u][5], (float)zh[u][6], (float)zh[u][7]};
+        den += wgt;
       }
       M = cm;
       c += kMuSlots * kMuGroups;
@@ -810,8 +820,8 @@ DecodeLayout decode_layout(const Shape& s, int batch, int max_context_len, int g
   off = align256(off + sizeof(float) * (size_t)batch * s.H * s.RK);
   L.off_ml = off;
   off = align256(off + sizeof(float) * (size_t)L.max_slots * s.H * 2);
-  L.off_z = off;
-  off = align256(off + sizeof(float) * (size_t)L.max_slots * s.H * s.RV);
+  L.off_z = off;                                    // z / l in fp16
+  off = align256(off + sizeof(f16) * (size_t)L.max_slots * s.H * s.RV);
   L.off_zf = off;
   off = align256(off + sizeof(float) * (size_t)batch * s.H * s.RV);
   L.bytes = off;
@@ -839,16 +849,24 @@ hipError_t launch_qproj(const Shape& s, int rows, const void* q, const void* b_k
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const Shape& s, int rows, const float* pz, const float* pml, const int32_t* plan,
-                        const int32_t* lens, float* zf, hipStream_t st) {
+hipError_t launch_merge(const Shape& s, int rows, const void* pz, const float* pml, const int32_t* plan,
+                        const int32_t* lens, float* zf, hipStream_t st, bool z16) {
   // few (row, head) pairs -> long sequences split into many ranges
   const bool few = (long long)rows * s.H < 512;
-  if (few)
-    hipLaunchKernelGGL(merge_kernel<4>, dim3(rows * s.H * ((s.RV + 255) / 256)), dim3(256), 0, st, pz, pml, plan,
-                       lens, rows, s.H, s.RV, zf);
-  else
-    hipLaunchKernelGGL(merge_kernel<1>, dim3(rows * s.H * ((s.RV + 1023) / 1024)), dim3(256), 0, st, pz, pml, plan,
-                       lens, rows, s.H, s.RV, zf);
+  const dim3 grid(rows * s.H * (few ? (s.RV + 255) / 256 : (s.RV + 1023) / 1024));
+  if (z16) {
+    const f16* z = static_cast<const f16*>(pz);
+    if (few)
+      hipLaunchKernelGGL((merge_kernel<4, f16>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, zf);
+    else
+      hipLaunchKernelGGL((merge_kernel<1, f16>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, zf);
+  } else {
+    const float* z = static_cast<const float*>(pz);
+    if (few)
+      hipLaunchKernelGGL((merge_kernel<4, float>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, zf);
+    else
+      hipLaunchKernelGGL((merge_kernel<1, float>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, zf);
+  }
   return hipGetLastError();
 }
 
@@ -933,7 +951,7 @@ static hipError_t decode_after_prologue(const DecodeLaunch& a) {
   int32_t* plan = reinterpret_cast<int32_t*>(a.ws + a.lay.off_plan);
   float* qt = reinterpret_cast<float*>(a.ws + a.lay.off_qt);
   float* pml = reinterpret_cast<float*>(a.ws + a.lay.off_ml);
-  float* pz = reinterpret_cast<float*>(a.ws + a.lay.off_z);
+  f16* pz = reinterpret_cast<f16*>(a.ws + a.lay.off_z);
   float* zf = reinterpret_cast<float*>(a.ws + a.lay.off_zf);
 
   // 2. latent attention (timed by its own dispatch when events are given)
@@ -947,7 +965,7 @@ static hipError_t decode_after_prologue(const DecodeLaunch& a) {
                        s.KV, s.RV);
     return hipGetLastError();
   }
-  err = launch_merge(s, a.batch, pz, pml, plan, a.context_lens, zf, a.stream);
+  err = launch_merge(s, a.batch, pz, pml, plan, a.context_lens, zf, a.stream, true);
   if (err != hipSuccess) return err;
   return launch_upproj(s, a.batch, zf, a.b_v, a.out, a.stream);
 }

@@ -103,14 +103,16 @@ hipError_t table_check_enqueue(const int32_t* block_tables, const int32_t* conte
 hipError_t launch_qproj(const Shape& s, int rows, const void* q, const void* b_k, float scale2, float* qt,
                         const int32_t* plan_lens, int plan_grid, int32_t* plan, hipStream_t st);
 // Log-sum-exp merge of each row's partial slots (slot_base at plan + 3 + rows;
-// rows with lens[row] == 0 give zeros).
-hipError_t launch_merge(const Shape& s, int rows, const float* pz, const float* pml, const int32_t* plan,
-                        const int32_t* lens, float* zf, hipStream_t st);
+// rows with lens[row] == 0 give zeros).  z16: the partial z are z / l in fp16
+// (decode); else unnormalised z in fp32 (prefill).
+hipError_t launch_merge(const Shape& s, int rows, const void* pz, const float* pml, const int32_t* plan,
+                        const int32_t* lens, float* zf, hipStream_t st, bool z16);
 // out[row, h] = zf[row, h] . B_v[:, g(h)*d : (g(h)+1)*d]
 hipError_t launch_upproj(const Shape& s, int rows, const float* zf, const void* b_v, void* out, hipStream_t st);
 
 // The latent attention launch (one kernel; qt, plan, pz, pml live in a.ws).
-hipError_t launch_attn_kernel(const DecodeLaunch& a, const float* qt, int32_t* plan, float* pz, float* pml);
+// Partial states: pz holds z / l in fp16, pml (m, l) in fp32.
+hipError_t launch_attn_kernel(const DecodeLaunch& a, const float* qt, int32_t* plan, _Float16* pz, float* pml);
 
 struct AppendLaunch {
   Shape s;
