@@ -642,25 +642,26 @@ upproj_valu_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
 
 // ---------------------------------------------------------------------------
 // host side
-// Few (sequence, head) pairs with d = 128 (long sequences at small batch): the
-// merge and the up-projection of one (sequence, head) in two 512-thread
-// workgroups, one per half of the 128 output dims, so Z never goes to memory
+// Few (sequence, head) pairs with d = 64 or 128 (long sequences at small
+// batch): the merge and the up-projection of one (sequence, head) in two
+// 512-thread workgroups, one per half of the d output dims, so Z never goes
+// to memory
 // and a pair's bytes are spread over two compute units.  Both halves merge all
 // of the pair's partial states; their ids (half * pairs + pair) put them on
 // one XCD when pairs % 8 == 0, so the second read of a slot can come from L2.
 //   1. Merge as in merge_kernel<4, f16>: four slot groups take every fourth
 //      slot, kMuSlots slots per round trip, base-2 log-sum-exp online.  The half's
-//      B_v columns (thread t: output dims 64*half + 8*(t%8) .. +7, latent rows
-//      (t/8)*r_v/64 .. +r_v/64-1) are fetched right behind the first round's
-//      loads: in flight during the merge without delaying its first round.
+//      B_v columns (thread t: output dims (d/2)*half + 8*(t % (d/16)) .. +7,
+//      latent rows kpt*g .. +kpt-1 of row group g = t / (d/16)) are fetched
+//      right behind the first round's loads: in flight during the merge
+//      without delaying its first round.
 //   2. The groups combine through LDS into the normalised z (LDS).
 //   3. out[b, h, half] = z . B_v columns: per-thread sums over its latent
-//      rows, reduced over the 64 row groups through LDS in two steps.
+//      rows, reduced over the row groups through LDS in two steps.
 constexpr int kMuGroups = 4;
 constexpr int kMuSlots = 8;
-constexpr int kMuD = 128;
-constexpr int kMuCols = 64;              // output dims per workgroup
 
+template <int D>
 __global__ void __launch_bounds__(512)
 merge_upproj_small_kernel(const f16* __restrict__ part_z, const float* __restrict__ part_ml,
                           const int32_t* __restrict__ plan, const int32_t* __restrict__ lens,
@@ -668,20 +669,27 @@ merge_upproj_small_kernel(const f16* __restrict__ part_z, const float* __restric
   __shared__ __attribute__((aligned(16))) float zl[kUpvMaxRV];
   __shared__ __attribute__((aligned(16))) float ca[kMuGroups][kUpvMaxRV];
   __shared__ float cm_s[kMuGroups], cl_s[kMuGroups];
-  __shared__ float red[64][kMuCols + 1];
-  __shared__ float red2[8][kMuCols];
+  constexpr int kCols = D / 2;                      // output dims per workgroup
+  constexpr int kCpr = kCols / 8;                    // threads per latent row (8 dims each)
+  constexpr int kGroups = 512 / kCpr;                // row groups
+  constexpr int kParts = 512 / kCols;                // first reduction step: parts of the row groups
+  static_assert(kGroups % kParts == 0, "whole parts");
+  __shared__ float red[kGroups][kCols + 1];
+  __shared__ float red2[kParts][kCols];
   const int t = threadIdx.x;
   const int pairs = batch * H;
   const int half_ = blockIdx.x / pairs, bh = blockIdx.x % pairs;
   const int h = bh % H, b = bh / H;
   const int kvh = h / (H / KV);
-  const size_t ld = (size_t)KV * kMuD;
+  const size_t ld = (size_t)KV * D;
 
-  // B_v columns and rows of this thread (clamped re-reads past r_v/64 rows are unused)
-  const int n8 = (t % 8) * 8, kq = t / 8;
-  const int kpt = RV / 64;                           // r_v is a multiple of 64, at most 1024
-  const f16* bcol = bv + (size_t)kvh * kMuD + half_ * kMuCols + n8;
-  half8 br[kUpvMaxRV / 64];
+  // B_v columns and rows of this thread (rows past r_v re-read the last row
+  // and are not used)
+  const int n8 = (t % kCpr) * 8, kq = t / kCpr;
+  const int kpt = (RV + kGroups - 1) / kGroups;     // latent rows per thread
+  constexpr int kMaxRows = (kUpvMaxRV + kGroups - 1) / kGroups;
+  const f16* bcol = bv + (size_t)kvh * D + half_ * kCols + n8;
+  half8 br[kMaxRows];
 
   // 1. merge: lane li of slot group g holds latent dims 8*li .. +7
   const int g = t / 128, li = t % 128;
@@ -711,9 +719,14 @@ merge_upproj_small_kernel(const f16* __restrict__ part_z, const float* __restric
   int c = s0 + g;
   const bool any = !empty && c < s1;                 // uniform over the slot group
   if (any) load_round(c);
+  // d = 128 takes r_v % 64 == 0, so every row group's rows exist; at d = 64
+  // the 128 row groups can outnumber the rows
+  constexpr bool kClamp = D == 64;
 #pragma unroll
-  for (int i = 0; i < kUpvMaxRV / 64; ++i)
-    br[i] = *reinterpret_cast<const half8*>(bcol + (size_t)(kq * kpt + min(i, kpt - 1)) * ld);
+  for (int i = 0; i < kMaxRows; ++i) {
+    const int row = kq * kpt + min(i, kpt - 1);
+    br[i] = *reinterpret_cast<const half8*>(bcol + (size_t)(kClamp ? min(row, RV - 1) : row) * ld);
+  }
   __builtin_amdgcn_sched_barrier(0);
   if (any) {
     for (;;) {
@@ -773,8 +786,8 @@ merge_upproj_small_kernel(const f16* __restrict__ part_z, const float* __restric
   // 3. up-projection of this half
   float acc[8] = {};
 #pragma unroll
-  for (int i = 0; i < kUpvMaxRV / 64; ++i) {
-    if (i < kpt) {
+  for (int i = 0; i < kMaxRows; ++i) {
+    if (i < kpt && (!kClamp || kq * kpt + i < RV)) {
       const float z = zl[kq * kpt + i];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += z * (float)br[i][e];
@@ -784,18 +797,19 @@ merge_upproj_small_kernel(const f16* __restrict__ part_z, const float* __restric
   for (int e = 0; e < 8; ++e) red[kq][n8 + e] = acc[e];
   __syncthreads();
   {
-    const int col = t % kMuCols, part = t / kMuCols;   // eight parts of eight row groups
+    constexpr int kPer = kGroups / kParts;            // row groups per part
+    const int col = t % kCols, part = t / kCols;
     float v = 0.f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v += red[part * 8 + q][col];
+    for (int q = 0; q < kPer; ++q) v += red[part * kPer + q][col];
     red2[part][col] = v;
   }
   __syncthreads();
-  if (t < kMuCols) {
+  if (t < kCols) {
     float sum = 0.f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) sum += red2[q][t];
-    out[((size_t)b * H + h) * kMuD + half_ * kMuCols + t] = (f16)sum;
+    for (int q = 0; q < kParts; ++q) sum += red2[q][t];
+    out[((size_t)b * H + h) * D + half_ * kCols + t] = (f16)sum;
   }
 }
 
@@ -959,10 +973,11 @@ static hipError_t decode_after_prologue(const DecodeLaunch& a) {
   if (err != hipSuccess) return err;
 
   // 3. merge, 4. up-projection (one launch for few (sequence, head) pairs at d = 128)
-  if ((long long)a.batch * s.H < 512 && s.D == kMuD && s.RV <= kUpvMaxRV && s.RV % 64 == 0) {
-    hipLaunchKernelGGL(merge_upproj_small_kernel, dim3(2 * a.batch * s.H), dim3(512), 0, a.stream, pz, pml, plan,
-                       a.context_lens, static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H,
-                       s.KV, s.RV);
+  if ((long long)a.batch * s.H < 512 && s.RV <= kUpvMaxRV &&
+      ((s.D == 128 && s.RV % 64 == 0) || (s.D == 64 && s.RV % 8 == 0))) {
+    const auto kern = s.D == 128 ? merge_upproj_small_kernel<128> : merge_upproj_small_kernel<64>;
+    hipLaunchKernelGGL(kern, dim3(2 * a.batch * s.H), dim3(512), 0, a.stream, pz, pml, plan, a.context_lens,
+                       static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H, s.KV, s.RV);
     return hipGetLastError();
   }
   err = launch_merge(s, a.batch, pz, pml, plan, a.context_lens, zf, a.stream, true);

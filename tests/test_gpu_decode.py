@@ -229,11 +229,11 @@ def test_ranges_spanning_many_sequences():
     check(got[live], ref[live], what="many short sequences")
 
 
-@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("d", [128, 64, 256])
 def test_single_long_sequence_every_range(d):
     """One sequence of 40,000 tokens (2,500 blocks): every workgroup range lies
-    inside it, so each (sequence, head) row merges ~250 partials.  d = 128
-    takes the fused small merge + up-projection, d = 64 the separate merge
+    inside it, so each (sequence, head) row merges ~250 partials.  d = 128 and
+    64 take the fused small merge + up-projection, d = 256 the separate merge
     (four slot groups) and VALU up-projection."""
     dev = gpu()
     lens = np.array([40000])
