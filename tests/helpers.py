@@ -83,11 +83,16 @@ def fp16_ulp(x):
 
 def check_latents(got16, exact, abssum, terms):
     """Append latents: the kernel rounds an fp32-accumulated dot product once to
-    fp16, so |got - exact| <= ulp16/2 + (terms/16 + 8) * 2^-24 * sum|w x|
-    (fp32 rounding on the longest accumulation path of 16-term MFMA steps).
+    fp16.  Every element must satisfy |got - exact| <= ulp16/2 + g * sum|w x|
+    with g = n * 2^-24 / (1 - n * 2^-24), n = terms + 8: the a-priori bound on
+    fp32 summation of `terms` exact products in any order (each partial sum
+    rounded once; the products of two fp16 values are exact in fp32), which
+    covers the sequential per-lane sums of the VALU paths as well as the MFMA
+    chains and the cross-lane reduction levels.
     Returns the fraction of latents within one fp16 step of round(exact)."""
     got = np.asarray(got16).astype(np.float64)
-    slack = (terms / 16 + 8) * 2.0 ** -24 * abssum
+    n = terms + 8
+    slack = n * 2.0 ** -24 / (1 - n * 2.0 ** -24) * abssum
     bound = 0.5 * fp16_ulp(np.maximum(np.abs(exact), np.abs(got))) + slack
     bad = np.abs(got - exact) > bound
     assert not bad.any(), f"{bad.sum()} latents beyond the fp32-accumulation bound"
