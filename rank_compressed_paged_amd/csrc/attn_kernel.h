@@ -16,7 +16,8 @@
 //   values   z[h,:] += P[h,t] . c_v[t,:] - one 32x32x16 f16 MFMA per 32 latent
 //            dims (rows = heads, k = the block's 16 tokens), whose B operand is
 //            exactly one 16-byte load of the dim-major V block.
-// Each (range, sequence) pair writes its (max, sum, z) partial state.
+// Each (range, sequence) pair writes its partial state: max and sum in fp32,
+// the normalised z / sum in fp16.
 //
 // Method: Proxima README text on wpnews ("Show HN: Proxima ..."), opening
 // description of STAR-KV (head-wise K latents, one joint V latent, compressed

@@ -1,16 +1,19 @@
 // STAR-KV decode kernels for gfx950 (MI355X).
 //
 // One decode call is four launches on the caller's stream:
-//   1. qproj_plan   q~ = scale*log2(e) * B_k[h] q  (MFMA at batch >= 16) and, in
-//                   its last workgroup, the work plan: every workgroup of
-//                   launch 2 gets an equal range of 16-token blocks of the whole
-//                   ragged batch (ranges may cross sequence boundaries).
-//   2. attn         the HBM-bound scan over the latent blocks (attn_kernel.hip);
-//                   each (range, sequence) pair leaves (max, sum, z) partials.
+//   1. qproj_plan   q~ = scale*log2(e) * B_k[h] q  (MFMA when r_k % 32 == 0 and
+//                   d % 16 == 0) and, in its last workgroup, the work plan:
+//                   every workgroup of launch 2 gets an equal range of 16-token
+//                   blocks of the whole ragged batch (ranges may cross sequence
+//                   boundaries).  A decode step (starkv_decode_step) runs the
+//                   step's append in the same launch (step_prologue).
+//   2. attn         the HBM-bound scan over the latent blocks (attn_kernel.h);
+//                   each (range, sequence) pair leaves a partial state: max m
+//                   and sum l in fp32, z / l in fp16.
 //   3. merge        log-sum-exp merge of a sequence's partials -> Z [B][H][r_v].
 //   4. upproj       out[b,h] = Z[b,h] . B_v[:, h*d:(h+1)*d]  (MFMA at batch >= 16).
-// With few (sequence, head) pairs at d = 128, launches 3 and 4 are one launch
-// (merge_upproj_small) that keeps Z in LDS.
+// With few (sequence, head) pairs at d = 64 or 128, launches 3 and 4 are one
+// launch (merge_upproj_small) that keeps Z in LDS.
 //
 // Method: Proxima README text on wpnews ("Show HN: Proxima ..."), opening
 // description of STAR-KV (head-wise K latents, one joint V latent, compressed
