@@ -117,3 +117,62 @@ def test_graph_append_prefill():
                        g["context_lens"], 1.0 / math.sqrt(128), max_context_len=max(lens), workspace=ws, out=out)
 
     replay_and_compare(step, {"out": out, "k_pool": g["k_pool"], "v_pool": g["v_pool"]}, "append+prefill")
+
+
+def _step_case(seed, h, kv, rk, rv, batch):
+    import torch
+    dev = gpu()
+    d = 64 if h <= 8 else 128
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, 700, size=batch)
+    lens[0] = 0 if batch > 3 else lens[0]
+    case = synth.make_case(seed, batch, h, d, rk, rv, lens, spare_tokens=1, kv_heads=kv)
+    g = to_dev(case, dev)
+    k_new, v_new = synth.make_new_rows(seed, batch, kv, d)
+    g["k_new"] = torch.from_numpy(k_new).to(dev)
+    g["v_new"] = torch.from_numpy(v_new).to(dev)
+    g["seqs"] = torch.arange(batch, dtype=torch.int32, device=dev)
+    g["pos"] = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    g["new_lens"] = g["pos"] + 1
+    return g, d, int(lens.max()) + 1
+
+
+@pytest.mark.parametrize("h,kv,rk,rv,batch", [(32, 32, 64, 1024, 6), (32, 32, 64, 1024, 64), (32, 8, 64, 512, 20)])
+def test_graph_decode_step(h, kv, rk, rv, batch):
+    """The one-call step (append, q~ and plan in one launch, then attention,
+    merge, up-projection) captured and replayed."""
+    import torch
+    import rank_compressed_paged_amd as starkv
+    g, d, max_len = _step_case(950 + batch + kv, h, kv, rk, rv, batch)
+    dims = starkv.dims_of(g["k_pool"], g["v_pool"], g["block_tables"], d, heads=h)
+    ws = torch.empty(starkv.decode_workspace_size(dims, batch, max_len), dtype=torch.uint8, device=g["q"].device)
+    out = torch.empty_like(g["q"])
+    log(f"graph decode_step H={h} H_kv={kv} r_k={rk} r_v={rv} batch={batch}")
+
+    def step():
+        starkv.decode_step(g["k_new"], g["v_new"], g["b_k"], g["b_v"], g["seqs"], g["pos"], g["q"], g["b_k"],
+                           g["b_v"], g["k_pool"], g["v_pool"], g["block_tables"], g["new_lens"], 1.0 / math.sqrt(d),
+                           max_context_len=max_len, workspace=ws, out=out)
+
+    replay_and_compare(step, {"out": out, "k_pool": g["k_pool"], "v_pool": g["v_pool"]},
+                       f"decode_step H={h} H_kv={kv} batch={batch}")
+
+
+@pytest.mark.parametrize("batch", [6, 40])
+def test_graph_append_decode_noalloc(batch):
+    """Append then the no-workspace decode (its scratch is the library's
+    fixed device array): the case that entry point exists for."""
+    import torch
+    import rank_compressed_paged_amd as starkv
+    g, d, max_len = _step_case(970 + batch, 32, 32, 64, 1024, batch)
+    out = torch.empty_like(g["q"])
+    log(f"graph append+decode_noalloc batch={batch}")
+
+    def step():
+        starkv.append(g["k_new"], g["v_new"], g["b_k"], g["b_v"], g["block_tables"], g["seqs"], g["pos"],
+                      g["k_pool"], g["v_pool"])
+        starkv.decode_noalloc(g["q"], g["b_k"], g["b_v"], g["k_pool"], g["v_pool"], g["block_tables"],
+                              g["new_lens"], 1.0 / math.sqrt(d), max_context_len=max_len, out=out)
+
+    replay_and_compare(step, {"out": out, "k_pool": g["k_pool"], "v_pool": g["v_pool"]},
+                       f"append+decode_noalloc batch={batch}")
