@@ -79,3 +79,41 @@ def test_step_without_new_rows_is_a_decode():
                         1.0, max_context_len=1000)
     torch.cuda.synchronize()
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("batch", [520, 1100])
+def test_step_batch_beyond_one_plan_pass(batch):
+    """More sequences than the plan workgroup has threads (512 in the step's
+    first launch, 256 in the decode's): the plan's scans run in several passes
+    and each sequence writes its ranges' first-sequence entries itself.  Short
+    ragged sequences, some empty, one new row each."""
+    import torch
+    import rank_compressed_paged_amd as starkv
+    dev = gpu()
+    rng = np.random.default_rng(1300 + batch)
+    lens = rng.integers(0, 90, size=batch).astype(np.int32)
+    case = synth.make_case(1300 + batch, batch, 8, 64, 32, 256, lens, spare_tokens=1)
+    seqs = np.arange(batch, dtype=np.int32)
+    poss = lens.copy()
+    k_new, v_new = synth.make_new_rows(1300 + batch, batch, 8, 64)
+    new_lens = (lens + 1).astype(np.int32)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    scale = 1.0 / math.sqrt(64)
+    log(f"step batch={batch} (multi-pass plan)")
+    a = to_dev(case, dev)
+    starkv.append(t(k_new), t(v_new), a["b_k"], a["b_v"], a["block_tables"], t(seqs), t(poss), a["k_pool"],
+                  a["v_pool"])
+    ref = starkv.decode(a["q"], a["b_k"], a["b_v"], a["k_pool"], a["v_pool"], a["block_tables"], t(new_lens), scale,
+                        max_context_len=int(new_lens.max()))
+    b = to_dev(case, dev)
+    got = starkv.decode_step(t(k_new), t(v_new), b["b_k"], b["b_v"], t(seqs), t(poss), b["q"], b["b_k"], b["b_v"],
+                             b["k_pool"], b["v_pool"], b["block_tables"], t(new_lens), scale,
+                             max_context_len=int(new_lens.max()))
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    kp, vp = oracle.append(k_new, v_new, case["b_k"], case["b_v"], case["block_tables"], seqs, poss,
+                           case["k_pool"], case["v_pool"])
+    want = oracle.decode(case["q"], case["b_k"], case["b_v"], kp, vp, case["block_tables"], new_lens, scale)
+    err = normwise_err(got.float().cpu().numpy(), want).max()
+    log(f"  normwise max {err:.3e}")
+    assert err <= DECODE_TOL
