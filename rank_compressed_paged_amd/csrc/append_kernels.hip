@@ -44,7 +44,7 @@ append_v_valu_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
 // heads, r_v 1024 on 256 units).  Past that, a V-side workgroup (164 VGPRs per
 // lane) leaves too few registers on its unit for a second one, so K-side
 // workgroups would wait for the V side: those appends use two launches.
-template <bool VM, bool KM>
+template <int VM, bool KM>
 __global__ void __launch_bounds__(512)
 append_kv_kernel(const f16* __restrict__ k, const f16* __restrict__ v, const f16* __restrict__ wk,
                  const f16* __restrict__ wv, int n, int KV, int D, int RK, int RV, SlotOf where,
@@ -72,8 +72,8 @@ hipError_t append_enqueue(const AppendLaunch& a) {
   // (or both sides are VALU): MFMA-sized V workgroups fill their compute units
   const bool both_valu = !r.kmfma && !r.vrows && !r.vmfma;
   if (both_valu || (!r.vrows && grid_kv <= a.cus)) {
-    const auto kern = r.vmfma ? (r.kmfma ? append_kv_kernel<true, true> : append_kv_kernel<true, false>)
-                              : (r.kmfma ? append_kv_kernel<false, true> : append_kv_kernel<false, false>);
+    const auto kern = r.vmfma ? (r.kmfma ? append_kv_kernel<1, true> : append_kv_kernel<1, false>)
+                              : (r.kmfma ? append_kv_kernel<0, true> : append_kv_kernel<0, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid_kv), dim3(512), 0, a.stream, k, v, wk, wv, a.n, s.KV, s.D, s.RK,
                        s.RV, where, kc, vc, r);
     return hipGetLastError();
