@@ -12,7 +12,8 @@
 //   2. attn         the HBM-bound scan over the latent blocks (attn_kernel.h);
 //                   each (range, sequence) pair leaves a partial state: max m
 //                   and sum l in fp32, z / l in fp16.
-//   3. merge        log-sum-exp merge of a sequence's partials -> Z [B][H][r_v].
+//   3. merge        log-sum-exp merge of a sequence's partials -> Z [B][H][r_v],
+//                   rounded to fp16 (fp32 for the many-row up-projection).
 //   4. upproj       out[b,h] = Z[b,h] . B_v[:, h*d:(h+1)*d]  (MFMA at batch >= 16).
 // With few (sequence, head) pairs at d = 64 or 128, launches 3 and 4 are one
 // launch (merge_upproj_small) that keeps Z in LDS.
@@ -303,15 +304,24 @@ __device__ __forceinline__ void merge_slots(const float* __restrict__ ml, const 
   }
 }
 
+// Four merged latents of one row: fp32 (prefill, and the many-row
+// up-projection) or rounded once to fp16 (decode's MFMA and VALU
+// up-projections take the fp16 row as their A operand).
+__device__ __forceinline__ void store_z4(float* p, floatx4 v) { *reinterpret_cast<floatx4*>(p) = v; }
+__device__ __forceinline__ void store_z4(f16* p, floatx4 v) {
+  *reinterpret_cast<half4*>(p) = half4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+}
+
 // One 256-thread workgroup merges 1024/W latent dims of one (sequence, head):
 // W slot groups (W = 1 or 4) each take every W-th slot, up to sixteen slots per
 // memory round trip, merge them online and combine through LDS.  W = 4 when
 // the launch has few workgroups (long sequences split into many ranges).
-template <int W, typename ZT>
+// ZT: the partial states' z type; OT: the merged row's type.
+template <int W, typename ZT, typename OT>
 __global__ void __launch_bounds__(256)
 merge_kernel(const ZT* __restrict__ part_z, const float* __restrict__ part_ml,
              const int32_t* __restrict__ plan, const int32_t* __restrict__ lens,
-             int batch, int H, int RV, float* __restrict__ zf) {
+             int batch, int H, int RV, OT* __restrict__ zf) {
   constexpr int kLanes = 256 / W;                   // threads per slot group
   constexpr int kDims = 4 * kLanes;                 // latent dims per workgroup
   __shared__ floatx4 ca[W][kLanes];
@@ -324,12 +334,12 @@ merge_kernel(const ZT* __restrict__ part_z, const float* __restrict__ part_ml,
   const int b = blockIdx.x / (dchunks * H);
   const int d = dc * kDims + li * 4;
   const bool live = d < RV;
-  float* zrow = zf + ((size_t)b * H + h) * RV;
+  OT* zrow = zf + ((size_t)b * H + h) * RV;
   const PlanView pv{plan, batch};
   const int s0 = pv.slot_base()[b];
   const int s1 = pv.slot_base()[b + 1];
   if (lens[b] == 0 || s1 <= s0) {
-    if (w == 0 && live) *reinterpret_cast<floatx4*>(zrow + d) = floatx4{};
+    if (w == 0 && live) store_z4(zrow + d, floatx4{});
     return;
   }
   const float* ml = part_ml + (size_t)h * 2;
@@ -346,7 +356,7 @@ merge_kernel(const ZT* __restrict__ part_z, const float* __restrict__ part_ml,
   else
     merge_slots<16, W>(ml, zb, zs, H, s0 + w, s1, a, M, den);
   if constexpr (W == 1) {
-    if (live) *reinterpret_cast<floatx4*>(zrow + d) = a * (1.f / den);
+    if (live) store_z4(zrow + d, a * (1.f / den));
   } else {
     ca[w][li] = a;
     if (li == 0) {
@@ -368,7 +378,7 @@ merge_kernel(const ZT* __restrict__ part_z, const float* __restrict__ part_ml,
           dsum += wgt * cl_s[q];
         }
       }
-      *reinterpret_cast<floatx4*>(zrow + d) = sum * (1.f / dsum);
+      store_z4(zrow + d, sum * (1.f / dsum));
     }
   }
 }
@@ -380,17 +390,20 @@ merge_kernel(const ZT* __restrict__ part_z, const float* __restrict__ part_ml,
 // MFMA path: a workgroup computes a [32 batch x 32 dims] tile of one head; its
 // eight waves split r_v and reduce through LDS.  B_v is stored dims-contiguous,
 // so each wave reads its [r_v/8 x 32] slice of B_v with coalesced 16-byte row
-// loads and transposes it through LDS into k-contiguous MFMA fragments.  Z
-// (fp32) enters the f16 MFMA as a hi + lo pair, so the product keeps ~22 bits
-// of Z.  All global loads are in flight before the first MFMA.
+// loads and transposes it through LDS into k-contiguous MFMA fragments.  An
+// fp32 Z (ZT = float) enters the f16 MFMA as a hi + lo pair, so the product
+// keeps ~22 bits of Z; an fp16 Z (ZT = f16, decode) is the A fragment itself,
+// one 16-byte load and one MFMA per k-step.  All global loads are in flight
+// before the first MFMA.
 constexpr int kUpWaves = 8;
 constexpr int kUpMaxSpan = 128;          // r_v / kUpWaves <= 128 (r_v <= 1024)
 constexpr int kUpPad = 8;
 
-template <int NS>                        // NS = r_v / (16 * kUpWaves) k-steps per wave
+template <int NS, typename ZT>           // NS = r_v / (16 * kUpWaves) k-steps per wave
 __global__ void __launch_bounds__(kUpWaves * 64)
-upproj_mfma_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
+upproj_mfma_kernel(const ZT* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
                    int batch, int H, int KV, int D) {
+  constexpr bool kZ16 = sizeof(ZT) == 2;
   constexpr int RV = NS * 16 * kUpWaves;
   constexpr int kspan = NS * 16;
   __shared__ __attribute__((aligned(16))) f16 bt[kUpWaves][32][kspan + kUpPad];
@@ -416,14 +429,19 @@ upproj_mfma_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
   const int kbase = w * kspan;
   // B_v slice rows kbase.., 32 dims from h*D + nt*32: lane -> (row l/4, 8 dims)
   const f16* bsrc = bv + (size_t)(kbase + (lane >> 2)) * ld + (size_t)kvh * D + nt * 32 + (lane & 3) * 8;
-  const float* zrow = zf + ((size_t)(brow ? b : batch - 1) * H + h) * RV + kbase + kofs;
+  const ZT* zrow = zf + ((size_t)(brow ? b : batch - 1) * H + h) * RV + kbase + kofs;
   half8 braw[NS];
-  floatx4 za[NS][2];
+  floatx4 za[kZ16 ? 1 : NS][2];
+  half8 zh[kZ16 ? NS : 1];
 #pragma unroll
   for (int u = 0; u < NS; ++u) {
     braw[u] = *reinterpret_cast<const half8*>(bsrc + (size_t)u * 16 * ld);
-    za[u][0] = *reinterpret_cast<const floatx4*>(zrow + u * 16);
-    za[u][1] = *reinterpret_cast<const floatx4*>(zrow + u * 16 + 4);
+    if constexpr (kZ16) {
+      zh[u] = *reinterpret_cast<const half8*>(zrow + u * 16);
+    } else {
+      za[u][0] = *reinterpret_cast<const floatx4*>(zrow + u * 16);
+      za[u][1] = *reinterpret_cast<const floatx4*>(zrow + u * 16 + 4);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);     // every load in flight before the first LDS write
   f16 (*tw)[kspan + kUpPad] = bt[w];
@@ -435,15 +453,19 @@ upproj_mfma_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
 #pragma unroll
   for (int u = 0; u < NS; ++u) {
     const half8 bb = *reinterpret_cast<const half8*>(&tw[lane & 31][u * 16 + kofs]);
-    half8 hi, lo;
+    if constexpr (kZ16) {
+      acc = mfma32x32x16(brow ? zh[u] : half8{}, bb, acc);
+    } else {
+      half8 hi, lo;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float z = brow ? za[u][e >> 2][e & 3] : 0.f;
-      hi[e] = (f16)z;
-      lo[e] = (f16)(z - (float)hi[e]);
+      for (int e = 0; e < 8; ++e) {
+        const float z = brow ? za[u][e >> 2][e & 3] : 0.f;
+        hi[e] = (f16)z;
+        lo[e] = (f16)(z - (float)hi[e]);
+      }
+      acc = mfma32x32x16(hi, bb, acc);
+      acc = mfma32x32x16(lo, bb, acc);
     }
-    acc = mfma32x32x16(hi, bb, acc);
-    acc = mfma32x32x16(lo, bb, acc);
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) red[w][r][lane] = acc[r];
@@ -581,8 +603,9 @@ upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
 constexpr int kSmallBatch = 16;
 constexpr int kUpvMaxRV = 1024;
 
+template <typename ZT>                   // merged rows in fp32 (prefill) or fp16 (decode)
 __global__ void __launch_bounds__(256)
-upproj_valu_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
+upproj_valu_kernel(const ZT* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
                    int batch, int H, int KV, int D, int RV) {
   __shared__ __attribute__((aligned(16))) float zl[kSmallBatch][kUpvMaxRV];
   __shared__ float red[64][4][33];
@@ -612,8 +635,17 @@ upproj_valu_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
     for (int i = 0; i < kPer; ++i) {
       const int idx = t + 256 * i;
       const int r = idx / (RV / 4), c = idx % (RV / 4);
-      zv[i] = idx < rows * (RV / 4) ? *reinterpret_cast<const floatx4*>(zf + ((size_t)(row0 + r) * H + h) * RV + c * 4)
-                                    : floatx4{};
+      if (idx < rows * (RV / 4)) {
+        const ZT* src = zf + ((size_t)(row0 + r) * H + h) * RV + c * 4;
+        if constexpr (sizeof(ZT) == 2) {
+          const half4 zz = *reinterpret_cast<const half4*>(src);
+          zv[i] = floatx4{(float)zz[0], (float)zz[1], (float)zz[2], (float)zz[3]};
+        } else {
+          zv[i] = *reinterpret_cast<const floatx4*>(src);
+        }
+      } else {
+        zv[i] = floatx4{};
+      }
     }
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the LDS writes
 #pragma unroll
@@ -665,7 +697,7 @@ upproj_valu_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
 // and a pair's bytes are spread over two compute units.  Both halves merge all
 // of the pair's partial states; their ids (half * pairs + pair) put them on
 // one XCD when pairs % 8 == 0, so the second read of a slot can come from L2.
-//   1. Merge as in merge_kernel<4, f16>: four slot groups take every fourth
+//   1. Merge as in merge_kernel<4, f16, .>: four slot groups take every fourth
 //      slot, kMuSlots slots per round trip, base-2 log-sum-exp online.  The half's
 //      B_v columns (thread t: output dims (d/2)*half + 8*(t % (d/16)) .. +7,
 //      latent rows kpt*g .. +kpt-1 of row group g = t / (d/16)) are fetched
@@ -880,53 +912,85 @@ hipError_t launch_qproj(const Shape& s, int rows, const void* q, const void* b_k
 }
 
 hipError_t launch_merge(const Shape& s, int rows, const void* pz, const float* pml, const int32_t* plan,
-                        const int32_t* lens, float* zf, hipStream_t st, bool z16) {
+                        const int32_t* lens, void* zf, hipStream_t st, bool z16, bool zout16) {
   // few (row, head) pairs -> long sequences split into many ranges
   const bool few = (long long)rows * s.H < 512;
   const dim3 grid(rows * s.H * (few ? (s.RV + 255) / 256 : (s.RV + 1023) / 1024));
-  if (z16) {
+  if (z16 && zout16) {
     const f16* z = static_cast<const f16*>(pz);
+    f16* o = static_cast<f16*>(zf);
     if (few)
-      hipLaunchKernelGGL((merge_kernel<4, f16>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, zf);
+      hipLaunchKernelGGL((merge_kernel<4, f16, f16>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, o);
     else
-      hipLaunchKernelGGL((merge_kernel<1, f16>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, zf);
+      hipLaunchKernelGGL((merge_kernel<1, f16, f16>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, o);
+  } else if (z16) {
+    const f16* z = static_cast<const f16*>(pz);
+    float* o = static_cast<float*>(zf);
+    if (few)
+      hipLaunchKernelGGL((merge_kernel<4, f16, float>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, o);
+    else
+      hipLaunchKernelGGL((merge_kernel<1, f16, float>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, o);
   } else {
+    if (zout16) return hipErrorInvalidValue;       // fp32 partials are merged for the fp32 paths only
     const float* z = static_cast<const float*>(pz);
+    float* o = static_cast<float*>(zf);
     if (few)
-      hipLaunchKernelGGL((merge_kernel<4, float>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, zf);
+      hipLaunchKernelGGL((merge_kernel<4, float, float>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, o);
     else
-      hipLaunchKernelGGL((merge_kernel<1, float>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, zf);
+      hipLaunchKernelGGL((merge_kernel<1, float, float>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, o);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_upproj(const Shape& s, int rows, const float* zf, const void* b_v, void* out, hipStream_t st) {
-  if (rows >= 256 && s.D == 128 && s.RV % kUpRowsSpan == 0) {
+static bool upproj_rows_path(const Shape& s, int rows) {
+  return rows >= 256 && s.D == 128 && s.RV % kUpRowsSpan == 0;
+}
+
+bool upproj_accepts_z16(const Shape& s, int rows) { return !upproj_rows_path(s, rows); }
+
+template <typename ZT>
+static void launch_upproj_mfma(const Shape& s, int rows, const ZT* zf, const f16* bv, f16* o, int grid,
+                               hipStream_t st) {
+  const dim3 g(grid), b(kUpWaves * 64);
+  switch (s.RV / (16 * kUpWaves)) {
+    case 1: hipLaunchKernelGGL((upproj_mfma_kernel<1, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+    case 2: hipLaunchKernelGGL((upproj_mfma_kernel<2, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+    case 3: hipLaunchKernelGGL((upproj_mfma_kernel<3, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+    case 4: hipLaunchKernelGGL((upproj_mfma_kernel<4, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+    case 5: hipLaunchKernelGGL((upproj_mfma_kernel<5, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+    case 6: hipLaunchKernelGGL((upproj_mfma_kernel<6, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+    case 7: hipLaunchKernelGGL((upproj_mfma_kernel<7, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+    default: hipLaunchKernelGGL((upproj_mfma_kernel<8, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+  }
+}
+
+hipError_t launch_upproj(const Shape& s, int rows, const void* zf, bool z16, const void* b_v, void* out,
+                         hipStream_t st) {
+  const f16* bv = static_cast<const f16*>(b_v);
+  f16* o = static_cast<f16*>(out);
+  if (upproj_rows_path(s, rows)) {
+    if (z16) return hipErrorInvalidValue;
     const int rtiles = (rows + kUpRowsTile - 1) / kUpRowsTile;
     const int grid = rtiles * ((s.H + 7) / 8) * 8;
-    hipLaunchKernelGGL(upproj_rows_kernel, dim3(grid), dim3(512), 0, st, zf, static_cast<const f16*>(b_v),
-                       static_cast<f16*>(out), rows, s.H, s.KV, s.RV);
+    hipLaunchKernelGGL(upproj_rows_kernel, dim3(grid), dim3(512), 0, st, static_cast<const float*>(zf), bv, o, rows,
+                       s.H, s.KV, s.RV);
     return hipGetLastError();
   }
   if (rows >= kSmallBatch && s.D % 32 == 0 && s.RV % (16 * kUpWaves) == 0 && s.RV <= kUpWaves * kUpMaxSpan) {
     const int groups = ((rows + 31) / 32) * s.H;
     const int grid = ((groups + 7) / 8) * 8 * (s.D / 32);
-    const f16* bv = static_cast<const f16*>(b_v);
-    f16* o = static_cast<f16*>(out);
-    switch (s.RV / (16 * kUpWaves)) {
-      case 1: hipLaunchKernelGGL(upproj_mfma_kernel<1>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-      case 2: hipLaunchKernelGGL(upproj_mfma_kernel<2>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-      case 3: hipLaunchKernelGGL(upproj_mfma_kernel<3>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-      case 4: hipLaunchKernelGGL(upproj_mfma_kernel<4>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-      case 5: hipLaunchKernelGGL(upproj_mfma_kernel<5>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-      case 6: hipLaunchKernelGGL(upproj_mfma_kernel<6>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-      case 7: hipLaunchKernelGGL(upproj_mfma_kernel<7>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-      default: hipLaunchKernelGGL(upproj_mfma_kernel<8>, dim3(grid), dim3(kUpWaves * 64), 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-    }
+    if (z16)
+      launch_upproj_mfma(s, rows, static_cast<const f16*>(zf), bv, o, grid, st);
+    else
+      launch_upproj_mfma(s, rows, static_cast<const float*>(zf), bv, o, grid, st);
   } else {
-    const int grid = s.H * ((s.D + 31) / 32);
-    hipLaunchKernelGGL(upproj_valu_kernel, dim3(grid, (rows + kSmallBatch - 1) / kSmallBatch), dim3(256), 0, st, zf,
-                       static_cast<const f16*>(b_v), static_cast<f16*>(out), rows, s.H, s.KV, s.D, s.RV);
+    const dim3 grid(s.H * ((s.D + 31) / 32), (rows + kSmallBatch - 1) / kSmallBatch);
+    if (z16)
+      hipLaunchKernelGGL(upproj_valu_kernel<f16>, grid, dim3(256), 0, st, static_cast<const f16*>(zf), bv, o, rows,
+                         s.H, s.KV, s.D, s.RV);
+    else
+      hipLaunchKernelGGL(upproj_valu_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(zf), bv, o,
+                         rows, s.H, s.KV, s.D, s.RV);
   }
   return hipGetLastError();
 }
@@ -996,9 +1060,11 @@ static hipError_t decode_after_prologue(const DecodeLaunch& a) {
                        static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H, s.KV, s.RV);
     return hipGetLastError();
   }
-  err = launch_merge(s, a.batch, pz, pml, plan, a.context_lens, zf, a.stream, true);
+  // merged rows in fp16 wherever the up-projection takes them
+  const bool z16 = upproj_accepts_z16(s, a.batch);
+  err = launch_merge(s, a.batch, pz, pml, plan, a.context_lens, zf, a.stream, true, z16);
   if (err != hipSuccess) return err;
-  return launch_upproj(s, a.batch, zf, a.b_v, a.out, a.stream);
+  return launch_upproj(s, a.batch, zf, z16, a.b_v, a.out, a.stream);
 }
 
 hipError_t decode_enqueue(const DecodeLaunch& a) {

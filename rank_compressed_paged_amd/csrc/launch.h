@@ -104,11 +104,17 @@ hipError_t launch_qproj(const Shape& s, int rows, const void* q, const void* b_k
                         const int32_t* plan_lens, int plan_grid, int32_t* plan, hipStream_t st);
 // Log-sum-exp merge of each row's partial slots (slot_base at plan + 3 + rows;
 // rows with lens[row] == 0 give zeros).  z16: the partial z are z / l in fp16
-// (decode); else unnormalised z in fp32 (prefill).
+// (decode); else unnormalised z in fp32 (prefill).  zout16: the merged rows
+// are written in fp16, else fp32.
 hipError_t launch_merge(const Shape& s, int rows, const void* pz, const float* pml, const int32_t* plan,
-                        const int32_t* lens, float* zf, hipStream_t st, bool z16);
-// out[row, h] = zf[row, h] . B_v[:, g(h)*d : (g(h)+1)*d]
-hipError_t launch_upproj(const Shape& s, int rows, const float* zf, const void* b_v, void* out, hipStream_t st);
+                        const int32_t* lens, void* zf, hipStream_t st, bool z16, bool zout16);
+// Whether launch_upproj can take fp16 merged rows for `rows` rows (every path
+// but the many-row one, which stages fp32 rows).
+bool upproj_accepts_z16(const Shape& s, int rows);
+// out[row, h] = zf[row, h] . B_v[:, g(h)*d : (g(h)+1)*d]; zf fp16 when z16
+// (only where upproj_accepts_z16), else fp32
+hipError_t launch_upproj(const Shape& s, int rows, const void* zf, bool z16, const void* b_v, void* out,
+                         hipStream_t st);
 
 // The latent attention launch (one kernel; qt, plan, pz, pml live in a.ws).
 // Partial states: pz holds z / l in fp16, pml (m, l) in fp32.

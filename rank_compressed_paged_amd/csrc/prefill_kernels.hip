@@ -772,10 +772,10 @@ hipError_t prefill_enqueue(const PrefillLaunch& a, int device) {
 
   if (!zdirect) {
     const PrefillPlan P{plan, a.rows, a.lay.tile_cap};
-    err = launch_merge(s, a.rows, pz, pml, plan, P.row_len_w(), zf, a.stream, false);
+    err = launch_merge(s, a.rows, pz, pml, plan, P.row_len_w(), zf, a.stream, false, false);
     if (err != hipSuccess) return err;
   }
-  return launch_upproj(s, a.rows, zf, a.b_v, a.out, a.stream);
+  return launch_upproj(s, a.rows, zf, false, a.b_v, a.out, a.stream);
 }
 
 }  // namespace starkv
