@@ -21,14 +21,19 @@ inline void launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t st, hipEve
 }
 
 // Shortest range of 16-token blocks an attention workgroup takes, by the
-// host's bound on the batch's blocks.  Each range flushes H*r_v fp32 of
+// host's bound on the batch's blocks.  Each range flushes H*r_v values of
 // partial state at its end, all ranges at about the same time: longer ranges
 // mean fewer partials and a shorter write burst.  Small decodes (up to 1,024
 // blocks) are latency-bound instead and want every block in flight at once.
 // Measured on MI355X at 32 heads, r_v 1024: 4 blocks took a 1 x 1,024-token
 // decode's attention from 22 to 15 us; 12 blocks took 16 x 2,048 tokens from
 // 46 to 43 us (8 and 16 were slower); larger batches fill every CU anyway.
-constexpr int min_blocks_per_wg(long long blocks_ub) { return blocks_ub <= 1024 ? 4 : 12; }
+// Up to 128 blocks a range is one block: a 256-token decode at 4 heads, d 64
+// went from 17.0 to 13.7 us per step (attention 7.0 -> 5.4 us), 64-128 blocks
+// at 32 heads were unchanged, and 256-512 blocks were 10-14 % slower.
+constexpr int min_blocks_per_wg(long long blocks_ub) {
+  return blocks_ub <= 128 ? 1 : (blocks_ub <= 1024 ? 4 : 12);
+}
 // Hard cap on attention workgroups (sizes the workspace without a device query).
 constexpr int kMaxGrid = 1024;
 // Lazy-rescale threshold (log2 units) of the running softmax maximum.
