@@ -383,6 +383,86 @@ merge_kernel(const ZT* __restrict__ part_z, const float* __restrict__ part_ml,
   }
 }
 
+// Many (sequence, head) pairs (decode, r_v <= 1024): TP threads per pair, 8
+// latent dims each (one 16-byte load per slot), 256 / TP pairs per workgroup
+// (TP = 128 up to r_v = 1024, 64 up to 512), so no thread is idle at r_v 512
+// and a wave instruction reads 1 KiB of a slot.  The online log-sum-exp of
+// merge_slots, at most eight slots per memory round trip (80 VGPRs, six waves
+// per SIMD: every workgroup of a 64 x 32-head decode is resident at once).
+template <int TP, typename OT>
+__global__ void __launch_bounds__(256)
+merge_wide_kernel(const f16* __restrict__ part_z, const float* __restrict__ part_ml,
+                  const int32_t* __restrict__ plan, const int32_t* __restrict__ lens,
+                  int batch, int H, int RV, OT* __restrict__ zf) {
+  constexpr int PPW = 256 / TP;
+  const int li = threadIdx.x % TP;
+  const long long pair = (long long)blockIdx.x * PPW + threadIdx.x / TP;
+  if (pair >= (long long)batch * H) return;          // whole pairs leave; no barrier follows
+  const int h = (int)(pair % H);
+  const int b = (int)(pair / H);
+  const int d = li * 8;
+  const bool live = d < RV;
+  OT* zrow = zf + (size_t)pair * RV;
+  const PlanView pv{plan, batch};
+  const int s0 = pv.slot_base()[b];
+  const int s1 = pv.slot_base()[b + 1];
+  if (lens[b] == 0 || s1 <= s0) {
+    if (live) {
+      store_z4(zrow + d, floatx4{});
+      store_z4(zrow + d + 4, floatx4{});
+    }
+    return;
+  }
+  const float* ml = part_ml + (size_t)h * 2;
+  const f16* zb = part_z + (size_t)h * RV + (live ? d : 0);
+  const size_t zs = (size_t)H * RV;
+  floatx4 a0 = {}, a1 = {};
+  float M = -INFINITY, den = 0.f;
+  const int n = s1 - s0;
+  auto run = [&](auto Uc) {
+    constexpr int U = decltype(Uc)::value;
+    for (int c = s0; c < s1; c += U) {
+      float m[U], l[U];
+      half8 z[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int sl = min(c + u, s1 - 1);
+        m[u] = ml[(size_t)sl * H * 2];
+        l[u] = ml[(size_t)sl * H * 2 + 1];
+        z[u] = *reinterpret_cast<const half8*>(zb + (size_t)sl * zs);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      float cm = M;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        m[u] = c + u < s1 ? m[u] : -INFINITY;
+        cm = fmaxf(cm, m[u]);
+      }
+      const float sc = fast_exp2(M - cm);
+      a0 *= sc;
+      a1 *= sc;
+      den *= sc;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wgt = fast_exp2(m[u] - cm) * l[u];
+        a0 += wgt * floatx4{(float)z[u][0], (float)z[u][1], (float)z[u][2], (float)z[u][3]};
+        a1 += wgt * floatx4{(float)z[u][4], (float)z[u][5], (float)z[u][6], (float)z[u][7]};
+        den += wgt;
+      }
+      M = cm;
+    }
+  };
+  if (n <= 4)
+    run(std::integral_constant<int, 4>{});
+  else
+    run(std::integral_constant<int, 8>{});
+  if (live) {
+    const float inv = 1.f / den;
+    store_z4(zrow + d, a0 * inv);
+    store_z4(zrow + d + 4, a1 * inv);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 4. per-head up-projection by B_v
 // ---------------------------------------------------------------------------
@@ -916,7 +996,17 @@ hipError_t launch_merge(const Shape& s, int rows, const void* pz, const float* p
   // few (row, head) pairs -> long sequences split into many ranges
   const bool few = (long long)rows * s.H < 512;
   const dim3 grid(rows * s.H * (few ? (s.RV + 255) / 256 : (s.RV + 1023) / 1024));
-  if (z16 && zout16) {
+  if (z16 && zout16 && !few && s.RV <= 1024 && s.RV % 8 == 0) {
+    const f16* z = static_cast<const f16*>(pz);
+    f16* o = static_cast<f16*>(zf);
+    const long long pairs = (long long)rows * s.H;
+    if (s.RV <= 512)
+      hipLaunchKernelGGL((merge_wide_kernel<64, f16>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, z, pml,
+                         plan, lens, rows, s.H, s.RV, o);
+    else
+      hipLaunchKernelGGL((merge_wide_kernel<128, f16>), dim3((unsigned)((pairs + 1) / 2)), dim3(256), 0, st, z, pml,
+                         plan, lens, rows, s.H, s.RV, o);
+  } else if (z16 && zout16) {
     const f16* z = static_cast<const f16*>(pz);
     f16* o = static_cast<f16*>(zf);
     if (few)
