@@ -199,8 +199,8 @@ starkv_status starkv_decode_step(const starkv_dims* dims, int32_t batch, int32_t
  *
  *   A call whose workspace (carved for its actual launch grid) would exceed
  *   the scratch returns STARKV_ERR_WORKSPACE and enqueues nothing.  At 32
- *   heads and r_v = 1024 that is about 64 KiB * (256 + batch) + 136 KiB *
- *   batch on a 256-CU GPU, so batches up to about 240 fit; use starkv_decode
+ *   heads and r_v = 1024 that is about 64 KiB * (256 + batch) + 72 KiB *
+ *   batch on a 256-CU GPU, so batches up to about 360 fit; use starkv_decode
  *   with a caller workspace beyond that.
  *   Nothing in the scratch needs to start at zero; every call overwrites what
  *   it reads.  All calls on one GPU share that GPU's scratch: two calls whose

@@ -13,7 +13,7 @@
 //                   each (range, sequence) pair leaves a partial state: max m
 //                   and sum l in fp32, z / l in fp16.
 //   3. merge        log-sum-exp merge of a sequence's partials -> Z [B][H][r_v],
-//                   rounded to fp16 (fp32 for the many-row up-projection).
+//                   rounded once to fp16.
 //   4. upproj       out[b,h] = Z[b,h] . B_v[:, h*d:(h+1)*d]  (MFMA at batch >= 16).
 // With few (sequence, head) pairs at d = 64 or 128, launches 3 and 4 are one
 // launch (merge_upproj_small) that keeps Z in LDS.
@@ -304,10 +304,8 @@ __device__ __forceinline__ void merge_slots(const float* __restrict__ ml, const 
   }
 }
 
-// Four merged latents of one row: fp32 (prefill, and the many-row
-// up-projection) or rounded once to fp16 (decode's MFMA and VALU
-// up-projections take the fp16 row as their A operand).
-__device__ __forceinline__ void store_z4(float* p, floatx4 v) { *reinterpret_cast<floatx4*>(p) = v; }
+// Four merged latents of one row, rounded once to fp16: every up-projection
+// takes the fp16 row as its MFMA A operand (or VALU factor).
 __device__ __forceinline__ void store_z4(f16* p, floatx4 v) {
   *reinterpret_cast<half4*>(p) = half4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
 }
@@ -316,12 +314,12 @@ __device__ __forceinline__ void store_z4(f16* p, floatx4 v) {
 // W slot groups (W = 1 or 4) each take every W-th slot, up to sixteen slots per
 // memory round trip, merge them online and combine through LDS.  W = 4 when
 // the launch has few workgroups (long sequences split into many ranges).
-// ZT: the partial states' z type; OT: the merged row's type.
-template <int W, typename ZT, typename OT>
+// ZT: the partial states' z type (fp16 z / l in decode, fp32 z in prefill).
+template <int W, typename ZT>
 __global__ void __launch_bounds__(256)
 merge_kernel(const ZT* __restrict__ part_z, const float* __restrict__ part_ml,
              const int32_t* __restrict__ plan, const int32_t* __restrict__ lens,
-             int batch, int H, int RV, OT* __restrict__ zf) {
+             int batch, int H, int RV, f16* __restrict__ zf) {
   constexpr int kLanes = 256 / W;                   // threads per slot group
   constexpr int kDims = 4 * kLanes;                 // latent dims per workgroup
   __shared__ floatx4 ca[W][kLanes];
@@ -334,7 +332,7 @@ merge_kernel(const ZT* __restrict__ part_z, const float* __restrict__ part_ml,
   const int b = blockIdx.x / (dchunks * H);
   const int d = dc * kDims + li * 4;
   const bool live = d < RV;
-  OT* zrow = zf + ((size_t)b * H + h) * RV;
+  f16* zrow = zf + ((size_t)b * H + h) * RV;
   const PlanView pv{plan, batch};
   const int s0 = pv.slot_base()[b];
   const int s1 = pv.slot_base()[b + 1];
@@ -389,11 +387,11 @@ merge_kernel(const ZT* __restrict__ part_z, const float* __restrict__ part_ml,
 // and a wave instruction reads 1 KiB of a slot.  The online log-sum-exp of
 // merge_slots, at most eight slots per memory round trip (80 VGPRs, six waves
 // per SIMD: every workgroup of a 64 x 32-head decode is resident at once).
-template <int TP, typename OT>
+template <int TP>
 __global__ void __launch_bounds__(256)
 merge_wide_kernel(const f16* __restrict__ part_z, const float* __restrict__ part_ml,
                   const int32_t* __restrict__ plan, const int32_t* __restrict__ lens,
-                  int batch, int H, int RV, OT* __restrict__ zf) {
+                  int batch, int H, int RV, f16* __restrict__ zf) {
   constexpr int PPW = 256 / TP;
   const int li = threadIdx.x % TP;
   const long long pair = (long long)blockIdx.x * PPW + threadIdx.x / TP;
@@ -402,7 +400,7 @@ merge_wide_kernel(const f16* __restrict__ part_z, const float* __restrict__ part
   const int b = (int)(pair / H);
   const int d = li * 8;
   const bool live = d < RV;
-  OT* zrow = zf + (size_t)pair * RV;
+  f16* zrow = zf + (size_t)pair * RV;
   const PlanView pv{plan, batch};
   const int s0 = pv.slot_base()[b];
   const int s1 = pv.slot_base()[b + 1];
@@ -470,20 +468,17 @@ merge_wide_kernel(const f16* __restrict__ part_z, const float* __restrict__ part
 // MFMA path: a workgroup computes a [32 batch x 32 dims] tile of one head; its
 // eight waves split r_v and reduce through LDS.  B_v is stored dims-contiguous,
 // so each wave reads its [r_v/8 x 32] slice of B_v with coalesced 16-byte row
-// loads and transposes it through LDS into k-contiguous MFMA fragments.  An
-// fp32 Z (ZT = float) enters the f16 MFMA as a hi + lo pair, so the product
-// keeps ~22 bits of Z; an fp16 Z (ZT = f16, decode) is the A fragment itself,
-// one 16-byte load and one MFMA per k-step.  All global loads are in flight
-// before the first MFMA.
+// loads and transposes it through LDS into k-contiguous MFMA fragments.  The
+// fp16 Z row is the A fragment itself: one 16-byte load and one MFMA per
+// k-step.  All global loads are in flight before the first MFMA.
 constexpr int kUpWaves = 8;
 constexpr int kUpMaxSpan = 128;          // r_v / kUpWaves <= 128 (r_v <= 1024)
 constexpr int kUpPad = 8;
 
-template <int NS, typename ZT>           // NS = r_v / (16 * kUpWaves) k-steps per wave
+template <int NS>                        // NS = r_v / (16 * kUpWaves) k-steps per wave
 __global__ void __launch_bounds__(kUpWaves * 64)
-upproj_mfma_kernel(const ZT* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
+upproj_mfma_kernel(const f16* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
                    int batch, int H, int KV, int D) {
-  constexpr bool kZ16 = sizeof(ZT) == 2;
   constexpr int RV = NS * 16 * kUpWaves;
   constexpr int kspan = NS * 16;
   __shared__ __attribute__((aligned(16))) f16 bt[kUpWaves][32][kspan + kUpPad];
@@ -509,19 +504,13 @@ upproj_mfma_kernel(const ZT* __restrict__ zf, const f16* __restrict__ bv, f16* _
   const int kbase = w * kspan;
   // B_v slice rows kbase.., 32 dims from h*D + nt*32: lane -> (row l/4, 8 dims)
   const f16* bsrc = bv + (size_t)(kbase + (lane >> 2)) * ld + (size_t)kvh * D + nt * 32 + (lane & 3) * 8;
-  const ZT* zrow = zf + ((size_t)(brow ? b : batch - 1) * H + h) * RV + kbase + kofs;
+  const f16* zrow = zf + ((size_t)(brow ? b : batch - 1) * H + h) * RV + kbase + kofs;
   half8 braw[NS];
-  floatx4 za[kZ16 ? 1 : NS][2];
-  half8 zh[kZ16 ? NS : 1];
+  half8 zh[NS];
 #pragma unroll
   for (int u = 0; u < NS; ++u) {
     braw[u] = *reinterpret_cast<const half8*>(bsrc + (size_t)u * 16 * ld);
-    if constexpr (kZ16) {
-      zh[u] = *reinterpret_cast<const half8*>(zrow + u * 16);
-    } else {
-      za[u][0] = *reinterpret_cast<const floatx4*>(zrow + u * 16);
-      za[u][1] = *reinterpret_cast<const floatx4*>(zrow + u * 16 + 4);
-    }
+    zh[u] = *reinterpret_cast<const half8*>(zrow + u * 16);
   }
   __builtin_amdgcn_sched_barrier(0);     // every load in flight before the first LDS write
   f16 (*tw)[kspan + kUpPad] = bt[w];
@@ -533,19 +522,7 @@ upproj_mfma_kernel(const ZT* __restrict__ zf, const f16* __restrict__ bv, f16* _
 #pragma unroll
   for (int u = 0; u < NS; ++u) {
     const half8 bb = *reinterpret_cast<const half8*>(&tw[lane & 31][u * 16 + kofs]);
-    if constexpr (kZ16) {
-      acc = mfma32x32x16(brow ? zh[u] : half8{}, bb, acc);
-    } else {
-      half8 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float z = brow ? za[u][e >> 2][e & 3] : 0.f;
-        hi[e] = (f16)z;
-        lo[e] = (f16)(z - (float)hi[e]);
-      }
-      acc = mfma32x32x16(hi, bb, acc);
-      acc = mfma32x32x16(lo, bb, acc);
-    }
+    acc = mfma32x32x16(brow ? zh[u] : half8{}, bb, acc);
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) red[w][r][lane] = acc[r];
@@ -568,25 +545,24 @@ upproj_mfma_kernel(const ZT* __restrict__ zf, const f16* __restrict__ bv, f16* _
 // latent dims; per span both operands are staged in LDS with every load of a
 // thread issued before its first LDS write, and the next span's loads are in
 // flight while this span's MFMAs run:
-//   Z   [64 rows x 128] fp32, coalesced (a wave instruction reads 512 B of
-//       each of two rows); A fragments are split into fp16 hi + lo on the way
-//       to the MFMA;
+//   Z   [64 rows x 128] fp16, coalesced (a wave instruction reads the 256 B
+//       span of each of four rows); an A fragment is one 16-byte LDS read;
 //   B_v [128 x 128 dims] transposed to [128 dims][128] so each lane's B
 //       fragment (8 consecutive k of one output dim) is one 16-byte LDS read.
 //       A thread packs two adjacent k of one dim into a dword, so a wave
 //       writes consecutive dwords of one LDS row (no bank conflicts).
 constexpr int kUpRowsTile = 64;
 constexpr int kUpRowsSpan = 128;         // latent dims staged at once (two workgroups fit a CU's LDS)
-constexpr int kUpRowsPad = 4;            // LDS row padding (floats / dwords)
+constexpr int kUpRowsPad = 4;            // LDS row padding (dwords)
 
 __global__ void __launch_bounds__(512)
-upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
+upproj_rows_kernel(const f16* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
                    int rows, int H, int KV, int RV) {
   constexpr int D = 128;
   constexpr int BRow = kUpRowsSpan / 2 + kUpRowsPad;     // dwords
-  constexpr int ZRow = kUpRowsSpan + kUpRowsPad;         // floats
+  constexpr int ZRow = kUpRowsSpan + 2 * kUpRowsPad;     // halves
   __shared__ __attribute__((aligned(16))) uint32_t bt[D][BRow];
-  __shared__ __attribute__((aligned(16))) float zl[kUpRowsTile][ZRow];
+  __shared__ __attribute__((aligned(16))) f16 zl[kUpRowsTile][ZRow];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int rtiles = (rows + kUpRowsTile - 1) / kUpRowsTile;
@@ -604,10 +580,10 @@ upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
   static_assert(512 / kPairs * kNPer == D && kNPer % 8 == 0, "B_v staging covers the tile");
   const int kp = threadIdx.x % kPairs, sn = (threadIdx.x / kPairs) * kNPer;
   const f16* bsrc = bv + (size_t)(2 * kp) * ld + (size_t)kvh * D + sn;
-  constexpr int kZPieces = kUpRowsTile * kUpRowsSpan / 4 / 512;   // 16-byte Z pieces per thread
+  constexpr int kZPieces = kUpRowsTile * kUpRowsSpan / 8 / 512;   // 16-byte Z pieces per thread
   floatx16 acc = {};
   half8 braw[2][kNPer / 8];
-  floatx4 zv[kZPieces];
+  half8 zv[kZPieces];
   // Z is read exactly once: non-temporal loads keep it from evicting the
   // B_v slices that the head's other row tiles re-read from L2
   auto load_span = [&](int k0) {
@@ -619,10 +595,10 @@ upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
 #pragma unroll
     for (int i = 0; i < kZPieces; ++i) {
       const int f = i * 512 + threadIdx.x;
-      const int r = f / (kUpRowsSpan / 4), c4 = (f % (kUpRowsSpan / 4)) * 4;
-      zv[i] = row0 + r < rows ? __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(
-                                    zf + ((size_t)(row0 + r) * H + h) * RV + k0 + c4))
-                              : floatx4{};
+      const int r = f / (kUpRowsSpan / 8), c8 = (f % (kUpRowsSpan / 8)) * 8;
+      zv[i] = row0 + r < rows ? __builtin_nontemporal_load(reinterpret_cast<const half8*>(
+                                    zf + ((size_t)(row0 + r) * H + h) * RV + k0 + c8))
+                              : half8{};
     }
   };
   load_span(0);
@@ -631,8 +607,8 @@ upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
 #pragma unroll
     for (int i = 0; i < kZPieces; ++i) {
       const int f = i * 512 + threadIdx.x;
-      const int r = f / (kUpRowsSpan / 4), c4 = (f % (kUpRowsSpan / 4)) * 4;
-      *reinterpret_cast<floatx4*>(&zl[r][c4]) = zv[i];
+      const int r = f / (kUpRowsSpan / 8), c8 = (f % (kUpRowsSpan / 8)) * 8;
+      *reinterpret_cast<half8*>(&zl[r][c8]) = zv[i];
     }
     // dims 2e, 2e+1 of a loaded row sit in dword e of its half8 (low, high
     // half); the LDS dword of dim n pairs k = 2kp (low) with k = 2kp+1 (high)
@@ -648,23 +624,14 @@ upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
     }
     __syncthreads();
     if (k0 + kUpRowsSpan < RV) load_span(k0 + kUpRowsSpan);   // in flight during this span's MFMAs
-    const float* za = &zl[rt * 32 + (lane & 31)][(lane >> 5) * 8];
+    const f16* za = &zl[rt * 32 + (lane & 31)][(lane >> 5) * 8];
     const uint32_t* brow = &bt[nt * 32 + (lane & 31)][(lane >> 5) * 4];
 #pragma unroll
     for (int u = 0; u < kUpRowsSpan / 16; ++u) {
       // read back through the type it was written with (uint32), then reinterpret
       const half8 bb = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(brow + u * 8));
-      const floatx4 z0 = *reinterpret_cast<const floatx4*>(za + u * 16);
-      const floatx4 z1 = *reinterpret_cast<const floatx4*>(za + u * 16 + 4);
-      half8 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float zz = e < 4 ? z0[e] : z1[e - 4];
-        hi[e] = (f16)zz;
-        lo[e] = (f16)(zz - (float)hi[e]);
-      }
-      acc = mfma32x32x16(hi, bb, acc);
-      acc = mfma32x32x16(lo, bb, acc);
+      const half8 zh = *reinterpret_cast<const half8*>(za + u * 16);
+      acc = mfma32x32x16(zh, bb, acc);
     }
   }
   const int n = nt * 32 + (lane & 31);
@@ -683,9 +650,8 @@ upproj_rows_kernel(const float* __restrict__ zf, const f16* __restrict__ bv, f16
 constexpr int kSmallBatch = 16;
 constexpr int kUpvMaxRV = 1024;
 
-template <typename ZT>                   // merged rows in fp32 (prefill) or fp16 (decode)
 __global__ void __launch_bounds__(256)
-upproj_valu_kernel(const ZT* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
+upproj_valu_kernel(const f16* __restrict__ zf, const f16* __restrict__ bv, f16* __restrict__ out,
                    int batch, int H, int KV, int D, int RV) {
   __shared__ __attribute__((aligned(16))) float zl[kSmallBatch][kUpvMaxRV];
   __shared__ float red[64][4][33];
@@ -716,13 +682,8 @@ upproj_valu_kernel(const ZT* __restrict__ zf, const f16* __restrict__ bv, f16* _
       const int idx = t + 256 * i;
       const int r = idx / (RV / 4), c = idx % (RV / 4);
       if (idx < rows * (RV / 4)) {
-        const ZT* src = zf + ((size_t)(row0 + r) * H + h) * RV + c * 4;
-        if constexpr (sizeof(ZT) == 2) {
-          const half4 zz = *reinterpret_cast<const half4*>(src);
-          zv[i] = floatx4{(float)zz[0], (float)zz[1], (float)zz[2], (float)zz[3]};
-        } else {
-          zv[i] = *reinterpret_cast<const floatx4*>(src);
-        }
+        const half4 zz = *reinterpret_cast<const half4*>(zf + ((size_t)(row0 + r) * H + h) * RV + c * 4);
+        zv[i] = floatx4{(float)zz[0], (float)zz[1], (float)zz[2], (float)zz[3]};
       } else {
         zv[i] = floatx4{};
       }
@@ -964,8 +925,8 @@ DecodeLayout decode_layout(const Shape& s, int batch, int max_context_len, int g
   off = align256(off + sizeof(float) * (size_t)L.max_slots * s.H * 2);
   L.off_z = off;                                    // z / l in fp16
   off = align256(off + sizeof(f16) * (size_t)L.max_slots * s.H * s.RV);
-  L.off_zf = off;
-  off = align256(off + sizeof(float) * (size_t)batch * s.H * s.RV);
+  L.off_zf = off;                                   // merged rows in fp16
+  off = align256(off + sizeof(f16) * (size_t)batch * s.H * s.RV);
   L.bytes = off;
   return L;
 }
@@ -992,95 +953,60 @@ hipError_t launch_qproj(const Shape& s, int rows, const void* q, const void* b_k
 }
 
 hipError_t launch_merge(const Shape& s, int rows, const void* pz, const float* pml, const int32_t* plan,
-                        const int32_t* lens, void* zf, hipStream_t st, bool z16, bool zout16) {
+                        const int32_t* lens, f16* zf, hipStream_t st, bool z16) {
   // few (row, head) pairs -> long sequences split into many ranges
   const bool few = (long long)rows * s.H < 512;
   const dim3 grid(rows * s.H * (few ? (s.RV + 255) / 256 : (s.RV + 1023) / 1024));
-  if (z16 && zout16 && !few && s.RV <= 1024 && s.RV % 8 == 0) {
+  if (z16 && !few && s.RV <= 1024 && s.RV % 8 == 0) {
     const f16* z = static_cast<const f16*>(pz);
-    f16* o = static_cast<f16*>(zf);
     const long long pairs = (long long)rows * s.H;
     if (s.RV <= 512)
-      hipLaunchKernelGGL((merge_wide_kernel<64, f16>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, z, pml,
-                         plan, lens, rows, s.H, s.RV, o);
+      hipLaunchKernelGGL(merge_wide_kernel<64>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, z, pml, plan,
+                         lens, rows, s.H, s.RV, zf);
     else
-      hipLaunchKernelGGL((merge_wide_kernel<128, f16>), dim3((unsigned)((pairs + 1) / 2)), dim3(256), 0, st, z, pml,
-                         plan, lens, rows, s.H, s.RV, o);
-  } else if (z16 && zout16) {
-    const f16* z = static_cast<const f16*>(pz);
-    f16* o = static_cast<f16*>(zf);
-    if (few)
-      hipLaunchKernelGGL((merge_kernel<4, f16, f16>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, o);
-    else
-      hipLaunchKernelGGL((merge_kernel<1, f16, f16>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, o);
+      hipLaunchKernelGGL(merge_wide_kernel<128>, dim3((unsigned)((pairs + 1) / 2)), dim3(256), 0, st, z, pml, plan,
+                         lens, rows, s.H, s.RV, zf);
   } else if (z16) {
     const f16* z = static_cast<const f16*>(pz);
-    float* o = static_cast<float*>(zf);
     if (few)
-      hipLaunchKernelGGL((merge_kernel<4, f16, float>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, o);
+      hipLaunchKernelGGL((merge_kernel<4, f16>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, zf);
     else
-      hipLaunchKernelGGL((merge_kernel<1, f16, float>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, o);
+      hipLaunchKernelGGL((merge_kernel<1, f16>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, zf);
   } else {
-    if (zout16) return hipErrorInvalidValue;       // fp32 partials are merged for the fp32 paths only
     const float* z = static_cast<const float*>(pz);
-    float* o = static_cast<float*>(zf);
     if (few)
-      hipLaunchKernelGGL((merge_kernel<4, float, float>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, o);
+      hipLaunchKernelGGL((merge_kernel<4, float>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, zf);
     else
-      hipLaunchKernelGGL((merge_kernel<1, float, float>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, o);
+      hipLaunchKernelGGL((merge_kernel<1, float>), grid, dim3(256), 0, st, z, pml, plan, lens, rows, s.H, s.RV, zf);
   }
   return hipGetLastError();
 }
 
-static bool upproj_rows_path(const Shape& s, int rows) {
-  return rows >= 256 && s.D == 128 && s.RV % kUpRowsSpan == 0;
-}
-
-bool upproj_accepts_z16(const Shape& s, int rows) { return !upproj_rows_path(s, rows); }
-
-template <typename ZT>
-static void launch_upproj_mfma(const Shape& s, int rows, const ZT* zf, const f16* bv, f16* o, int grid,
-                               hipStream_t st) {
-  const dim3 g(grid), b(kUpWaves * 64);
-  switch (s.RV / (16 * kUpWaves)) {
-    case 1: hipLaunchKernelGGL((upproj_mfma_kernel<1, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-    case 2: hipLaunchKernelGGL((upproj_mfma_kernel<2, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-    case 3: hipLaunchKernelGGL((upproj_mfma_kernel<3, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-    case 4: hipLaunchKernelGGL((upproj_mfma_kernel<4, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-    case 5: hipLaunchKernelGGL((upproj_mfma_kernel<5, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-    case 6: hipLaunchKernelGGL((upproj_mfma_kernel<6, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-    case 7: hipLaunchKernelGGL((upproj_mfma_kernel<7, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-    default: hipLaunchKernelGGL((upproj_mfma_kernel<8, ZT>), g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
-  }
-}
-
-hipError_t launch_upproj(const Shape& s, int rows, const void* zf, bool z16, const void* b_v, void* out,
-                         hipStream_t st) {
+hipError_t launch_upproj(const Shape& s, int rows, const f16* zf, const void* b_v, void* out, hipStream_t st) {
   const f16* bv = static_cast<const f16*>(b_v);
   f16* o = static_cast<f16*>(out);
-  if (upproj_rows_path(s, rows)) {
-    if (z16) return hipErrorInvalidValue;
+  if (rows >= 256 && s.D == 128 && s.RV % kUpRowsSpan == 0) {
     const int rtiles = (rows + kUpRowsTile - 1) / kUpRowsTile;
     const int grid = rtiles * ((s.H + 7) / 8) * 8;
-    hipLaunchKernelGGL(upproj_rows_kernel, dim3(grid), dim3(512), 0, st, static_cast<const float*>(zf), bv, o, rows,
-                       s.H, s.KV, s.RV);
+    hipLaunchKernelGGL(upproj_rows_kernel, dim3(grid), dim3(512), 0, st, zf, bv, o, rows, s.H, s.KV, s.RV);
     return hipGetLastError();
   }
   if (rows >= kSmallBatch && s.D % 32 == 0 && s.RV % (16 * kUpWaves) == 0 && s.RV <= kUpWaves * kUpMaxSpan) {
     const int groups = ((rows + 31) / 32) * s.H;
-    const int grid = ((groups + 7) / 8) * 8 * (s.D / 32);
-    if (z16)
-      launch_upproj_mfma(s, rows, static_cast<const f16*>(zf), bv, o, grid, st);
-    else
-      launch_upproj_mfma(s, rows, static_cast<const float*>(zf), bv, o, grid, st);
+    const dim3 g(((groups + 7) / 8) * 8 * (s.D / 32)), b(kUpWaves * 64);
+    switch (s.RV / (16 * kUpWaves)) {
+      case 1: hipLaunchKernelGGL(upproj_mfma_kernel<1>, g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+      case 2: hipLaunchKernelGGL(upproj_mfma_kernel<2>, g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+      case 3: hipLaunchKernelGGL(upproj_mfma_kernel<3>, g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+      case 4: hipLaunchKernelGGL(upproj_mfma_kernel<4>, g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+      case 5: hipLaunchKernelGGL(upproj_mfma_kernel<5>, g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+      case 6: hipLaunchKernelGGL(upproj_mfma_kernel<6>, g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+      case 7: hipLaunchKernelGGL(upproj_mfma_kernel<7>, g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+      default: hipLaunchKernelGGL(upproj_mfma_kernel<8>, g, b, 0, st, zf, bv, o, rows, s.H, s.KV, s.D); break;
+    }
   } else {
     const dim3 grid(s.H * ((s.D + 31) / 32), (rows + kSmallBatch - 1) / kSmallBatch);
-    if (z16)
-      hipLaunchKernelGGL(upproj_valu_kernel<f16>, grid, dim3(256), 0, st, static_cast<const f16*>(zf), bv, o, rows,
-                         s.H, s.KV, s.D, s.RV);
-    else
-      hipLaunchKernelGGL(upproj_valu_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(zf), bv, o,
-                         rows, s.H, s.KV, s.D, s.RV);
+    hipLaunchKernelGGL(upproj_valu_kernel, grid, dim3(256), 0, st, zf, bv, o, rows, s.H, s.KV, s.D, s.RV);
   }
   return hipGetLastError();
 }
@@ -1136,7 +1062,7 @@ static hipError_t decode_after_prologue(const DecodeLaunch& a) {
   float* qt = reinterpret_cast<float*>(a.ws + a.lay.off_qt);
   float* pml = reinterpret_cast<float*>(a.ws + a.lay.off_ml);
   f16* pz = reinterpret_cast<f16*>(a.ws + a.lay.off_z);
-  float* zf = reinterpret_cast<float*>(a.ws + a.lay.off_zf);
+  f16* zf = reinterpret_cast<f16*>(a.ws + a.lay.off_zf);
 
   // 2. latent attention (timed by its own dispatch when events are given)
   hipError_t err = launch_attn_kernel(a, qt, plan, pz, pml);
@@ -1150,11 +1076,9 @@ static hipError_t decode_after_prologue(const DecodeLaunch& a) {
                        static_cast<const f16*>(a.b_v), static_cast<f16*>(a.out), a.batch, s.H, s.KV, s.RV);
     return hipGetLastError();
   }
-  // merged rows in fp16 wherever the up-projection takes them
-  const bool z16 = upproj_accepts_z16(s, a.batch);
-  err = launch_merge(s, a.batch, pz, pml, plan, a.context_lens, zf, a.stream, true, z16);
+  err = launch_merge(s, a.batch, pz, pml, plan, a.context_lens, zf, a.stream, true);
   if (err != hipSuccess) return err;
-  return launch_upproj(s, a.batch, zf, z16, a.b_v, a.out, a.stream);
+  return launch_upproj(s, a.batch, zf, a.b_v, a.out, a.stream);
 }
 
 hipError_t decode_enqueue(const DecodeLaunch& a) {

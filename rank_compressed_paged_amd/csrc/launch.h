@@ -108,18 +108,12 @@ hipError_t table_check_enqueue(const int32_t* block_tables, const int32_t* conte
 hipError_t launch_qproj(const Shape& s, int rows, const void* q, const void* b_k, float scale2, float* qt,
                         const int32_t* plan_lens, int plan_grid, int32_t* plan, hipStream_t st);
 // Log-sum-exp merge of each row's partial slots (slot_base at plan + 3 + rows;
-// rows with lens[row] == 0 give zeros).  z16: the partial z are z / l in fp16
-// (decode); else unnormalised z in fp32 (prefill).  zout16: the merged rows
-// are written in fp16, else fp32.
+// rows with lens[row] == 0 give zeros) into fp16 merged rows zf.  z16: the
+// partial z are z / l in fp16 (decode); else unnormalised z in fp32 (prefill).
 hipError_t launch_merge(const Shape& s, int rows, const void* pz, const float* pml, const int32_t* plan,
-                        const int32_t* lens, void* zf, hipStream_t st, bool z16, bool zout16);
-// Whether launch_upproj can take fp16 merged rows for `rows` rows (every path
-// but the many-row one, which stages fp32 rows).
-bool upproj_accepts_z16(const Shape& s, int rows);
-// out[row, h] = zf[row, h] . B_v[:, g(h)*d : (g(h)+1)*d]; zf fp16 when z16
-// (only where upproj_accepts_z16), else fp32
-hipError_t launch_upproj(const Shape& s, int rows, const void* zf, bool z16, const void* b_v, void* out,
-                         hipStream_t st);
+                        const int32_t* lens, _Float16* zf, hipStream_t st, bool z16);
+// out[row, h] = zf[row, h] . B_v[:, g(h)*d : (g(h)+1)*d], zf in fp16
+hipError_t launch_upproj(const Shape& s, int rows, const _Float16* zf, const void* b_v, void* out, hipStream_t st);
 
 // The latent attention launch (one kernel; qt, plan, pz, pml live in a.ws).
 // Partial states: pz holds z / l in fp16, pml (m, l) in fp32.

@@ -242,7 +242,7 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
                     const int32_t* __restrict__ block_tables, int mb_stride, const int32_t* __restrict__ qs,
                     const int32_t* __restrict__ lens, const int32_t* __restrict__ plan, int rows, int tile_cap,
                     int H, int G, int HKV, float* __restrict__ part_z, float* __restrict__ part_ml,
-                    float* __restrict__ zdirect, float tau) {
+                    f16* __restrict__ zdirect, float tau) {
   using C = PfCfg<RK, RV>;
   // P, rescale factors and rescale flags of three blocks in flight: scores
   // run two blocks ahead of the z accumulation
@@ -614,7 +614,7 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
 
     if (zdirect) {
       // Every row's context fits one range: write z / l straight into the
-      // merged buffer (no partial state, no merge pass).
+      // merged buffer, rounded once to fp16 (no partial state, no merge pass).
       if (scorer) {
         const float l_row = row_sum();
         if (lane < 16) lrow_lds[srow] = l_row;
@@ -628,9 +628,9 @@ prefill_attn_kernel(const float* __restrict__ qt, const f16* __restrict__ q, con
           const int rr = rt * 32 + (r & 3) + 8 * (r >> 2) + rlane;     // mfma_row(r, lane)
           if (rr < nrows) {
             const float inv = 1.f / lrow_lds[rr];
-            float* zp = zdirect + ((size_t)(row0 + rr) * H + h) * RV + w * C::TPW * 32 + c32;
+            f16* zp = zdirect + ((size_t)(row0 + rr) * H + h) * RV + w * C::TPW * 32 + c32;
 #pragma unroll
-            for (int t = 0; t < C::TPW; ++t) zp[t * 32] = acc[rt][t][r] * inv;
+            for (int t = 0; t < C::TPW; ++t) zp[t * 32] = (f16)(acc[rt][t][r] * inv);
           }
         }
       __syncthreads();                       // LDS is reused by the next item
@@ -708,15 +708,15 @@ PrefillLayout prefill_layout(const Shape& s, int batch, int rows, int max_contex
   off = pf_align256(off + sizeof(float) * (size_t)L.max_slots * s.H * 2);
   L.off_z = off;
   off = pf_align256(off + sizeof(float) * (size_t)L.max_slots * s.H * s.RV);
-  L.off_zf = off;
-  off = pf_align256(off + sizeof(float) * (size_t)rows * s.H * s.RV);
+  L.off_zf = off;                                   // merged rows in fp16
+  off = pf_align256(off + sizeof(f16) * (size_t)rows * s.H * s.RV);
   L.bytes = off;
   return L;
 }
 
 template <int RK, int RV>
 static hipError_t launch_pf_attn(const PrefillLaunch& a, const float* qt, float scale2, const int32_t* plan, float* pz,
-                                 float* pml, float* zdirect, int device) {
+                                 float* pml, f16* zdirect, int device) {
   const auto kernel = prefill_attn_kernel<RK, RV>;
   static std::atomic<int> resident[64];
   int res = (device >= 0 && device < 64) ? resident[device].load(std::memory_order_relaxed) : 0;
@@ -746,7 +746,7 @@ hipError_t prefill_enqueue(const PrefillLaunch& a, int device) {
   float* qt = reinterpret_cast<float*>(a.ws + a.lay.off_qt);
   float* pml = reinterpret_cast<float*>(a.ws + a.lay.off_ml);
   float* pz = reinterpret_cast<float*>(a.ws + a.lay.off_z);
-  float* zf = reinterpret_cast<float*>(a.ws + a.lay.off_zf);
+  f16* zf = reinterpret_cast<f16*>(a.ws + a.lay.off_zf);
 
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(256), 0, a.stream, a.query_start, a.context_lens, a.batch,
                      a.rows, a.lay.range_blocks, a.lay.tile_cap, plan);
@@ -762,7 +762,7 @@ hipError_t prefill_enqueue(const PrefillLaunch& a, int device) {
 
   err = hipErrorInvalidValue;
   // one context range for every row: the attention kernel writes Z itself
-  float* zdirect = a.lay.max_ranges == 1 ? zf : nullptr;
+  f16* zdirect = a.lay.max_ranges == 1 ? zf : nullptr;
 #define X(rk, rv) \
   if (s.RK == rk && s.RV == rv)                                                                           \
     err = launch_pf_attn<rk, rv>(a, qproj_fused ? nullptr : qt, scale2, plan, pz, pml, zdirect, device);
@@ -772,10 +772,10 @@ hipError_t prefill_enqueue(const PrefillLaunch& a, int device) {
 
   if (!zdirect) {
     const PrefillPlan P{plan, a.rows, a.lay.tile_cap};
-    err = launch_merge(s, a.rows, pz, pml, plan, P.row_len_w(), zf, a.stream, false, false);
+    err = launch_merge(s, a.rows, pz, pml, plan, P.row_len_w(), zf, a.stream, false);
     if (err != hipSuccess) return err;
   }
-  return launch_upproj(s, a.rows, zf, false, a.b_v, a.out, a.stream);
+  return launch_upproj(s, a.rows, zf, a.b_v, a.out, a.stream);
 }
 
 }  // namespace starkv

@@ -174,7 +174,7 @@ def test_prefill_workspace_size(lib):
     f = lib.starkv_prefill_workspace_size
     a = f(ctypes.byref(d), 4, 2048, 8192)
     assert a > 0 and a % 256 == 0
-    # q~ and the merged latent rows alone: rows * H * (r_k + r_v) fp32
+    # q~ (fp32) and one fp32 partial state per row alone: rows * H * (r_k + r_v) * 4 bytes
     assert a >= 2048 * 32 * (64 + 1024) * 4
     assert f(ctypes.byref(d), 4, 512, 8192) < a
     assert f(ctypes.byref(d), 0, 512, 8192) == 0
