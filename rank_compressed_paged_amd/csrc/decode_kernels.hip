@@ -549,8 +549,10 @@ upproj_mfma_kernel(const f16* __restrict__ zf, const f16* __restrict__ bv, f16* 
 //       span of each of four rows); an A fragment is one 16-byte LDS read;
 //   B_v [128 x 128 dims] transposed to [128 dims][128] so each lane's B
 //       fragment (8 consecutive k of one output dim) is one 16-byte LDS read.
-//       A thread packs two adjacent k of one dim into a dword, so a wave
-//       writes consecutive dwords of one LDS row (no bank conflicts).
+//       A wave instruction reads 128 contiguous bytes of each of 8 B_v rows
+//       (16 bytes from each of 64 rows took 1.5x as long); a thread packs two
+//       adjacent k of one dim into a dword, stored at a column swizzled by
+//       the dim group so that the writes do not collide in the LDS banks.
 constexpr int kUpRowsTile = 64;
 constexpr int kUpRowsSpan = 128;         // latent dims staged at once (two workgroups fit a CU's LDS)
 constexpr int kUpRowsPad = 4;            // LDS row padding (dwords)
@@ -574,12 +576,17 @@ upproj_rows_kernel(const f16* __restrict__ zf, const f16* __restrict__ bv, f16* 
   const size_t ld = (size_t)KV * D;
   const int rt = w & 1, nt = w >> 1;
   const int row0 = rtile * kUpRowsTile;
-  // B_v staging: thread t takes latent rows 2*(t%P), 2*(t%P)+1 of the span
-  // (P = span/2 pairs) and output dims (span/8)*(t/P) .. +span/8-1
+  // B_v staging: thread t takes latent rows 2*(t/8), 2*(t/8)+1 of the span
+  // and output dims 8*(t%8) + 64*i .. +7 (i = 0, 1), so a wave instruction
+  // reads 128 contiguous bytes of each of 8 rows.  In LDS the dword of
+  // (dim n, k pair kp) sits at column kp ^ 4*((n/8)%8): the eight dim groups
+  // of one instruction's writes then land in distinct banks (checked on the
+  // CPU: conflict-free writes, reads at most 2-way)
   constexpr int kPairs = kUpRowsSpan / 2, kNPer = kUpRowsSpan / 8;
-  static_assert(512 / kPairs * kNPer == D && kNPer % 8 == 0, "B_v staging covers the tile");
-  const int kp = threadIdx.x % kPairs, sn = (threadIdx.x / kPairs) * kNPer;
-  const f16* bsrc = bv + (size_t)(2 * kp) * ld + (size_t)kvh * D + sn;
+  static_assert(512 / kPairs == 8 && 8 * 8 * 2 == D && kNPer == 16, "B_v staging covers the tile");
+  const int kp = threadIdx.x / 8, bm = threadIdx.x % 8;
+  const int kcol = kp ^ (4 * bm);             // swizzled column of this thread's dwords
+  const f16* bsrc = bv + (size_t)(2 * kp) * ld + (size_t)kvh * D + 8 * bm;
   constexpr int kZPieces = kUpRowsTile * kUpRowsSpan / 8 / 512;   // 16-byte Z pieces per thread
   floatx16 acc = {};
   half8 braw[2][kNPer / 8];
@@ -591,7 +598,7 @@ upproj_rows_kernel(const f16* __restrict__ zf, const f16* __restrict__ bv, f16* 
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < kNPer / 8; ++i)
-        braw[j][i] = *reinterpret_cast<const half8*>(bsrc + (size_t)(k0 + j) * ld + 8 * i);
+        braw[j][i] = *reinterpret_cast<const half8*>(bsrc + (size_t)(k0 + j) * ld + 64 * i);
 #pragma unroll
     for (int i = 0; i < kZPieces; ++i) {
       const int f = i * 512 + threadIdx.x;
@@ -618,18 +625,21 @@ upproj_rows_kernel(const f16* __restrict__ zf, const f16* __restrict__ bv, f16* 
       const u32x4 r1 = __builtin_bit_cast(u32x4, braw[1][i]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        bt[sn + 8 * i + 2 * e][kp] = (r0[e] & 0xFFFFu) | (r1[e] << 16);
-        bt[sn + 8 * i + 2 * e + 1][kp] = (r0[e] >> 16) | (r1[e] & 0xFFFF0000u);
+        const int n = 8 * bm + 64 * i + 2 * e;
+        bt[n][kcol] = (r0[e] & 0xFFFFu) | (r1[e] << 16);
+        bt[n + 1][kcol] = (r0[e] >> 16) | (r1[e] & 0xFFFF0000u);
       }
     }
     __syncthreads();
     if (k0 + kUpRowsSpan < RV) load_span(k0 + kUpRowsSpan);   // in flight during this span's MFMAs
     const f16* za = &zl[rt * 32 + (lane & 31)][(lane >> 5) * 8];
-    const uint32_t* brow = &bt[nt * 32 + (lane & 31)][(lane >> 5) * 4];
+    const int bn = nt * 32 + (lane & 31);
+    const uint32_t* brow = &bt[bn][0];
+    const int bswz = 4 * ((bn >> 3) & 7);
 #pragma unroll
     for (int u = 0; u < kUpRowsSpan / 16; ++u) {
       // read back through the type it was written with (uint32), then reinterpret
-      const half8 bb = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(brow + u * 8));
+      const half8 bb = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(brow + (((lane >> 5) * 4 + u * 8) ^ bswz)));
       const half8 zh = *reinterpret_cast<const half8*>(za + u * 16);
       acc = mfma32x32x16(zh, bb, acc);
     }

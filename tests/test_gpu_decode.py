@@ -391,6 +391,27 @@ def test_rank_shapes(rk, rv):
         check(got[:4], ref[:4], what=f"r_k={rk} r_v={rv} scale={scale:.3f}")
 
 
+@pytest.mark.parametrize("rk,rv", [(64, 1024), (64, 768), (32, 512), (64, 256)])
+def test_many_pairs_merge_every_rank(rk, rv):
+    """20 sequences x 32 heads (640 pairs) take the wide merge, four pairs per
+    workgroup up to r_v 512 and two above, and the MFMA up-projection of the
+    fp16 merged rows with a partial 32-row tile; one sequence is empty and one
+    spans many attention ranges."""
+    dev = gpu()
+    rng = np.random.default_rng(rk * 7 + rv)
+    lens = rng.integers(1, 900, size=20).astype(np.int32)
+    lens[3] = 0
+    lens[11] = 2600
+    case = synth.make_case(900 + rk + rv, len(lens), 32, 128, rk, rv, lens)
+    log(f"many pairs r_k={rk} r_v={rv}")
+    for scale in scales(128):
+        out = decode_gpu(to_dev(case, dev), lens, scale, dev).float().cpu().numpy()
+        ref = oracle.decode(case["q"], case["b_k"], case["b_v"], case["k_pool"], case["v_pool"],
+                            case["block_tables"], lens, scale)
+        assert not np.abs(out[3]).any()
+        check(out, ref, what=f"many pairs r_k={rk} r_v={rv} scale={scale:.3f}")
+
+
 @pytest.mark.parametrize("rk,rv,per_seq", [(32, 256, 6), (64, 512, 1)])
 def test_append_then_decode_other_ranks(rk, rv, per_seq):
     """Append (MFMA path at 24 tokens, VALU at 4) then decode, at non-default ranks."""
