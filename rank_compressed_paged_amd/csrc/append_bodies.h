@@ -102,19 +102,25 @@ __device__ __forceinline__ void append_k_valu_body(int idx, const f16* __restric
 }
 
 // V side, MFMA: a workgroup computes a [16 tokens x 16 latents] tile with the
-// 16x16x32 f16 MFMA, so one wave load instruction reads 16 rows x 64 bytes
-// (four lanes per row) of w_v and v instead of 32 rows x 32 bytes; the
-// 32x32 tiles spent the launch on address lookups.  Eight waves split the
-// H_kv*d contraction and reduce through LDS; each wave issues the loads of up
-// to sixteen k-steps (its whole share at H_kv*d = 4096) before its first
-// MFMA, so the launch costs about one memory round trip instead of one per
-// batch of k-steps.
+// 16x16x32 f16 MFMA.  Eight waves split the H_kv*d contraction into equal
+// spans (k-steps of 32 in increasing order within a span) and reduce through
+// LDS.  Each wave stages its span through its own LDS rows, kVChunk k at a
+// time: one wave load instruction reads 256 contiguous bytes of each of four
+// rows (the 16 token rows, then the 16 w_v rows), where reading the MFMA
+// fragments straight from memory took 16 rows x 64 bytes per instruction and
+// the launch was bound by that request count.  The next chunk's loads are in
+// flight while this chunk's fragments are read and multiplied.  The chain of
+// a lane (span steps in order, then zero-token steps up to whole batches of
+// kAppendVBatch, as append_v_split_body reproduces) fixes the rounding.
 constexpr int kAppendVWaves = 8;
 constexpr int kAppendVBatch = 16;
+constexpr int kVChunk = 128;               // k per staged chunk (four k-steps)
+constexpr int kVRow = kVChunk + 8;         // halves per LDS row (16-byte pad)
 
 __device__ __forceinline__ void append_v_mfma_body(int bid, const f16* __restrict__ v, const f16* __restrict__ wv,
                                                    int n, int K, int RV, SlotOf where, f16* __restrict__ vc) {
   __shared__ float red[kAppendVWaves][4][64];
+  __shared__ __attribute__((aligned(16))) f16 stage[kAppendVWaves][32][kVRow];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   // XCD-aware order (workgroup i runs on XCD i % 8): the token tiles of one
@@ -125,14 +131,17 @@ __device__ __forceinline__ void append_v_mfma_body(int bid, const f16* __restric
   const int jt = (y / ttiles) * 8 + x;
   const int tt = y % ttiles;
   if (jt >= jtiles) return;                 // uniform over the workgroup, before any barrier
-  const int t = tt * 16 + (lane & 15);
-  const bool trow = t < n;
+  const bool tlive = tt * 16 + (lane & 15) < n;
   const int j = jt * 16 + (lane & 15);
-  const int kofs = (lane >> 4) * 8;
   const int ksteps = K / (32 * kAppendVWaves);
   const int kbase = w * ksteps * 32;
-  const f16* xrow = v + (size_t)(trow ? t : n - 1) * K + kofs;
-  const f16* wrow = wv + (size_t)j * K + kofs;
+  const int nchunks = (ksteps * 32 + kVChunk - 1) / kVChunk;
+  // staging: piece i of a lane is row 4i + lane/16 of the wave's 32 (token rows
+  // 0-15, clamped to the last token; w_v rows 16-31), 16 bytes at 8*(lane%16)
+  const int prow = lane >> 4, pcol = (lane & 15) * 8;
+  auto src_row = [&](int r) -> const f16* {
+    return r < 16 ? v + (size_t)min(tt * 16 + r, n - 1) * K : wv + (size_t)(jt * 16 + r - 16) * K;
+  };
   // destination of the value this lane stores (waves 0-3, see the end): its
   // sequence and position are read before the operands and its table entry
   // right behind them, so the slot lookup overlaps the contraction instead of
@@ -144,24 +153,43 @@ __device__ __forceinline__ void append_v_mfma_body(int bid, const f16* __restric
     dseq = where.seq[ti];
     dpos = where.pos[ti];
   }
+  f16 (*st)[kVRow] = stage[w];
+  half8 buf[8];
+  // chunk c covers k in [kbase + c*kVChunk, + cw); a partial last chunk
+  // re-reads its first columns in the lanes past its width (never multiplied)
+  auto load = [&](int c) {
+    const int cw = min(kVChunk, ksteps * 32 - c * kVChunk);
+    const int col = pcol < cw ? pcol : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      buf[i] = *reinterpret_cast<const half8*>(src_row(4 * i + prow) + kbase + c * kVChunk + col);
+  };
   floatx4 acc = {};
-  for (int c = 0; c < ksteps; c += kAppendVBatch) {
-    half8 a[kAppendVBatch], b[kAppendVBatch];
+  half8 blast = {};                          // w_v fragment of the span's last step
+  load(0);
+  if (storer) dphys = where.bt[(size_t)dseq * where.mb + dpos / kBlock];
+  for (int c = 0; c < nchunks; ++c) {
 #pragma unroll
-    for (int u = 0; u < kAppendVBatch; ++u) {
-      const int k0 = kbase + min(c + u, ksteps - 1) * 32;
-      a[u] = *reinterpret_cast<const half8*>(xrow + k0);
-      b[u] = *reinterpret_cast<const half8*>(wrow + k0);
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<half8*>(&st[4 * i + prow][pcol]) = buf[i];
+    if (c + 1 < nchunks) load(c + 1);        // in flight while this chunk is multiplied
+    const int steps = min(kVChunk / 32, ksteps - c * (kVChunk / 32));
+    half8 fa[kVChunk / 32], fb[kVChunk / 32];
+#pragma unroll
+    for (int u = 0; u < kVChunk / 32; ++u) {
+      const int kc = min(u, steps - 1) * 32 + 8 * (lane >> 4);
+      fa[u] = *reinterpret_cast<const half8*>(&st[lane & 15][kc]);
+      fb[u] = *reinterpret_cast<const half8*>(&st[16 + (lane & 15)][kc]);
     }
-    __builtin_amdgcn_sched_barrier(0);      // every load of the batch is in flight before the first MFMA
-    if (c == 0 && storer) dphys = where.bt[(size_t)dseq * where.mb + dpos / kBlock];
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < kAppendVBatch; ++u) {
-      const bool live = trow && c + u < ksteps;   // clamped re-reads contribute nothing
-      acc = mfma16x16x32(live ? a[u] : half8{}, b[u], acc);
+    for (int u = 0; u < kVChunk / 32; ++u) {
+      if (u < steps) acc = mfma16x16x32(tlive ? fa[u] : half8{}, fb[u], acc);
+      if (u == steps - 1) blast = fb[u];     // static index: no register array indexed at run time
     }
   }
+  // the chain ends in whole batches of kAppendVBatch steps: the steps past the
+  // span repeat the last w_v fragment with zero tokens
+  const int pad = (ksteps + kAppendVBatch - 1) / kAppendVBatch * kAppendVBatch - ksteps;
+  for (int e = 0; e < pad; ++e) acc = mfma16x16x32(half8{}, blast, acc);
   // result layout: lane l, register r holds D[4(l/16) + r][l % 16]
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[w][r][lane] = acc[r];
