@@ -169,12 +169,9 @@ starkv_status starkv_decode(const starkv_dims* dims, int32_t batch, int32_t max_
  * layout, alignment and error are exactly those of the two calls in that
  * order on `stream` (context_lens already count the new tokens); the append's
  * projection, the query projection and the decode plan share the first
- * launch, so the two projections run side by side.  An MFMA V projection that
- * would fill every compute unit by itself is split into the eight k-spans of
- * the plain append's MFMA V body, its fp32 partial sums kept in the workspace
- * and added in span order by a second launch before the attention: the same
- * chains and the same order, so the V pool is bit-identical to starkv_append's.
- * n_new == 0 is a plain decode.  Workspace: as for starkv_decode.
+ * launch, so the two projections run side by side.  The append bodies are
+ * starkv_append's, so the pools are bit-identical to its.  n_new == 0 is a
+ * plain decode.  Workspace: as for starkv_decode.
  */
 starkv_status starkv_decode_step(const starkv_dims* dims, int32_t batch, int32_t max_context_len,
                                  int32_t n_new, const void* k_new, const void* v_new,

@@ -111,7 +111,7 @@ __device__ __forceinline__ void append_k_valu_body(int idx, const f16* __restric
 // the launch was bound by that request count.  The next chunk's loads are in
 // flight while this chunk's fragments are read and multiplied.  The chain of
 // a lane (span steps in order, then zero-token steps up to whole batches of
-// kAppendVBatch, as append_v_split_body reproduces) fixes the rounding.
+// kAppendVBatch) fixes the rounding.
 constexpr int kAppendVWaves = 8;
 constexpr int kAppendVBatch = 16;
 constexpr int kVChunk = 128;               // k per staged chunk (four k-steps)
@@ -200,148 +200,6 @@ __device__ __forceinline__ void append_v_mfma_body(int bid, const f16* __restric
     for (int q = 0; q < kAppendVWaves; ++q) sum += red[q][w][lane];
     vc[((size_t)dphys * RV + j) * kBlock + dpos % kBlock] = (f16)sum;
   }
-}
-
-// V side of a decode step's append, split into the eight k-spans of the MFMA
-// V body above (span q: k in [q*K/8, (q+1)*K/8), the share of its wave q).
-// Workgroup bid computes the span's fp32 partial sums for a tile of up to 64
-// tokens x 32 latents; append_v_finish then adds the eight spans in order and
-// stores.  Bit for bit the MFMA V body's result: each 16 x 16 sub-tile runs
-// that body's 16x16x32 MFMA chain (the span's 32-wide k-steps in increasing
-// order, then its zero-operand steps that pad the chain to whole load
-// batches), and the finishing sum has that body's order.  What changes is the
-// load pattern: rows are read whole (a wave instruction reads two 512-byte row
-// segments instead of sixteen 64-byte pieces) into LDS in stages of 256 k,
-// and a workgroup reads 96 KiB instead of 256 KiB, so the V side spreads over
-// every compute unit.  Span q's workgroups all run on XCD q (workgroup i runs
-// on XCD i % 8): only that XCD's L2 holds the span's w_v columns and token
-// rows.  part: [8][n][r_v] fp32.
-constexpr int kSplitLat = 32;            // latents per workgroup tile
-constexpr int kSplitMaxTok = 64;         // tokens per workgroup tile (at most)
-constexpr int kSplitStage = 256;         // k per LDS stage
-constexpr int kSplitPad = 8;             // halves of LDS row padding
-constexpr int kSplitInFlight = 2;        // stages whose loads are in flight together
-
-__host__ __device__ constexpr int split_token_rows(int n) { return n >= kSplitMaxTok ? kSplitMaxTok : 16 * ((n + 15) / 16); }
-
-// Row and 16-byte column of piece p of a stage whose rows hold per_row pieces
-// (shifts for whole stages: a division per piece cost microseconds of issue).
-__device__ __forceinline__ void split_piece(int p, int per_row, int& row, int& col) {
-  if (per_row == kSplitStage / 8) {
-    row = p / (kSplitStage / 8);
-    col = p % (kSplitStage / 8);
-  } else {
-    row = p / per_row;
-    col = p - row * per_row;
-  }
-}
-
-__device__ __forceinline__ void append_v_split_body(int bid, int trows, const f16* __restrict__ v,
-                                                    const f16* __restrict__ wv, int n, int K, int RV,
-                                                    float* __restrict__ part) {
-  constexpr int kRows = kSplitMaxTok + kSplitLat;
-  constexpr int Row = kSplitStage + kSplitPad;
-  constexpr int kPer = kRows * kSplitStage / 8 / 512;     // 16-byte pieces per thread per stage
-  __shared__ __attribute__((aligned(16))) f16 st[kRows][Row];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int span = bid % 8;
-  const int nlt = (RV + kSplitLat - 1) / kSplitLat;
-  const int lt = (bid / 8) % nlt, tt = (bid / 8) / nlt;
-  const int t0 = tt * trows, j0 = lt * kSplitLat;
-  const int rows = trows + kSplitLat;
-  const int Ks = K / kAppendVWaves;                       // the span's k (a multiple of 32)
-  const int ksteps = Ks / 32;
-  const int nstage = (Ks + kSplitStage - 1) / kSplitStage;
-  // wave w: the 16 x 16 sub-tile of tokens 16*(w/2), latents 16*(w%2)
-  const int ti = w >> 1, li = w & 1;
-  const bool mma = ti * 16 < trows;
-  const bool tlive = t0 + ti * 16 + (lane & 15) < n;
-  const size_t kspan = (size_t)span * Ks;
-  floatx4 acc = {};
-  for (int g0 = 0; g0 < nstage; g0 += kSplitInFlight) {
-    half8 buf[kSplitInFlight][kPer];
-#pragma unroll
-    for (int gi = 0; gi < kSplitInFlight; ++gi) {
-      const int g = g0 + gi;
-      const int per_row = max(min(kSplitStage, Ks - g * kSplitStage) / 8, 1);
-#pragma unroll
-      for (int m = 0; m < kPer; ++m) {
-        int row, col;
-        split_piece(tid + 512 * m, per_row, row, col);
-        if (g < nstage && row < rows) {
-          const f16* src = row < trows ? v + (size_t)min(t0 + row, n - 1) * K
-                                       : wv + (size_t)min(j0 + row - trows, RV - 1) * K;
-          buf[gi][m] = *reinterpret_cast<const half8*>(src + kspan + (size_t)g * kSplitStage + col * 8);
-        }
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);      // every load of the group in flight before the first LDS write
-#pragma unroll
-    for (int gi = 0; gi < kSplitInFlight; ++gi) {
-      const int g = g0 + gi;
-      if (g >= nstage) break;                 // uniform over the workgroup
-      const int sw = min(kSplitStage, Ks - g * kSplitStage);
-      __syncthreads();                        // the previous stage's fragments are read
-#pragma unroll
-      for (int m = 0; m < kPer; ++m) {
-        int row, col;
-        split_piece(tid + 512 * m, sw / 8, row, col);
-        if (row < rows) *reinterpret_cast<half8*>(&st[row][col * 8]) = buf[gi][m];
-      }
-      __syncthreads();
-      if (mma) {
-        // fragments of four steps at a time (LDS reads in flight together), then the chain
-        constexpr int kGroup = 4;
-#pragma unroll
-        for (int k0 = 0; k0 < kSplitStage / 32; k0 += kGroup) {
-          half8 fa[kGroup], fb[kGroup];
-#pragma unroll
-          for (int u = 0; u < kGroup; ++u) {
-            const int kc = min((k0 + u) * 32, sw - 32) + 8 * (lane >> 4);
-            fa[u] = *reinterpret_cast<const half8*>(&st[ti * 16 + (lane & 15)][kc]);
-            fb[u] = *reinterpret_cast<const half8*>(&st[trows + li * 16 + (lane & 15)][kc]);
-          }
-#pragma unroll
-          for (int u = 0; u < kGroup; ++u)
-            if ((k0 + u) * 32 < sw) acc = mfma16x16x32(tlive ? fa[u] : half8{}, fb[u], acc);
-        }
-      }
-    }
-  }
-  if (!mma) return;                           // no barrier follows
-  // the MFMA V body's chain ends in whole batches of kAppendVBatch steps; its
-  // steps past the span repeat the last step's w_v fragment with zero tokens
-  const int pad = (ksteps + kAppendVBatch - 1) / kAppendVBatch * kAppendVBatch - ksteps;
-  if (pad > 0) {
-    const int sw = Ks - (nstage - 1) * kSplitStage;
-    const half8 b = *reinterpret_cast<const half8*>(&st[trows + li * 16 + (lane & 15)][sw - 32 + 8 * (lane >> 4)]);
-    for (int e = 0; e < pad; ++e) acc = mfma16x16x32(half8{}, b, acc);
-  }
-  // result layout: lane l, register r holds D[4(l/16) + r][l % 16]
-  const int j = j0 + li * 16 + (lane & 15);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = t0 + ti * 16 + 4 * (lane >> 4) + r;
-    if (t < n && j < RV) part[((size_t)span * n + t) * RV + j] = acc[r];
-  }
-}
-
-// Adds the eight span partials of append_v_split_body (span order, from 0, as
-// the MFMA V body's reduction) for token t and latents j, rounds once to fp16
-// and scatters into the token's slot.
-__device__ __forceinline__ void append_v_finish_body(int t, int j, const float* __restrict__ part, int n, int RV,
-                                                     SlotOf where, f16* __restrict__ vc) {
-  float p[kAppendVWaves];
-#pragma unroll
-  for (int q = 0; q < kAppendVWaves; ++q) p[q] = part[((size_t)q * n + t) * RV + j];
-  int phys, slot;
-  where(t, phys, slot);
-  float sum = 0.f;
-#pragma unroll
-  for (int q = 0; q < kAppendVWaves; ++q) sum += p[q];
-  vc[((size_t)phys * RV + j) * kBlock + slot] = (f16)sum;
 }
 
 // V side, many tokens (prefill chunks): a workgroup of eight waves computes a
@@ -553,8 +411,6 @@ __device__ __forceinline__ void append_v_valu_body(int bx, int by, int vlat, con
 struct AppendRoles {
   bool vrows;            // many tokens: V side on append_v_rows (its own launch)
   bool vmfma, kmfma;     // MFMA (else VALU) bodies
-  bool vsplit;           // MFMA V side split into k-spans (append_v_split_body; needs partial space)
-  int vtrows;            // split V side: tokens per workgroup tile
   long long nv;          // V-side workgroups
   int vlat;              // VALU V side: latents per workgroup (4: contraction in two parts, or 8)
   int vgx;               // VALU V side: workgroups per token group (r_v / vlat)
@@ -569,9 +425,7 @@ struct AppendRoles {
 // While they fit, the VALU V side splits its contraction over two waves per
 // latent and MFMA K tiles spread one per workgroup (both: fewer bytes in
 // flight per compute unit); otherwise eight latents or tiles per workgroup.
-// split: the caller has room for the split V side's partial sums (taken when
-// the V side is on MFMA).
-inline AppendRoles append_roles(const Shape& s, int n, long long slots = 0, bool split = false) {
+inline AppendRoles append_roles(const Shape& s, int n, long long slots = 0) {
   AppendRoles r{};
   const int K = s.KV * s.D;
   r.kmfma = s.RK % 32 == 0 && s.D % 16 == 0;      // also for small n: rows read along d
@@ -581,11 +435,7 @@ inline AppendRoles append_roles(const Shape& s, int n, long long slots = 0, bool
   r.ktiles = ((nn + 31) / 32) * s.KV * (s.RK / 32);
   const long long kvalu = (nn * s.KV * s.RK + 511) / 512;
   const long long kwg8 = r.kmfma ? (r.ktiles + 7) / 8 : kvalu;
-  r.vsplit = r.vmfma && split;
-  if (r.vsplit) {
-    r.vtrows = split_token_rows(n);
-    r.nv = 8LL * ((s.RV + kSplitLat - 1) / kSplitLat) * ((nn + r.vtrows - 1) / r.vtrows);
-  } else if (r.vmfma) {
+  if (r.vmfma) {
     r.nv = ((s.RV / 16 + 7) / 8) * 8LL * ((nn + 15) / 16);
   } else {
     const long long groups = (nn + kAppendGroup - 1) / kAppendGroup;
@@ -607,19 +457,16 @@ inline AppendRoles append_roles(const Shape& s, int n, long long slots = 0, bool
 }
 
 // One role of a shared append launch (512 threads, workgroup bid).  The
-// body choices are template arguments (VM: V side 0 VALU, 1 MFMA, 2 MFMA split
-// into k-spans, its partial sums to `part`; KM: K side on MFMA, else VALU) so
-// that a launch carries only the registers of the bodies it runs.
+// body choices are template arguments (VM: V side 0 VALU, 1 MFMA; KM: K side
+// on MFMA, else VALU) so that a launch carries only the registers of the
+// bodies it runs.
 template <int VM, bool KM>
 __device__ __forceinline__ void append_role(int bid, const AppendRoles& r, const f16* __restrict__ k,
                                             const f16* __restrict__ v, const f16* __restrict__ wk,
                                             const f16* __restrict__ wv, int n, int KV, int D, int RK, int RV,
-                                            SlotOf where, f16* __restrict__ kc, f16* __restrict__ vc,
-                                            float* __restrict__ part = nullptr) {
+                                            SlotOf where, f16* __restrict__ kc, f16* __restrict__ vc) {
   if (bid < r.nv) {                          // whole workgroup: the V side's barriers see every wave
-    if constexpr (VM == 2)
-      append_v_split_body(bid, r.vtrows, v, wv, n, KV * D, RV, part);
-    else if constexpr (VM == 1)
+    if constexpr (VM == 1)
       append_v_mfma_body(bid, v, wv, n, KV * D, RV, where, vc);
     else
       append_v_valu_body(bid % r.vgx, bid / r.vgx, r.vlat, v, wv, n, KV * D, RV, where, vc);

@@ -6,9 +6,7 @@
 //                   every workgroup of launch 2 gets an equal range of 16-token
 //                   blocks of the whole ragged batch (ranges may cross sequence
 //                   boundaries).  A decode step (starkv_decode_step) runs the
-//                   step's append in the same launch (step_prologue); a V
-//                   projection split into k-spans there is finished by one more
-//                   launch (append_v_finish) before launch 2.
+//                   step's append in the same launch (step_prologue).
 //   2. attn         the HBM-bound scan over the latent blocks (attn_kernel.h);
 //                   each (range, sequence) pair leaves a partial state: max m
 //                   and sum l in fp32, z / l in fp16.
@@ -216,21 +214,18 @@ qproj_plan_valu_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, fl
 // fetched by twice the compute units; or 512 VALU outputs each) and, in the
 // last workgroup, the plan.  The three are independent: the append writes the
 // new tokens' slots, which only the attention launch after this one reads.
-// VM: V side 0 VALU, 1 MFMA, 2 MFMA split into k-spans (partial sums to
-// `part`, added and stored by append_v_finish_kernel before the attention);
-// MF: K side and q~ on MFMA (template arguments, so that a launch holds only
-// the registers of the bodies it runs).
+// VM: V side 0 VALU, 1 MFMA; MF: K side and q~ on MFMA (template arguments,
+// so that a launch holds only the registers of the bodies it runs).
 template <int VM, bool MF>
 __global__ void __launch_bounds__(512)
 step_prologue_kernel(const f16* __restrict__ k, const f16* __restrict__ v, const f16* __restrict__ wk,
                      const f16* __restrict__ wv, int n, SlotOf where, f16* __restrict__ kc, f16* __restrict__ vc,
                      AppendRoles roles, int nA, const f16* __restrict__ q, const f16* __restrict__ bk,
                      float* __restrict__ qt, int batch, int H, int KV, int D, int RK, int RV, float scale2,
-                     int nQ, const int32_t* __restrict__ lens, int grid, int32_t* __restrict__ plan,
-                     float* __restrict__ part) {
+                     int nQ, const int32_t* __restrict__ lens, int grid, int32_t* __restrict__ plan) {
   const int bid = blockIdx.x;
   if (bid < nA) {
-    append_role<VM, MF>(bid, roles, k, v, wk, wv, n, KV, D, RK, RV, where, kc, vc, part);
+    append_role<VM, MF>(bid, roles, k, v, wk, wv, n, KV, D, RK, RV, where, kc, vc);
     return;
   }
   if (bid < nA + nQ) {
@@ -243,14 +238,6 @@ step_prologue_kernel(const f16* __restrict__ k, const f16* __restrict__ v, const
     return;
   }
   build_plan<512>(lens, batch, grid, plan);
-}
-
-// Second launch of a decode step whose V side was split into k-spans: token
-// blockIdx.y, latents blockIdx.x * 256 + threadIdx.x.
-__global__ void __launch_bounds__(256)
-append_v_finish_kernel(const float* __restrict__ part, int n, int RV, SlotOf where, f16* __restrict__ vc) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j < RV) append_v_finish_body(blockIdx.y, j, part, n, RV, where, vc);
 }
 
 // ---------------------------------------------------------------------------
@@ -1108,18 +1095,7 @@ hipError_t decode_step_enqueue(const DecodeLaunch& a, const AppendLaunch& ap) {
   const long long units = ((a.batch + 31LL) / 32) * ((s.H * (s.RK / 32) + 3) / 4);
   const long long nQ = qmfma ? units : ((long long)a.batch * s.H * s.RK + 511) / 512;
   // the append's workgroups spread while all of the launch fits the compute units
-  AppendRoles r = append_roles(s, ap.n, ap.cus > 0 ? std::max(0LL, ap.cus - nQ - 1) : 0);
-  // An MFMA V side that fills every compute unit by itself (the K side and q~
-  // then wait for it) is split into k-spans, its partial sums kept where the
-  // attention's partial states and merged rows go later (free until the
-  // attention launch); with its registers and LDS two workgroups share a unit
-  // when the K side and q~ are on MFMA.  Below that, the second launch costs
-  // more than the split saves.
-  const size_t part_bytes = sizeof(float) * kAppendVWaves * (size_t)ap.n * s.RV;
-  if (r.vmfma && ap.cus > 0 && r.nv >= ap.cus && ap.n < 65536 && part_bytes <= a.lay.bytes - a.lay.off_z) {
-    const long long wg_slots = (qmfma ? 2LL : 1LL) * ap.cus;
-    r = append_roles(s, ap.n, std::max(0LL, wg_slots - nQ - 1), true);
-  }
+  const AppendRoles r = append_roles(s, ap.n, ap.cus > 0 ? std::max(0LL, ap.cus - nQ - 1) : 0);
   const long long nA = r.nv + r.kwg;
   // the many-token V side has its own kernel: append, then decode
   if (r.vrows || nA * 512 > (1LL << 30)) {
@@ -1133,25 +1109,17 @@ hipError_t decode_step_enqueue(const DecodeLaunch& a, const AppendLaunch& ap) {
   const long long grid = nA + nQ + 1;
   if (grid * 512 > (1LL << 31)) return hipErrorInvalidConfiguration;
   const SlotOf where{ap.block_tables, ap.token_seq, ap.token_pos, s.MB};
-  float* part = reinterpret_cast<float*>(a.ws + a.lay.off_z);
   // MF: the K side and q~ on MFMA (both need r_k % 32 == 0 and d % 16 == 0)
-  const auto kern = r.vsplit ? (qmfma ? step_prologue_kernel<2, true> : step_prologue_kernel<2, false>)
-                    : r.vmfma ? (qmfma ? step_prologue_kernel<1, true> : step_prologue_kernel<1, false>)
-                              : (qmfma ? step_prologue_kernel<0, true> : step_prologue_kernel<0, false>);
+  const auto kern = r.vmfma ? (qmfma ? step_prologue_kernel<1, true> : step_prologue_kernel<1, false>)
+                            : (qmfma ? step_prologue_kernel<0, true> : step_prologue_kernel<0, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, a.stream,
                      static_cast<const f16*>(ap.k), static_cast<const f16*>(ap.v), static_cast<const f16*>(ap.w_k),
                      static_cast<const f16*>(ap.w_v), ap.n, where, static_cast<f16*>(ap.k_cache),
                      static_cast<f16*>(ap.v_cache), r, (int)nA, static_cast<const f16*>(a.q),
                      static_cast<const f16*>(a.b_k), qt, a.batch, s.H, s.KV, s.D, s.RK, s.RV, a.scale * kLog2e,
-                     (int)nQ, a.context_lens, a.grid, plan, part);
-  hipError_t err = hipGetLastError();
+                     (int)nQ, a.context_lens, a.grid, plan);
+  const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (r.vsplit) {
-    hipLaunchKernelGGL(append_v_finish_kernel, dim3((s.RV + 255) / 256, ap.n), dim3(256), 0, a.stream, part, ap.n,
-                       s.RV, where, static_cast<f16*>(ap.v_cache));
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
   return decode_after_prologue(a);
 }
 

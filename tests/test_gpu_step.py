@@ -1,12 +1,10 @@
 """starkv_decode_step (append + decode with the append, query projection and
 plan in one first launch) against starkv_append followed by starkv_decode:
 bit-identical outputs and pool images, across the append paths (VALU both
-sides, MFMA both sides, the MFMA V side split into k-spans whose partial sums
-are added in a second launch -- taken when the unsplit V side would fill
-every compute unit of a 256-unit GPU --, the many-token fallback), grouped
-heads, r_k 16 and head_dim 64; plus parity with the oracle.  The split V side
-computes the same MFMA chains and the same ordered sum as the plain append's
-MFMA V body, so the pools match bit for bit."""
+sides, MFMA both sides in one shared launch, the many-token fallback), MFMA V
+sides from 16 to 252 rows with contractions of 256 to 8,192 (one k-step per
+wave and a padded chain up to eight staged chunks per wave), grouped heads,
+r_k 16 and head_dim 64; plus parity with the oracle."""
 
 import math
 
@@ -22,14 +20,14 @@ pytestmark = pytest.mark.gpu
 CASES = [  # (heads, kv_heads, d, r_k, r_v, batch, new tokens per sequence)
     (32, 32, 128, 64, 1024, 4, 1),      # VALU both sides, VALU q~
     (32, 32, 128, 64, 1024, 24, 1),     # MFMA both sides (one shared launch), MFMA q~
-    (32, 32, 128, 64, 1024, 64, 1),     # large MFMA V side: split into k-spans (plain append: two launches)
+    (32, 32, 128, 64, 1024, 64, 1),     # MFMA V side filling every CU (plain append: two launches)
     (32, 32, 128, 64, 512, 20, 16),     # 320 new rows: many-token V kernel, append then decode
     (32, 8, 128, 64, 512, 16, 2),       # grouped heads
     (16, 16, 64, 16, 256, 40, 1),       # r_k 16: VALU K side beside the MFMA V side
-    (32, 32, 128, 64, 1024, 100, 1),    # split V side: two token tiles, the second ragged
-    (32, 32, 256, 64, 1024, 64, 1),     # split V side: k-spans of 1,024 (four stages, two load groups)
-    (8, 2, 128, 32, 256, 84, 3),        # split V side: k-spans of 32 (one step, padded chain)
-    (16, 16, 64, 16, 256, 84, 3),       # split V side beside the VALU K side and q~
+    (32, 32, 128, 64, 1024, 100, 1),    # MFMA V side: seven token tiles, the last ragged
+    (32, 32, 256, 64, 1024, 64, 1),     # MFMA V side: 1,024 k per wave (eight staged chunks)
+    (8, 2, 128, 32, 256, 84, 3),        # MFMA V side: 32 k per wave (one step, padded chain)
+    (16, 16, 64, 16, 256, 84, 3),       # MFMA V side beside the VALU K side and q~
 ]
 
 
