@@ -308,7 +308,8 @@ __device__ __forceinline__ void append_v_rows_body(int bid, const f16* __restric
   }
 }
 
-// V side, VALU (fewer than 16 tokens): a workgroup of eight waves owns vlat
+// V side, VALU (shapes the MFMA tile does not fit: r_v % 16 != 0 or
+// H_kv*d % 256 != 0): a workgroup of eight waves owns vlat
 // (4 or 8) joint latents and up to four tokens; wave w takes latent
 // vlat*bx + w % vlat over part w / vlat of each contraction pass, so at vlat
 // 4 a launch's w_v rows are spread over twice the compute units.  Per pass the tokens' v rows are
@@ -430,7 +431,7 @@ inline AppendRoles append_roles(const Shape& s, int n, long long slots = 0) {
   const int K = s.KV * s.D;
   r.kmfma = s.RK % 32 == 0 && s.D % 16 == 0;      // also for small n: rows read along d
   r.vrows = n >= 256 && s.RV % kAppendRowsLat == 0 && K % kAppendRowsSpan == 0;
-  r.vmfma = !r.vrows && n >= 16 && s.RV % 16 == 0 && K % (32 * kAppendVWaves) == 0;
+  r.vmfma = !r.vrows && s.RV % 16 == 0 && K % (32 * kAppendVWaves) == 0;   // any token count: rows past n are masked
   const long long nn = n;
   r.ktiles = ((nn + 31) / 32) * s.KV * (s.RK / 32);
   const long long kvalu = (nn * s.KV * s.RK + 511) / 512;

@@ -38,12 +38,11 @@ append_v_valu_kernel(const f16* __restrict__ v, const f16* __restrict__ wv, int 
 }
 
 // Both sides in one launch of 512-thread workgroups (roles in append_role):
-// small appends (fewer than 16 tokens: both sides VALU, latency-bound chains
-// of a few memory round trips that now run side by side), and MFMA-sized ones
-// while every workgroup gets a compute unit of its own (up to 48 tokens at 32
-// heads, r_v 1024 on 256 units).  Past that, a V-side workgroup (164 VGPRs per
-// lane) leaves too few registers on its unit for a second one, so K-side
-// workgroups would wait for the V side: those appends use two launches.
+// appends whose V side is VALU (latency-bound chains of a few memory round
+// trips that run side by side), and MFMA-sized ones while every workgroup gets
+// a compute unit of its own (up to 48 tokens at 32 heads, r_v 1024 on 256
+// units).  Past that, K-side workgroups would wait for V-side ones: those
+// appends use two launches.
 template <int VM, bool KM>
 __global__ void __launch_bounds__(512)
 append_kv_kernel(const f16* __restrict__ k, const f16* __restrict__ v, const f16* __restrict__ wk,
