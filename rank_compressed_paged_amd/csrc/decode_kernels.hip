@@ -171,6 +171,61 @@ __device__ __forceinline__ void qproj_mfma_body(int unit, int tid, const f16* __
   }
 }
 
+// The same unit with both operands staged through LDS, 128 d at a time: a
+// wave load instruction reads 256 contiguous bytes of each of four rows (q
+// rows of the batch tile, then the pair's B_k rows) instead of 32 bytes of
+// each of 32, then the MFMA fragments come from LDS.  The same chain of
+// k-steps, so q~ is bit-identical to qproj_mfma_body's.  Needs the caller's
+// LDS: ql[4 waves][64 rows][kQRow] halves.
+constexpr int kQChunk = 128;
+constexpr int kQRow = kQChunk + 8;
+__device__ __forceinline__ void qproj_mfma_staged_body(int unit, int tid, const f16* __restrict__ q,
+                                                       const f16* __restrict__ bk, float* __restrict__ qt,
+                                                       int batch, int H, int KV, int D, int RK, float scale2,
+                                                       f16 (*ql)[kQRow]) {
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int rtiles = RK / 32;
+  const int npairs = H * rtiles;
+  const int groups = (npairs + 3) / 4;
+  const int btile = unit / groups;
+  const int pair = (unit % groups) * 4 + w;
+  if (pair >= npairs) return;
+  const int head = pair / rtiles;
+  const int r = (pair % rtiles) * 32 + (lane & 31);
+  const int b = btile * 32 + (lane & 31);
+  const int kofs = (lane >> 5) * 8;
+  const bool brow = b < batch;
+  // staging: piece i of a lane is row 4i + lane/16 of the wave's 64 (q rows
+  // 0-31 clamped to the batch, B_k rows 32-63), 16 bytes at 8*(lane%16)
+  const int prow = lane >> 4, pcol = (lane & 15) * 8;
+  const int kvh = head / (H / KV);
+  auto src_row = [&](int rr) -> const f16* {
+    return rr < 32 ? q + ((size_t)min(btile * 32 + rr, batch - 1) * H + head) * D
+                   : bk + ((size_t)kvh * RK + (pair % rtiles) * 32 + rr - 32) * D;
+  };
+  floatx16 acc = {};
+  for (int c0 = 0; c0 < D; c0 += kQChunk) {
+    const int cw = min(kQChunk, D - c0);
+    const int col = pcol < cw ? pcol : 0;
+    half8 buf[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) buf[i] = *reinterpret_cast<const half8*>(src_row(4 * i + prow) + c0 + col);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) *reinterpret_cast<half8*>(&ql[4 * i + prow][pcol]) = buf[i];
+    for (int k0 = 0; k0 < cw; k0 += 16) {
+      const half8 a = *reinterpret_cast<const half8*>(&ql[lane & 31][k0 + kofs]);
+      const half8 bb = *reinterpret_cast<const half8*>(&ql[32 + (lane & 31)][k0 + kofs]);
+      acc = mfma32x32x16(brow ? a : half8{}, bb, acc);
+    }
+  }
+#pragma unroll
+  for (int reg = 0; reg < 16; ++reg) {
+    const int bi = btile * 32 + mfma_row(reg, lane);
+    if (bi < batch) qt[((size_t)bi * H + head) * RK + r] = acc[reg] * scale2;
+  }
+}
+
 // VALU q~ projection: one thread per (row, head, latent) output idx.
 __device__ __forceinline__ void qproj_valu_body(long long idx, const f16* __restrict__ q, const f16* __restrict__ bk,
                                                 float* __restrict__ qt, int batch, int H, int KV, int D, int RK,
@@ -188,11 +243,12 @@ __global__ void __launch_bounds__(256)
 qproj_plan_mfma_kernel(const f16* __restrict__ q, const f16* __restrict__ bk, float* __restrict__ qt,
                        int batch, int H, int KV, int D, int RK, float scale2,
                        const int32_t* __restrict__ lens, int grid, int32_t* __restrict__ plan) {
+  __shared__ __attribute__((aligned(16))) f16 ql[4][64][kQRow];
   if (lens != nullptr && blockIdx.x == gridDim.x - 1) {
     build_plan<256>(lens, batch, grid, plan);
     return;
   }
-  qproj_mfma_body(blockIdx.x, threadIdx.x, q, bk, qt, batch, H, KV, D, RK, scale2);
+  qproj_mfma_staged_body(blockIdx.x, threadIdx.x, q, bk, qt, batch, H, KV, D, RK, scale2, ql[threadIdx.x >> 6]);
 }
 
 // VALU path (small batches): one thread per (b, h, r).
