@@ -12,8 +12,9 @@
 //   2. prefill_attn   per (tile, context range, query head): q~ of the tile,
 //                     scores on MFMA, causal online softmax, z += P . c_v on
 //                     MFMA;
-//   3. merge          log-sum-exp merge of each row's range partials (shared;
-//                     skipped when every row fits one range);
+//   3. merge          log-sum-exp merge of each row's range partials into fp16
+//                     rows Z (shared; skipped when every row fits one range:
+//                     the attention kernel then writes Z itself);
 //   4. upproj         out = Z . B_v column block (shared).
 //
 // Method: Proxima README text on wpnews ("Show HN: Proxima ..."), opening
