@@ -1,8 +1,9 @@
 """starkv_decode_step (append + decode with the append, query projection and
 plan in one first launch) against starkv_append followed by starkv_decode:
 bit-identical outputs and pool images, across the append paths (VALU both
-sides, MFMA both sides in one shared launch, the many-token fallback), MFMA V
-sides from 16 to 252 rows with contractions of 256 to 8,192 (one k-step per
+sides where the MFMA tiles do not fit, MFMA both sides in one shared launch,
+the many-token fallback), MFMA V
+sides from 4 to 252 rows with contractions of 256 to 8,192 (one k-step per
 wave and a padded chain up to eight staged chunks per wave), grouped heads,
 r_k 16 and head_dim 64; plus parity with the oracle."""
 
@@ -18,7 +19,8 @@ from rank_compressed_paged_amd import synth
 pytestmark = pytest.mark.gpu
 
 CASES = [  # (heads, kv_heads, d, r_k, r_v, batch, new tokens per sequence)
-    (32, 32, 128, 64, 1024, 4, 1),      # VALU both sides, VALU q~
+    (32, 32, 128, 64, 1024, 4, 1),      # MFMA V side on a masked 16-row tile, MFMA K side and q~
+    (10, 10, 64, 16, 256, 6, 1),        # H_kv*d = 640: VALU V side; r_k 16: VALU K side and q~
     (32, 32, 128, 64, 1024, 24, 1),     # MFMA both sides (one shared launch), MFMA q~
     (32, 32, 128, 64, 1024, 64, 1),     # MFMA V side filling every CU (plain append: two launches)
     (32, 32, 128, 64, 512, 20, 16),     # 320 new rows: many-token V kernel, append then decode
