@@ -83,6 +83,67 @@ __device__ __forceinline__ void append_k_mfma_body(int tile, int lane, const f16
     if (tt * 32 + mfma_row(reg, lane) < n) kc[dst[reg]] = (f16)acc[reg];
 }
 
+// The same tile with both operands staged through LDS, 128 d at a time (the
+// standalone K launch, one tile per 64-thread workgroup): a wave load
+// instruction reads 256 contiguous bytes of each of four rows (the tile's k
+// rows, then its w_k rows) instead of 32 bytes of each of 32.  The same chain
+// of k-steps, so the K pool is bit-identical to append_k_mfma_body's.
+// kl: the wave's LDS rows [64][kKRow].
+constexpr int kKChunk = 128;
+constexpr int kKRow = kKChunk + 8;
+__device__ __forceinline__ void append_k_mfma_staged_body(int tile, int lane, const f16* __restrict__ k,
+                                                          const f16* __restrict__ wk, int n, int H, int D, int RK,
+                                                          SlotOf where, f16* __restrict__ kc, f16 (*kl)[kKRow]) {
+  const int rtiles = RK / 32;
+  const int rt = tile % rtiles;
+  const int h = (tile / rtiles) % H;
+  const int tt = tile / (rtiles * H);
+  const int t = tt * 32 + (lane & 31);
+  const bool trow = t < n;
+  const int r = rt * 32 + (lane & 31);
+  const int kofs = (lane >> 5) * 8;
+  const int tl = min(tt * 32 + (lane & 31), n - 1);
+  const int lseq = where.seq[tl], lpos = where.pos[tl];
+  int lphys = 0;
+  // staging: piece i of a lane is row 4i + lane/16 of the 64 (k rows of the
+  // tile's tokens, clamped to the last token; then w_k rows), 16 bytes at
+  // 8*(lane%16); past a partial chunk's width the lane re-reads column 0
+  const int prow = lane >> 4, pcol = (lane & 15) * 8;
+  auto src_row = [&](int rr) -> const f16* {
+    return rr < 32 ? k + ((size_t)min(tt * 32 + rr, n - 1) * H + h) * D : wk + ((size_t)h * RK + rt * 32 + rr - 32) * D;
+  };
+  floatx16 acc = {};
+  for (int c0 = 0; c0 < D; c0 += kKChunk) {
+    const int cw = min(kKChunk, D - c0);
+    const int col = pcol < cw ? pcol : 0;
+    half8 buf[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) buf[i] = *reinterpret_cast<const half8*>(src_row(4 * i + prow) + c0 + col);
+    __builtin_amdgcn_sched_barrier(0);      // the table entry is read behind the operands
+    if (c0 == 0) lphys = where.bt[(size_t)lseq * where.mb + lpos / kBlock];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) *reinterpret_cast<half8*>(&kl[4 * i + prow][pcol]) = buf[i];
+    for (int k0 = 0; k0 < cw; k0 += 16) {
+      const half8 a = *reinterpret_cast<const half8*>(&kl[lane & 31][k0 + kofs]);
+      const half8 b = *reinterpret_cast<const half8*>(&kl[32 + (lane & 31)][k0 + kofs]);
+      acc = mfma32x32x16(trow ? a : half8{}, b, acc);
+    }
+  }
+  // every shuffle is issued before the first store (the stores are guarded)
+  size_t dst[16];
+#pragma unroll
+  for (int reg = 0; reg < 16; ++reg) {
+    const int src = mfma_row(reg, lane);    // token row of this register, looked up by lane src
+    const int phys = __shfl(lphys, src, 64);
+    const int slot = __shfl(lpos, src, 64) % kBlock;
+    dst[reg] = (((size_t)phys * H + h) * kBlock + slot) * RK + r;
+  }
+#pragma unroll
+  for (int reg = 0; reg < 16; ++reg)
+    if (tt * 32 + mfma_row(reg, lane) < n) kc[dst[reg]] = (f16)acc[reg];
+}
+
 // K side, VALU: one thread per (token, head, latent).
 __device__ __forceinline__ void append_k_valu_body(int idx, const f16* __restrict__ k, const f16* __restrict__ wk,
                                                    int n, int H, int D, int RK, SlotOf where,

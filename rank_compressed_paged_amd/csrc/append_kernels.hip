@@ -10,7 +10,8 @@ namespace starkv {
 __global__ void __launch_bounds__(64)
 append_k_mfma_kernel(const f16* __restrict__ k, const f16* __restrict__ wk, int n, int H, int D, int RK,
                      SlotOf where, f16* __restrict__ kc) {
-  append_k_mfma_body(blockIdx.x, threadIdx.x, k, wk, n, H, D, RK, where, kc);
+  __shared__ __attribute__((aligned(16))) f16 kl[64][kKRow];
+  append_k_mfma_staged_body(blockIdx.x, threadIdx.x, k, wk, n, H, D, RK, where, kc, kl);
 }
 
 __global__ void __launch_bounds__(256)

@@ -8,8 +8,9 @@ piece, where it is written in LDS, and where the MFMA fragments are read.
   distinct banks, and the 16-byte fragment reads may be at most 2-way;
 - MFMA V append (append_v_mfma_body): each wave's 32 rows (16 token rows, 16
   w_v rows) staged 128 k at a time, partial last chunks included;
-- standalone query projection (qproj_mfma_staged_body): 64 rows (32 q rows,
-  32 B_k rows) staged 128 d at a time.
+- standalone query projection (qproj_mfma_staged_body) and standalone K append
+  (append_k_mfma_staged_body), which share one map: 64 rows (32 query or key
+  rows, 32 B_k or w_k rows) staged 128 d at a time.
 
 These are host-side checks of the mappings only; the GPU parity tests run the
 kernels themselves.
